@@ -1,0 +1,30 @@
+"""CPU oracle for frame-block-causal attention and the reference-anchored KV window.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or link
+anything in this package; only the tests, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code with the HIP library: it takes
+plain numpy arrays and computes in float64 with the most literal formulation of
+the pages' definitions.
+
+Sources (the pages are web notes on "DiT as Real-Time Rerenderer: Streaming
+Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
+  * attention.py  -- Key Designs 2 ("Causal 3D attention for streaming
+    autoregression"), the Attn(Q,K,V) equation with the frame mask M.
+  * listkv.py     -- Key Designs 4 ("Reference-preserving KV cache update and
+    live style switching"), and Key Designs 1 for the reference as one extra
+    latent frame placed before the first frame.
+
+Every function here is pinned by tests/test_oracle.py and tests/test_listkv.py
+against things other than itself (brute-force loops, textbook special cases,
+closed forms and invariants).
+"""
+
+from .attention import (  # noqa: F401
+    visible,
+    attn_block_causal,
+    attn_brute_force,
+    attn_rows,
+    attn_stream_step,
+    attn_stream_rows,
+)
+from .listkv import ListKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401
