@@ -1,0 +1,476 @@
+// C-ABI host layer of librtr_attn.so: argument checks, the host-side metadata
+// of the reference-anchored rolling KV ring, and kernel launches.
+//
+// The cache semantics follow the RTR-DiT notes ("DiT as Real-Time Rerenderer
+// ...", Key Designs 4): a fixed-length window of past latent frames to which
+// newly generated frames are appended and from which the oldest are evicted
+// once it is full; reference frames held in a separate resident slot in front
+// that appending never touches; a condition switch that replaces, keeps or
+// clears the reference and keeps only the most recent window frame(s).
+//
+// Physical layout: window frame slots form a ring over the caller's
+// [W, k, H, d] buffers.  Logical position p (0 = oldest) lives in slot
+// (head + p) mod W.  Appending into a full ring overwrites slot `head` and
+// advances it, so evicting never moves data; trimming on a switch only moves
+// `head` and `count`.  Every piece of metadata lives on the host, so no call
+// reads device memory or waits for the device.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "rtr_internal.h"
+
+struct rtr_kv_cache {
+    void *k_ring, *v_ring, *k_ref, *v_ref;
+    int32_t W, R_cap;
+    int64_t kpf;
+    int32_t H, d;
+    rtr_dtype dt;
+    // metadata
+    int32_t count, head, ref_frames;
+    int64_t ref_gen, next_id;
+    int64_t slot_frame_id[RTR_MAX_WINDOW];  // indexed by physical slot
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    return RTR_OK;
+}
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;  // token indices stay far from int32 overflow
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t esize(rtr_dtype dt) { return dt == RTR_BF16 ? 2 : 4; }
+bool valid_dtype(int dt) { return dt == RTR_BF16 || dt == RTR_F32; }
+
+bool overlaps(const void *a, int64_t na, const void *b, int64_t nb) {
+    if (!a || !b || na <= 0 || nb <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+float resolve_scale(float scale, int d) {
+    return (scale > 0.f) ? scale : 1.0f / std::sqrt((float)d);
+}
+
+int check_scale(float scale) {
+    if (std::isinf(scale)) return fail(RTR_EINVAL, "scale must be finite");
+    return RTR_OK;
+}
+
+int64_t frame_bytes(const rtr_kv_cache *kv) { return kv->kpf * kv->H * kv->d * esize(kv->dt); }
+
+// One append of a frame to the ring metadata; returns the slot written or -1
+// when W == 0 (nothing is kept).
+int ring_push(int32_t W, int32_t &count, int32_t &head, int64_t &next_id, int64_t *slot_ids) {
+    const int64_t id = next_id++;
+    if (W == 0) return -1;
+    int slot;
+    if (count < W) {
+        slot = (head + count) % W;
+        ++count;
+    } else {
+        slot = head;
+        head = (head + 1) % W;
+    }
+    slot_ids[slot] = id;
+    return slot;
+}
+
+// Slots of the next n appends; frames evicted again by the same append get -1.
+void plan_append(const rtr_kv_cache *kv, int32_t n, int32_t *slots, int32_t &count, int32_t &head,
+                 int64_t &next_id, int64_t *slot_ids) {
+    count = kv->count;
+    head = kv->head;
+    next_id = kv->next_id;
+    std::memcpy(slot_ids, kv->slot_frame_id, sizeof(kv->slot_frame_id));
+    const int32_t keep_from = n - (n < kv->W ? n : kv->W);  // survivors: f >= n - min(n, W)
+    for (int32_t f = 0; f < n; ++f) {
+        const int s = ring_push(kv->W, count, head, next_id, slot_ids);
+        if (slots) slots[f] = (f >= keep_from) ? s : -1;
+    }
+}
+
+int check_cache(const rtr_kv_cache *kv) {
+    if (!kv) return fail(RTR_EINVAL, "cache handle is NULL");
+    return RTR_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(RTR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rtr_version(void) { return 100; }
+
+const char *rtr_last_error(void) { return g_err.c_str(); }
+
+const char *rtr_status_string(int code) {
+    switch (code) {
+        case RTR_OK: return "ok";
+        case RTR_EINVAL: return "invalid argument";
+        case RTR_EUNSUPPORTED: return "unsupported";
+        case RTR_EHIP: return "HIP error";
+        case RTR_ESTATE: return "invalid cache state";
+        default: return "unknown status";
+    }
+}
+
+int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
+                          rtr_dtype in_dtype, rtr_dtype out_dtype, float scale,
+                          rtr_stream stream) {
+    if (T < 0 || T > kMaxTokens) return fail(RTR_EINVAL, "T=%lld out of range [0, 2^30]", (long long)T);
+    if (H < 1) return fail(RTR_EINVAL, "H=%d must be >= 1", H);
+    if (tokens_per_frame < 1) return fail(RTR_EINVAL, "tokens_per_frame must be >= 1");
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (d != 64 && d != 128) return fail(RTR_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (in_dtype == RTR_F32 && out_dtype != RTR_F32)
+        return fail(RTR_EUNSUPPORTED, "float32 input needs float32 output");
+    if (int rc = check_scale(scale)) return rc;
+    if (T == 0) return ok();
+    if (!q || !k || !v || !o) return fail(RTR_EINVAL, "q, k, v and o must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return fail(RTR_EINVAL, "device pointers must be 16-byte aligned");
+    const int64_t in_bytes = T * H * d * esize(in_dtype);
+    const int64_t out_bytes = T * H * d * esize(out_dtype);
+    const int64_t lse_bytes = T * H * 4;
+    for (const void *x : {q, k, v}) {
+        if (overlaps(o, out_bytes, x, in_bytes)) return fail(RTR_EINVAL, "o overlaps an input");
+        if (overlaps(lse, lse_bytes, x, in_bytes)) return fail(RTR_EINVAL, "lse overlaps an input");
+    }
+    if (overlaps(lse, lse_bytes, o, out_bytes)) return fail(RTR_EINVAL, "lse overlaps o");
+
+    rtr::AttnProblem p;
+    p.q = q;
+    p.o = o;
+    p.lse = lse;
+    p.kseg[0] = k;
+    p.vseg[0] = v;
+    p.nseg = 1;
+    p.seg_len = T;
+    p.Tq = T;
+    p.Tk = T;
+    p.tokens_per_frame = tokens_per_frame < T ? tokens_per_frame : T;
+    p.prefix = 0;
+    p.H = H;
+    p.d = d;
+    p.scale = resolve_scale(scale, d);
+    p.in_dtype = in_dtype;
+    p.out_dtype = out_dtype;
+    const hipError_t e = rtr::launch_attention(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
+                  int32_t window_frames, int32_t ref_capacity_frames, int64_t tokens_per_frame,
+                  int32_t H, int32_t d, rtr_dtype dtype) {
+    if (!out) return fail(RTR_EINVAL, "out is NULL");
+    if (window_frames < 0 || window_frames > RTR_MAX_WINDOW)
+        return fail(RTR_EUNSUPPORTED, "window_frames=%d outside [0, %d]", window_frames, RTR_MAX_WINDOW);
+    if (ref_capacity_frames < 0 || ref_capacity_frames > RTR_MAX_REF)
+        return fail(RTR_EUNSUPPORTED, "ref_capacity_frames=%d outside [0, %d]", ref_capacity_frames,
+                    RTR_MAX_REF);
+    if (tokens_per_frame < 1) return fail(RTR_EINVAL, "tokens_per_frame must be >= 1");
+    if (H < 1) return fail(RTR_EINVAL, "H must be >= 1");
+    if (!valid_dtype(dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (d != 64 && d != 128) return fail(RTR_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    const int64_t total_frames = (int64_t)RTR_MAX_REF + RTR_MAX_WINDOW + RTR_MAX_CHUNK;
+    if (tokens_per_frame * total_frames > kMaxTokens)
+        return fail(RTR_EUNSUPPORTED, "tokens_per_frame too large");
+    if (window_frames > 0 && (!k_ring || !v_ring))
+        return fail(RTR_EINVAL, "ring buffers must be non-NULL when window_frames > 0");
+    if (ref_capacity_frames > 0 && (!k_ref || !v_ref))
+        return fail(RTR_EINVAL, "reference buffers must be non-NULL when ref capacity > 0");
+    if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(k_ref) || !aligned16(v_ref))
+        return fail(RTR_EINVAL, "cache buffers must be 16-byte aligned");
+    const int64_t fb = tokens_per_frame * H * d * esize(dtype);
+    const int64_t ring_b = fb * window_frames, ref_b = fb * ref_capacity_frames;
+    const void *bufs[4] = {k_ring, v_ring, k_ref, v_ref};
+    const int64_t sizes[4] = {ring_b, ring_b, ref_b, ref_b};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(bufs[i], sizes[i], bufs[j], sizes[j]))
+                return fail(RTR_EINVAL, "cache buffers overlap");
+
+    rtr_kv_cache *kv = new (std::nothrow) rtr_kv_cache();
+    if (!kv) return fail(RTR_EINVAL, "out of host memory");
+    kv->k_ring = k_ring;
+    kv->v_ring = v_ring;
+    kv->k_ref = k_ref;
+    kv->v_ref = v_ref;
+    kv->W = window_frames;
+    kv->R_cap = ref_capacity_frames;
+    kv->kpf = tokens_per_frame;
+    kv->H = H;
+    kv->d = d;
+    kv->dt = dtype;
+    kv->count = 0;
+    kv->head = 0;
+    kv->ref_frames = 0;
+    kv->ref_gen = 0;
+    kv->next_id = 0;
+    for (auto &x : kv->slot_frame_id) x = -1;
+    *out = kv;
+    return ok();
+}
+
+int rtr_kv_destroy(rtr_kv_cache *kv) {
+    delete kv;
+    return ok();
+}
+
+int rtr_kv_next_slots(const rtr_kv_cache *kv, int32_t n_frames, int32_t *slots) {
+    if (int rc = check_cache(kv)) return rc;
+    if (n_frames < 0) return fail(RTR_EINVAL, "n_frames must be >= 0");
+    if (n_frames > 0 && !slots) return fail(RTR_EINVAL, "slots is NULL");
+    int32_t count, head;
+    int64_t next_id, ids[RTR_MAX_WINDOW];
+    plan_append(kv, n_frames, slots, count, head, next_id, ids);
+    return ok();
+}
+
+int rtr_kv_commit_inplace(rtr_kv_cache *kv, int32_t n_frames) {
+    if (int rc = check_cache(kv)) return rc;
+    if (n_frames < 0) return fail(RTR_EINVAL, "n_frames must be >= 0");
+    int32_t count, head;
+    int64_t next_id, ids[RTR_MAX_WINDOW];
+    plan_append(kv, n_frames, nullptr, count, head, next_id, ids);
+    kv->count = count;
+    kv->head = head;
+    kv->next_id = next_id;
+    std::memcpy(kv->slot_frame_id, ids, sizeof ids);
+    return ok();
+}
+
+int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new, int32_t n_frames,
+                        rtr_stream stream) {
+    if (int rc = check_cache(kv)) return rc;
+    if (n_frames < 0) return fail(RTR_EINVAL, "n_frames must be >= 0");
+    if (n_frames == 0) return ok();
+    if (!k_new || !v_new) return fail(RTR_EINVAL, "k_new and v_new must be non-NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(RTR_EINVAL, "k_new/v_new must be 16-byte aligned");
+    const int64_t fb = frame_bytes(kv);
+    const int64_t nb = fb * n_frames;
+    const int64_t ring_b = fb * kv->W;
+    for (const void *src : {k_new, v_new})
+        for (const void *dst : {kv->k_ring, kv->v_ring})
+            if (overlaps(src, nb, dst, ring_b)) return fail(RTR_EINVAL, "new frames overlap the ring buffers");
+
+    // Frames f < n - min(n, W) are evicted again by this same append: they get
+    // ids but are never copied.
+    const int32_t survivors = n_frames < kv->W ? n_frames : kv->W;
+    const int32_t first = n_frames - survivors;
+    int32_t slots[RTR_MAX_WINDOW];
+    int32_t count = kv->count, head = kv->head;
+    int64_t next_id = kv->next_id, ids[RTR_MAX_WINDOW];
+    std::memcpy(ids, kv->slot_frame_id, sizeof ids);
+    for (int32_t f = 0; f < n_frames; ++f) {
+        const int s = ring_push(kv->W, count, head, next_id, ids);
+        if (f >= first) slots[f - first] = s;
+    }
+    rtr::CopyJobs jobs;
+    for (int32_t f = 0; f < survivors; ++f) {
+        const int64_t src_off = (int64_t)(first + f) * fb;
+        const int64_t dst_off = (int64_t)slots[f] * fb;
+        jobs.src[jobs.n] = (const char *)k_new + src_off;
+        jobs.dst[jobs.n++] = (char *)kv->k_ring + dst_off;
+        jobs.src[jobs.n] = (const char *)v_new + src_off;
+        jobs.dst[jobs.n++] = (char *)kv->v_ring + dst_off;
+    }
+    jobs.bytes = fb;
+    if (jobs.n > 0) {
+        const hipError_t e = rtr::launch_frame_copies(jobs, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "ring copy launch");
+    }
+    kv->count = count;
+    kv->head = head;
+    kv->next_id = next_id;
+    std::memcpy(kv->slot_frame_id, ids, sizeof ids);
+    return ok();
+}
+
+int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, const void *v_ref,
+                     int32_t ref_frames, int32_t keep_recent, rtr_stream stream) {
+    if (int rc = check_cache(kv)) return rc;
+    if (mode != RTR_REF_KEEP && mode != RTR_REF_REPLACE && mode != RTR_REF_CLEAR)
+        return fail(RTR_EINVAL, "unknown reference mode %d", (int)mode);
+    if (keep_recent < -1) return fail(RTR_EINVAL, "keep_recent must be >= -1");
+    const int64_t fb = frame_bytes(kv);
+    bool copy = false;
+    if (mode == RTR_REF_REPLACE) {
+        if (kv->R_cap < 1) return fail(RTR_ESTATE, "cache was created without reference capacity");
+        if (ref_frames < 1 || ref_frames > kv->R_cap)
+            return fail(RTR_EINVAL, "ref_frames=%d outside [1, %d]", ref_frames, kv->R_cap);
+        if ((k_ref == nullptr) != (v_ref == nullptr))
+            return fail(RTR_EINVAL, "k_ref and v_ref must both be NULL or both non-NULL");
+        if (k_ref) {
+            if (!aligned16(k_ref) || !aligned16(v_ref)) return fail(RTR_EINVAL, "reference pointers must be 16-byte aligned");
+            const int64_t nb = fb * ref_frames;
+            const bool same = (k_ref == kv->k_ref && v_ref == kv->v_ref);
+            if (!same) {
+                for (const void *src : {k_ref, v_ref}) {
+                    for (const void *dst : {kv->k_ref, kv->v_ref})
+                        if (overlaps(src, nb, dst, fb * kv->R_cap))
+                            return fail(RTR_EINVAL, "new reference overlaps the reference slot");
+                    for (const void *dst : {kv->k_ring, kv->v_ring})
+                        if (overlaps(src, nb, dst, fb * kv->W))
+                            return fail(RTR_EINVAL, "new reference overlaps the ring buffers");
+                }
+                copy = true;
+            }
+        }
+    }
+    if (copy) {
+        rtr::CopyJobs jobs;
+        jobs.src[0] = k_ref;
+        jobs.dst[0] = kv->k_ref;
+        jobs.src[1] = v_ref;
+        jobs.dst[1] = kv->v_ref;
+        jobs.n = 2;
+        jobs.bytes = fb * ref_frames;
+        const hipError_t e = rtr::launch_frame_copies(jobs, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "reference copy launch");
+    }
+    if (mode == RTR_REF_REPLACE) {
+        kv->ref_frames = ref_frames;
+        ++kv->ref_gen;
+    } else if (mode == RTR_REF_CLEAR) {
+        kv->ref_frames = 0;
+    }
+    if (keep_recent >= 0 && keep_recent < kv->count) {
+        kv->head = (kv->head + kv->count - keep_recent) % kv->W;
+        kv->count = keep_recent;
+    }
+    return ok();
+}
+
+int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                         void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
+                         float scale, rtr_stream stream) {
+    if (int rc = check_cache(kv)) return rc;
+    if (chunk_frames < 1 || chunk_frames > RTR_MAX_CHUNK)
+        return fail(RTR_EUNSUPPORTED, "chunk_frames=%d outside [1, %d]", chunk_frames, RTR_MAX_CHUNK);
+    if (!valid_dtype(out_dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (kv->dt == RTR_F32 && out_dtype != RTR_F32)
+        return fail(RTR_EUNSUPPORTED, "float32 cache needs float32 output");
+    if (int rc = check_scale(scale)) return rc;
+    if (!q || !k || !v || !o) return fail(RTR_EINVAL, "q, k, v and o must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return fail(RTR_EINVAL, "device pointers must be 16-byte aligned");
+    const int64_t fb = frame_bytes(kv);
+    const int64_t Tq = (int64_t)chunk_frames * kv->kpf;
+    const int64_t in_b = fb * chunk_frames;
+    const int64_t out_b = Tq * kv->H * kv->d * esize(out_dtype);
+    const int64_t lse_b = Tq * kv->H * 4;
+    const void *ins[7] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
+    const int64_t in_sz[7] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
+    for (int i = 0; i < 7; ++i) {
+        if (overlaps(o, out_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "o overlaps an input or the cache");
+        if (overlaps(lse, lse_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "lse overlaps an input or the cache");
+    }
+    if (overlaps(lse, lse_b, o, out_b)) return fail(RTR_EINVAL, "lse overlaps o");
+
+    rtr::AttnProblem p;
+    int nseg = 0;
+    for (int r = 0; r < kv->ref_frames; ++r) {
+        p.kseg[nseg] = (const char *)kv->k_ref + r * fb;
+        p.vseg[nseg++] = (const char *)kv->v_ref + r * fb;
+    }
+    for (int i = 0; i < kv->count; ++i) {
+        const int slot = (kv->head + i) % kv->W;
+        p.kseg[nseg] = (const char *)kv->k_ring + slot * fb;
+        p.vseg[nseg++] = (const char *)kv->v_ring + slot * fb;
+    }
+    for (int c = 0; c < chunk_frames; ++c) {
+        p.kseg[nseg] = (const char *)k + c * fb;
+        p.vseg[nseg++] = (const char *)v + c * fb;
+    }
+    p.q = q;
+    p.o = o;
+    p.lse = lse;
+    p.nseg = nseg;
+    p.seg_len = kv->kpf;
+    p.Tq = Tq;
+    p.prefix = (int64_t)(kv->ref_frames + kv->count) * kv->kpf;
+    p.Tk = p.prefix + Tq;
+    p.tokens_per_frame = kv->kpf;
+    p.H = kv->H;
+    p.d = kv->d;
+    p.scale = resolve_scale(scale, kv->d);
+    p.in_dtype = kv->dt;
+    p.out_dtype = out_dtype;
+    const hipError_t e = rtr::launch_attention(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out) {
+    if (int rc = check_cache(kv)) return rc;
+    if (!out) return fail(RTR_EINVAL, "out is NULL");
+    std::memset(out, 0, sizeof *out);
+    out->window_frames = kv->W;
+    out->count = kv->count;
+    out->head = kv->head;
+    out->ref_frames = kv->ref_frames;
+    out->ref_generation = kv->ref_gen;
+    out->next_frame_id = kv->next_id;
+    for (int p = 0; p < RTR_MAX_WINDOW; ++p) {
+        out->slot[p] = -1;
+        out->frame_id[p] = -1;
+    }
+    for (int p = 0; p < kv->count; ++p) {
+        const int s = (kv->head + p) % kv->W;
+        out->slot[p] = s;
+        out->frame_id[p] = kv->slot_frame_id[s];
+    }
+    return ok();
+}
+
+int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in) {
+    if (int rc = check_cache(kv)) return rc;
+    if (!in) return fail(RTR_EINVAL, "in is NULL");
+    if (in->window_frames != kv->W) return fail(RTR_ESTATE, "snapshot window %d != cache window %d", in->window_frames, kv->W);
+    if (in->count < 0 || in->count > kv->W) return fail(RTR_ESTATE, "count out of range");
+    if (kv->W > 0 ? (in->head < 0 || in->head >= kv->W) : in->head != 0) return fail(RTR_ESTATE, "head out of range");
+    if (in->ref_frames < 0 || in->ref_frames > kv->R_cap) return fail(RTR_ESTATE, "ref_frames out of range");
+    if (in->ref_generation < 0 || in->next_frame_id < 0) return fail(RTR_ESTATE, "negative counters");
+    int64_t prev = -1;
+    for (int p = 0; p < in->count; ++p) {
+        if (in->slot[p] != (in->head + p) % kv->W) return fail(RTR_ESTATE, "slot list is not a ring from head");
+        if (in->frame_id[p] <= prev || in->frame_id[p] >= in->next_frame_id)
+            return fail(RTR_ESTATE, "frame ids must increase and stay below next_frame_id");
+        prev = in->frame_id[p];
+    }
+    kv->count = in->count;
+    kv->head = in->head;
+    kv->ref_frames = in->ref_frames;
+    kv->ref_gen = in->ref_generation;
+    kv->next_id = in->next_frame_id;
+    for (auto &x : kv->slot_frame_id) x = -1;
+    for (int p = 0; p < in->count; ++p) kv->slot_frame_id[in->slot[p]] = in->frame_id[p];
+    return ok();
+}
+
+}  // extern "C"

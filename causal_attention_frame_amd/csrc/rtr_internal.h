@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI host layer (rtr_api.hip) and the HIP
+// kernels (attn_fwd.hip, kv_copy.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rtr_attn.h"
+
+namespace rtr {
+
+// Key frames one streaming call can see: anchored reference + window + chunk.
+constexpr int kMaxKeyFrames = RTR_MAX_REF + RTR_MAX_WINDOW + RTR_MAX_CHUNK;
+// Frame copies one append can enqueue (K and V of each surviving frame).
+constexpr int kMaxCopies = 2 * (RTR_MAX_WINDOW > RTR_MAX_REF ? RTR_MAX_WINDOW : RTR_MAX_REF);
+
+// One attention launch.  Keys are addressed through a segment table: key j lies
+// in segment f = j / seg_len, row j - f*seg_len of a [*, H, d] block starting at
+// kseg[f] / vseg[f].  The full-sequence form uses one segment holding all keys;
+// the streaming form uses one segment per latent frame (reference frames,
+// window frames in logical order, then the chunk's frames).
+//
+// Mask: query row i (0-based within q) may see key j iff
+//   j < min(prefix + (floor(i / tokens_per_frame) + 1) * tokens_per_frame, Tk),
+// which is the frame mask with `prefix` always-visible cached keys in front.
+struct AttnProblem {
+    const void *q = nullptr;
+    void *o = nullptr;
+    float *lse = nullptr;
+    const void *kseg[kMaxKeyFrames] = {};
+    const void *vseg[kMaxKeyFrames] = {};
+    int32_t nseg = 0;
+    int64_t seg_len = 0;
+    int64_t Tq = 0, Tk = 0;
+    int64_t tokens_per_frame = 1;
+    int64_t prefix = 0;
+    int32_t H = 0, d = 0;
+    float scale = 0.f;
+    rtr_dtype in_dtype = RTR_BF16, out_dtype = RTR_BF16;
+};
+
+hipError_t launch_attention(const AttnProblem &p, hipStream_t stream);
+
+// Copies of whole [k, H, d] frames (16-byte multiples, 16-byte aligned).
+struct CopyJobs {
+    const void *src[kMaxCopies] = {};
+    void *dst[kMaxCopies] = {};
+    int32_t n = 0;
+    int64_t bytes = 0;  // per copy
+};
+
+hipError_t launch_frame_copies(const CopyJobs &jobs, hipStream_t stream);
+
+}  // namespace rtr

@@ -1,0 +1,241 @@
+"""Thin Python binding over librtr_attn.so (ctypes).
+
+Argument marshalling only: every step of the computation runs in the library's
+HIP kernels.  PyTorch provides device memory and the current HIP stream.  The
+functions carry the C names; see include/rtr_attn.h for the full contract
+(layouts, ownership, error behaviour).
+
+There is no fallback: if the library is missing, loading it raises.
+"""
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+RTR_OK, RTR_EINVAL, RTR_EUNSUPPORTED, RTR_EHIP, RTR_ESTATE = 0, -1, -2, -3, -4
+RTR_BF16, RTR_F32 = 0, 1
+RTR_REF_KEEP, RTR_REF_REPLACE, RTR_REF_CLEAR = 0, 1, 2
+RTR_MAX_WINDOW, RTR_MAX_REF, RTR_MAX_CHUNK = 64, 1, 16
+
+_c_i32, _c_i64, _c_f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+
+
+class rtr_kv_state(ctypes.Structure):
+    _fields_ = [
+        ("window_frames", _c_i32),
+        ("count", _c_i32),
+        ("head", _c_i32),
+        ("ref_frames", _c_i32),
+        ("ref_generation", _c_i64),
+        ("next_frame_id", _c_i64),
+        ("slot", _c_i32 * RTR_MAX_WINDOW),
+        ("frame_id", _c_i64 * RTR_MAX_WINDOW),
+    ]
+
+    def as_dict(self):
+        n = self.count
+        return dict(window_frames=self.window_frames, count=n, head=self.head,
+                    ref_frames=self.ref_frames, ref_generation=self.ref_generation,
+                    next_frame_id=self.next_frame_id, slot=list(self.slot[:n]),
+                    frame_id=list(self.frame_id[:n]))
+
+
+# name -> (restype, argtypes); mirrors include/rtr_attn.h
+_SIGNATURES = {
+    "rtr_attn_block_causal": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32,
+                                             _c_i64, ctypes.c_int, ctypes.c_int, _c_f32, _vp]),
+    "rtr_kv_create": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                     _c_i64, _c_i32, _c_i32, ctypes.c_int]),
+    "rtr_kv_destroy": (ctypes.c_int, [_vp]),
+    "rtr_kv_append_evict": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp]),
+    "rtr_kv_next_slots": (ctypes.c_int, [_vp, _c_i32, ctypes.POINTER(_c_i32)]),
+    "rtr_kv_commit_inplace": (ctypes.c_int, [_vp, _c_i32]),
+    "rtr_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, ctypes.c_int,
+                                            _c_f32, _vp]),
+    "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
+    "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
+    "rtr_kv_set_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
+    "rtr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rtr_last_error": (ctypes.c_char_p, []),
+    "rtr_version": (ctypes.c_int, []),
+}
+
+_lib = None
+
+
+def lib():
+    """Load librtr_attn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+class RtrError(RuntimeError):
+    def __init__(self, code, fn):
+        L = lib()
+        msg = L.rtr_last_error().decode()
+        super().__init__(f"{fn}: {L.rtr_status_string(code).decode()} ({code}): {msg}")
+        self.code = code
+
+
+def _check(code, fn):
+    if code != RTR_OK:
+        raise RtrError(code, fn)
+
+
+# ---------------------------------------------------------------- marshalling
+def _ptr(x):
+    """Device address of a tensor (must be contiguous), an int address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_contiguous():
+        raise ValueError("tensors passed to librtr_attn must be contiguous")
+    return x.data_ptr()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RTR_BF16
+    if t.dtype == torch.float32:
+        return RTR_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+# ---------------------------------------------------------------- full form
+def rtr_attn_block_causal(q, k, v, tokens_per_frame, o=None, lse=None, scale=0.0,
+                          out_dtype=None, want_lse=False, stream=None):
+    """Frame-block-causal attention over one [T, H, d] sequence.
+    Returns (o, lse or None)."""
+    import torch
+    T, H, d = q.shape
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    _check(lib().rtr_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), T, H, d,
+                                       int(tokens_per_frame), _dtype_code(q), _dtype_code(o),
+                                       float(scale), _stream(stream, q.device)),
+           "rtr_attn_block_causal")
+    return o, lse
+
+
+# ---------------------------------------------------------------- the cache
+class KVCache:
+    """One layer's reference-anchored rolling KV cache (handle + buffers).
+
+    k_ring, v_ring: [W, k, H, d]; k_ref, v_ref: [R_cap, k, H, d] (or None).
+    Tensors are kept referenced for the handle's lifetime.  Integer device
+    addresses are accepted too (metadata-only use)."""
+
+    def __init__(self, k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
+                 tokens_per_frame, H, d, dtype):
+        self._bufs = (k_ring, v_ring, k_ref, v_ref)
+        self.W, self.R_cap, self.kpf, self.H, self.d = (window_frames, ref_capacity_frames,
+                                                        tokens_per_frame, H, d)
+        self.dtype = dtype
+        h = _vp()
+        _check(lib().rtr_kv_create(ctypes.byref(h), _ptr(k_ring), _ptr(v_ring), _ptr(k_ref),
+                                   _ptr(v_ref), window_frames, ref_capacity_frames,
+                                   tokens_per_frame, H, d, dtype), "rtr_kv_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().rtr_kv_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rtr_kv_create(k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
+                  tokens_per_frame, H, d, dtype=RTR_BF16):
+    return KVCache(k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
+                   tokens_per_frame, H, d, dtype)
+
+
+def rtr_kv_destroy(kv):
+    kv.close()
+
+
+def rtr_kv_append_evict(kv, k_new, v_new, n_frames, stream=None):
+    dev = k_new.device if hasattr(k_new, "device") else None
+    _check(lib().rtr_kv_append_evict(kv.handle, _ptr(k_new), _ptr(v_new), int(n_frames),
+                                     _stream(stream, dev) if dev is not None else stream),
+           "rtr_kv_append_evict")
+
+
+def rtr_kv_next_slots(kv, n_frames):
+    arr = (_c_i32 * max(1, n_frames))()
+    _check(lib().rtr_kv_next_slots(kv.handle, int(n_frames), arr), "rtr_kv_next_slots")
+    return list(arr[:n_frames])
+
+
+def rtr_kv_commit_inplace(kv, n_frames):
+    _check(lib().rtr_kv_commit_inplace(kv.handle, int(n_frames)), "rtr_kv_commit_inplace")
+
+
+def rtr_attn_stream_step(kv, q, k, v, chunk_frames, o=None, lse=None, scale=0.0, out_dtype=None,
+                         want_lse=False, stream=None):
+    """One streaming step for a chunk of `chunk_frames` frames.  Returns (o, lse or None)."""
+    import torch
+    Tq, H, d = q.shape
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((Tq, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    _check(lib().rtr_attn_stream_step(kv.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      int(chunk_frames), _dtype_code(o), float(scale),
+                                      _stream(stream, q.device)),
+           "rtr_attn_stream_step")
+    return o, lse
+
+
+def rtr_kv_reset_ref(kv, mode, k_ref=None, v_ref=None, ref_frames=1, keep_recent=1, stream=None):
+    dev = k_ref.device if hasattr(k_ref, "device") else None
+    s = _stream(stream, dev) if dev is not None else stream
+    _check(lib().rtr_kv_reset_ref(kv.handle, int(mode), _ptr(k_ref), _ptr(v_ref), int(ref_frames),
+                                  int(keep_recent), s), "rtr_kv_reset_ref")
+
+
+def rtr_kv_get_state(kv):
+    st = rtr_kv_state()
+    _check(lib().rtr_kv_get_state(kv.handle, ctypes.byref(st)), "rtr_kv_get_state")
+    return st
+
+
+def rtr_kv_set_state(kv, st):
+    _check(lib().rtr_kv_set_state(kv.handle, ctypes.byref(st)), "rtr_kv_set_state")
+
+
+def rtr_version():
+    return lib().rtr_version()

@@ -1,0 +1,170 @@
+/*
+ * rtr_attn.h -- C ABI of librtr_attn.so: frame-block-causal attention and the
+ * reference-anchored rolling KV cache of a streaming autoregressive video DiT,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: web notes on "DiT as Real-Time Rerenderer: Streaming
+ * Video Stylization with Autoregressive Diffusion Transformer" (RTR-DiT):
+ *   - Key Designs 2, Attn equation: Attn(Q,K,V) = softmax(Q K^T / sqrt(d) + M) V
+ *     with M_ij = 0 when floor(j/k) <= floor(i/k) and -inf otherwise; d is the
+ *     head dimension and k the number of spatial tokens per latent frame.
+ *   - Key Designs 1: the reference latent is prepended as one extra latent frame.
+ *   - Key Designs 4: a rolling 3D-attention KV cache; new frames are appended,
+ *     the oldest evicted once full; the reference tokens stay anchored at the
+ *     front as a resident slot; on a condition switch the cache keeps the most
+ *     recent frame and a new reference is anchored at the front.
+ *
+ * Conventions shared by every entry point
+ *   - Layout: token-major [tokens, H, d], d contiguous; row stride H*d elements.
+ *     Cache frames are [k, H, d] blocks; ring buffers hold W such frames and the
+ *     reference buffer R_cap frames.
+ *   - Memory: every device pointer is owned by the caller and must stay valid
+ *     until the work enqueued on `stream` has finished.  The library allocates
+ *     no device memory.  Device pointers must be 16-byte aligned.  Output
+ *     buffers must not overlap inputs.
+ *   - Asynchrony: device work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and nothing waits for it.  Cache metadata lives on the
+ *     host and changes at call time, so calls on one cache must be issued on
+ *     one stream (or the caller orders the streams).
+ *   - Errors: every argument is checked before anything is enqueued.  On error
+ *     the call returns a negative rtr_status, records a message readable with
+ *     rtr_last_error() (per thread), changes no state and enqueues nothing.
+ *     A failed kernel launch returns RTR_EHIP.
+ *   - Threads: a cache handle is not thread-safe.
+ */
+#ifndef RTR_ATTN_H
+#define RTR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RTR_OK = 0,
+    RTR_EINVAL = -1,        /* bad argument (null, negative size, misaligned, overlap) */
+    RTR_EUNSUPPORTED = -2,  /* valid request outside what this build implements */
+    RTR_EHIP = -3,          /* HIP runtime or launch failure */
+    RTR_ESTATE = -4         /* operation inconsistent with the cache state */
+} rtr_status;
+
+typedef enum { RTR_BF16 = 0, RTR_F32 = 1 } rtr_dtype;
+
+/* Reference handling on a condition switch (Key Designs 4). */
+typedef enum {
+    RTR_REF_KEEP = 0,     /* text-only switch: reference slot unchanged */
+    RTR_REF_REPLACE = 1,  /* anchor a new reference at the front */
+    RTR_REF_CLEAR = 2     /* drop the reference (text-guided mode) */
+} rtr_ref_mode;
+
+typedef void *rtr_stream; /* hipStream_t */
+
+#define RTR_MAX_WINDOW 64 /* window frames W */
+#define RTR_MAX_REF 1     /* reference frames R */
+#define RTR_MAX_CHUNK 16  /* frames per streaming chunk C */
+
+typedef struct rtr_kv_cache rtr_kv_cache; /* opaque, host-side ring metadata */
+
+/* Snapshot of a cache's metadata.  Window entries are in logical order, oldest
+ * first: entry p lives in physical ring slot slot[p] and holds the frame with
+ * generation-order id frame_id[p]. */
+typedef struct {
+    int32_t window_frames;  /* W */
+    int32_t count;          /* valid window frames, 0..W */
+    int32_t head;           /* physical slot of the oldest valid frame */
+    int32_t ref_frames;     /* reference frames currently anchored, 0..R_cap */
+    int64_t ref_generation; /* incremented by every REPLACE */
+    int64_t next_frame_id;  /* id the next appended frame receives */
+    int32_t slot[RTR_MAX_WINDOW];
+    int64_t frame_id[RTR_MAX_WINDOW];
+} rtr_kv_state;
+
+/* ------------------------------------------------------------------------
+ * Full-sequence form (training / teacher forcing).  Key Designs 2, Attn
+ * equation, over one sequence of T tokens whose frame 0 may be the reference.
+ *
+ *   q, k, v : [T, H, d] device, dtype in_dtype
+ *   o       : [T, H, d] device, dtype out_dtype (bf16 or f32 for bf16 input;
+ *             f32 for f32 input)
+ *   lse     : [H, T] device float32, natural-log softmax denominators
+ *             (log-sum-exp of the scaled, masked logits), or NULL
+ *   tokens_per_frame : k >= 1; k >= T gives the unmasked bidirectional teacher
+ *   d       : 64 or 128
+ *   scale   : logit scale; <= 0 selects 1/sqrt(d)
+ * T == 0 is a no-op.  Returns RTR_OK or a negative rtr_status.
+ * ---------------------------------------------------------------------- */
+int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
+                          rtr_dtype in_dtype, rtr_dtype out_dtype, float scale,
+                          rtr_stream stream);
+
+/* ------------------------------------------------------------------------
+ * KV cache of one attention layer over caller-owned device buffers
+ * (Key Designs 4).  k_ring, v_ring: [W, k, H, d]; k_ref, v_ref: [R_cap, k, H, d]
+ * (may be NULL when R_cap == 0).  Starts empty: count 0, no reference,
+ * generation 0, next frame id 0.  *out receives a handle to free with
+ * rtr_kv_destroy.  0 <= W <= RTR_MAX_WINDOW (W = 0 keeps no history; the ring
+ * pointers may then be NULL); 0 <= R_cap <= RTR_MAX_REF; d in {64, 128}.
+ * ---------------------------------------------------------------------- */
+int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
+                  int32_t window_frames, int32_t ref_capacity_frames,
+                  int64_t tokens_per_frame, int32_t H, int32_t d, rtr_dtype dtype);
+int rtr_kv_destroy(rtr_kv_cache *kv);
+
+/* Commit n_frames newly generated frames, given as [n_frames, k, H, d] device
+ * buffers k_new, v_new (Key Designs 4: appended in order; once the window is
+ * full each append evicts the oldest frame; the reference slot is never
+ * touched).  Only the newest min(n_frames, W) frames are copied; the copy is
+ * enqueued on `stream`.  n_frames == 0 is a no-op. */
+int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new,
+                        int32_t n_frames, rtr_stream stream);
+
+/* Physical ring slots the next n_frames appends would be written to, in
+ * order; frames that the same append would evict again get -1.  Changes
+ * nothing.  Lets a producer write K/V straight into the ring. */
+int rtr_kv_next_slots(const rtr_kv_cache *kv, int32_t n_frames, int32_t *slots);
+
+/* Metadata-only commit of n_frames frames that the caller has already written
+ * into the slots reported by rtr_kv_next_slots (zero-copy append).  Same
+ * state change as rtr_kv_append_evict; enqueues nothing. */
+int rtr_kv_commit_inplace(rtr_kv_cache *kv, int32_t n_frames);
+
+/* ------------------------------------------------------------------------
+ * Streaming form for one chunk of C = chunk_frames latent frames.  The chunk
+ * queries q ([C*k, H, d]) attend to the anchored reference frame(s), every
+ * valid window frame in logical order, and the chunk's own keys k, v
+ * ([C*k, H, d]) of chunk frames up to their own (the Attn mask with the chunk
+ * placed after the cached frames).  The cache is only read; commit the chunk
+ * afterwards with rtr_kv_append_evict.  o: [C*k, H, d] out_dtype; lse: [H, C*k]
+ * float32 or NULL.  1 <= C <= RTR_MAX_CHUNK; scale <= 0 selects 1/sqrt(d).
+ * ---------------------------------------------------------------------- */
+int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                         void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
+                         float scale, rtr_stream stream);
+
+/* Condition switch (Key Designs 4).  First the reference: KEEP leaves it,
+ * REPLACE anchors ref_frames (1..R_cap) new frames k_ref, v_ref
+ * ([ref_frames, k, H, d] device; both NULL means the caller already wrote
+ * them into the cache's reference buffers) and increments the generation,
+ * CLEAR removes it.  Then the window keeps only its newest keep_recent frames
+ * (-1 keeps all; the notes keep the most recent frame, keep_recent = 1).
+ * Window trimming moves no data. */
+int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, const void *v_ref,
+                     int32_t ref_frames, int32_t keep_recent, rtr_stream stream);
+
+/* Metadata snapshot / restore (checkpoint-resume).  set_state validates the
+ * snapshot against the cache's W and R_cap and changes nothing on error. */
+int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out);
+int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in);
+
+/* Diagnostics. */
+const char *rtr_status_string(int code);
+const char *rtr_last_error(void);
+int rtr_version(void); /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RTR_ATTN_H */

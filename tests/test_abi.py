@@ -1,0 +1,230 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+rejects bad arguments before touching the device, and its host-side ring
+metadata matches the oracle's literal list window under random schedules.
+
+No call here reaches a kernel launch: argument checks fail first, and the
+metadata paths used (in-place commit, reference KEEP/CLEAR/in-place REPLACE,
+state snapshots) never touch the device.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from causal_attention_frame_amd import rtr
+from oracle import ListKV, REF_CLEAR, REF_KEEP, REF_REPLACE
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "rtr_attn.h")
+FAKE = 0x7F0000000000          # a 16-byte aligned address that is never dereferenced
+MB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(rtr_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 12
+    L = rtr.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(rtr._SIGNATURES), "binding and header disagree"
+    assert rtr.rtr_version() == 100
+
+
+def test_status_strings():
+    L = rtr.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.rtr_status_string(code)
+    assert L.rtr_status_string(-99) == b"unknown status"
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE + MB, v=FAKE + 2 * MB, o=FAKE + 3 * MB, lse=None, T=64, H=2, d=128,
+             kpf=16, ind=rtr.RTR_BF16, outd=rtr.RTR_BF16, scale=0.0, stream=None)
+    a.update(kw)
+    return rtr.lib().rtr_attn_block_causal(a["q"], a["k"], a["v"], a["o"], a["lse"], a["T"],
+                                           a["H"], a["d"], a["kpf"], a["ind"], a["outd"],
+                                           a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), rtr.RTR_EINVAL),
+    (dict(T=1 << 31), rtr.RTR_EINVAL),
+    (dict(H=0), rtr.RTR_EINVAL),
+    (dict(kpf=0), rtr.RTR_EINVAL),
+    (dict(d=96), rtr.RTR_EUNSUPPORTED),
+    (dict(d=256), rtr.RTR_EUNSUPPORTED),
+    (dict(ind=7), rtr.RTR_EINVAL),
+    (dict(ind=rtr.RTR_F32, outd=rtr.RTR_BF16), rtr.RTR_EUNSUPPORTED),
+    (dict(q=None), rtr.RTR_EINVAL),
+    (dict(o=None), rtr.RTR_EINVAL),
+    (dict(k=FAKE + MB + 2), rtr.RTR_EINVAL),          # misaligned
+    (dict(lse=FAKE + 4 * MB + 4), rtr.RTR_EINVAL),    # misaligned lse
+    (dict(o=FAKE + 64), rtr.RTR_EINVAL),              # o overlaps q
+    (dict(lse=FAKE + 3 * MB), rtr.RTR_EINVAL),        # lse overlaps o
+    (dict(scale=float("inf")), rtr.RTR_EINVAL),
+])
+def test_block_causal_rejects_before_launch(kw, code):
+    assert _attn(**kw) == code
+    assert rtr.lib().rtr_last_error()
+
+
+def test_block_causal_empty_is_noop():
+    assert _attn(T=0, q=None, k=None, v=None, o=None) == rtr.RTR_OK
+
+
+def _cache(W=4, R=1, kpf=8, H=2, d=64, dtype=rtr.RTR_BF16):
+    fb = kpf * H * d * (2 if dtype == rtr.RTR_BF16 else 4)
+    base = FAKE
+    return rtr.KVCache(base, base + 64 * fb + 4096, base + 128 * fb + 8192,
+                       base + 130 * fb + 12288, W, R, kpf, H, d, dtype)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(W=-1), rtr.RTR_EUNSUPPORTED),
+    (dict(W=rtr.RTR_MAX_WINDOW + 1), rtr.RTR_EUNSUPPORTED),
+    (dict(R=2), rtr.RTR_EUNSUPPORTED),
+    (dict(kpf=0), rtr.RTR_EINVAL),
+    (dict(d=80), rtr.RTR_EUNSUPPORTED),
+])
+def test_create_rejects(args, code):
+    with pytest.raises(rtr.RtrError) as e:
+        _cache(**args)
+    assert e.value.code == code
+
+
+def test_create_rejects_overlapping_buffers():
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.KVCache(FAKE, FAKE + 128, FAKE + 100 * MB, FAKE + 200 * MB, 4, 1, 8, 2, 64, rtr.RTR_BF16)
+    assert e.value.code == rtr.RTR_EINVAL
+
+
+def _state(kv):
+    return rtr.rtr_kv_get_state(kv).as_dict()
+
+
+def test_failed_calls_change_nothing():
+    kv = _cache(W=3)
+    rtr.rtr_kv_commit_inplace(kv, 5)
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, None, None, 1, -1)
+    before = _state(kv)
+    L = rtr.lib()
+    h = kv.handle
+    assert L.rtr_kv_append_evict(h, None, FAKE, 1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_append_evict(h, FAKE + 3, FAKE + 64 * MB, 1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_append_evict(h, FAKE, FAKE + 64 * MB, 1, None) == rtr.RTR_EINVAL  # overlaps ring
+    assert L.rtr_kv_append_evict(h, FAKE, FAKE, -1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_reset_ref(h, 9, None, None, 1, 1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_reset_ref(h, rtr.RTR_REF_REPLACE, None, None, 2, 1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_reset_ref(h, rtr.RTR_REF_REPLACE, FAKE + 900 * MB, None, 1, 1, None) == rtr.RTR_EINVAL
+    assert L.rtr_kv_reset_ref(h, rtr.RTR_REF_KEEP, None, None, 0, -2, None) == rtr.RTR_EINVAL
+    assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
+                                  FAKE + 903 * MB, None, 0, 0, 0.0, None) == rtr.RTR_EUNSUPPORTED
+    assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
+                                  FAKE, None, 1, 0, 0.0, None) == rtr.RTR_EINVAL  # o over ring
+    assert L.rtr_attn_stream_step(h, None, FAKE + 901 * MB, FAKE + 902 * MB,
+                                  FAKE + 903 * MB, None, 1, 0, 0.0, None) == rtr.RTR_EINVAL
+    assert L.rtr_attn_stream_step(None, FAKE, FAKE, FAKE, FAKE, None, 1, 0, 0.0,
+                                  None) == rtr.RTR_EINVAL
+    bad = rtr.rtr_kv_get_state(kv)
+    bad.count = 2
+    bad.frame_id[1] = bad.frame_id[0]          # ids must increase
+    with pytest.raises(rtr.RtrError):
+        rtr.rtr_kv_set_state(kv, bad)
+    bad = rtr.rtr_kv_get_state(kv)
+    bad.window_frames = 5
+    with pytest.raises(rtr.RtrError):
+        rtr.rtr_kv_set_state(kv, bad)
+    assert _state(kv) == before
+
+
+def test_reference_replace_needs_capacity():
+    kv = _cache(R=0)
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, None, None, 1, 1)
+    assert e.value.code == rtr.RTR_ESTATE
+
+
+# ------------------------------------------------------------ ring vs ListKV
+_op = st.one_of(
+    st.tuples(st.just("append"), st.integers(0, 9)),
+    st.tuples(st.just("reset"), st.sampled_from([REF_KEEP, REF_REPLACE, REF_CLEAR]),
+              st.integers(-1, 6)),
+)
+
+
+def _check_against(kv, ref):
+    s = _state(kv)
+    assert s["count"] == len(ref.window)
+    assert s["frame_id"] == ref.frame_ids()
+    assert s["next_frame_id"] == ref.next_frame_id
+    assert s["ref_frames"] == ref.ref_frames()
+    assert s["ref_generation"] == ref.ref_generation
+    W = s["window_frames"]
+    # physical slots: distinct, in range, a ring walk from head
+    assert len(set(s["slot"])) == len(s["slot"])
+    assert all(0 <= x < max(W, 1) for x in s["slot"])
+    assert s["slot"] == [(s["head"] + p) % W for p in range(s["count"])] if W else s["slot"] == []
+
+
+@settings(max_examples=200, deadline=None)
+@given(W=st.integers(0, 7), ops=st.lists(_op, max_size=40))
+def test_ring_metadata_matches_listkv(W, ops):
+    kv = _cache(W=W)
+    ref = ListKV(W)
+    z = np.zeros((1, 1, 1, 1))
+    for op in ops:
+        if op[0] == "append":
+            n = op[1]
+            predicted = rtr.rtr_kv_next_slots(kv, n)
+            rtr.rtr_kv_commit_inplace(kv, n)
+            ref.append(np.zeros((n, 1, 1, 1)), np.zeros((n, 1, 1, 1)))
+            s = _state(kv)
+            # each surviving new frame sits where next_slots said it would
+            survivors = [p for p in predicted if p >= 0]
+            assert len(survivors) == min(n, W)
+            if survivors:
+                assert s["slot"][-len(survivors):] == survivors
+            assert predicted[:n - len(survivors)] == [-1] * (n - len(survivors))
+        else:
+            _, mode, keep = op
+            rtr.rtr_kv_reset_ref(kv, mode, None, None, 1, keep)
+            ref.reset_ref(mode, z, z, keep_recent=keep)
+        _check_against(kv, ref)
+
+
+def test_ring_matches_hand_schedule_file():
+    from tests.test_oracle import _read_schedule, MODES
+    W, ops = _read_schedule()
+    kv = _cache(W=W)
+    for op, ids, ref_gen in ops:
+        if op[0] == "append":
+            rtr.rtr_kv_commit_inplace(kv, int(op[1]))
+        else:
+            rtr.rtr_kv_reset_ref(kv, MODES[op[1]], None, None, 1, int(op[2]))
+        s = _state(kv)
+        assert s["frame_id"] == ids
+        assert (s["ref_generation"] if s["ref_frames"] else 0) == ref_gen
+
+
+def test_state_roundtrip_resume():
+    a = _cache(W=5)
+    rtr.rtr_kv_commit_inplace(a, 7)
+    rtr.rtr_kv_reset_ref(a, rtr.RTR_REF_REPLACE, None, None, 1, 2)
+    rtr.rtr_kv_commit_inplace(a, 4)
+    snap = rtr.rtr_kv_get_state(a)
+    b = _cache(W=5)
+    rtr.rtr_kv_set_state(b, snap)
+    for kv in (a, b):
+        rtr.rtr_kv_commit_inplace(kv, 3)
+        rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_CLEAR, None, None, 1, 1)
+        rtr.rtr_kv_commit_inplace(kv, 2)
+    assert _state(a) == _state(b)
