@@ -1,0 +1,257 @@
+"""Throughput of the frame-block-causal attention hot path on one MI355X.
+
+A step is one pass of the streaming hot path at steady state: the chunk's
+queries attend to the anchored reference frame, the full rolling window and the
+chunk's own frames (rtr_attn_stream_step), then the chunk's K/V are committed to
+the ring (rtr_kv_append_evict).  Default workload: the Wan-1.3B-shaped layer
+(12 heads, head_dim 128, 1560 tokens per latent frame, chunk of 3 frames,
+1 reference frame + 6-frame window), bf16 inputs, fp32 accumulation.
+
+Prints one JSON line.  `value` is algorithmic TFLOP/s of the whole step
+(4 * d * H * visible query-key pairs, masked pairs not counted) with all inputs
+resident in HBM.  `roofline` reports the attention kernel alone, timed with HIP
+events around each launch on the stream it runs on.  `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-causal attn TFLOP/s + latent frames/s per layer (frac of MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
+KERNEL_SRC = os.path.join(ROOT, "causal_attention_frame_amd", "csrc", "attn_fwd.hip")
+
+
+def stream_pairs_per_head(kpf, C, prefix_frames):
+    """Visible (query, key) pairs of one head in a streaming step: chunk frame c
+    sees the prefix frames and chunk frames 0..c."""
+    return sum(kpf * (prefix_frames * kpf + (c + 1) * kpf) for c in range(C))
+
+
+def full_pairs_per_head(T, kpf):
+    pairs = 0
+    for f0 in range(0, T, kpf):
+        rows = min(kpf, T - f0)
+        pairs += rows * min(f0 + kpf, T)
+    return pairs
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs;
+    None when absent or taken on a different kernel source."""
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["attn_hbm_bytes_per_launch_calibrated"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(workload, x, w, heads):
+    """The float64 oracle (as it stands) on `heads` heads of the same inputs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    kpf, H, d = w["k"], w["H"], w["d"]
+    sl = slice(0, heads)
+    if workload.endswith("stream_step"):
+        pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d),
+                             x["ring_k"].values.reshape(-1, H, d)])[:, sl]
+        pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d),
+                             x["ring_v"].values.reshape(-1, H, d)])[:, sl]
+        args = (pk, pv, x["q"].values[:, sl], x["k"].values[:, sl], x["v"].values[:, sl], kpf)
+        t0 = time.perf_counter()
+        oracle.attn_stream_step(*args)
+        dt = time.perf_counter() - t0
+        flops = 4 * d * heads * stream_pairs_per_head(kpf, w["C"], w["R"] + w["W"])
+        sample = (f"oracle.attn_stream_step (dense float64) on heads 0..{heads - 1} of {H}, "
+                  f"all {w['C'] * kpf} query rows")
+    else:
+        T = x["q"].shape[0]
+        rows = list(range(0, T, max(1, T // 256)))
+        t0 = time.perf_counter()
+        oracle.attn_rows(x["q"].values, x["k"].values, x["v"].values, kpf, rows, list(range(heads)))
+        dt = time.perf_counter() - t0
+        pairs = sum(min((r // kpf + 1) * kpf, T) for r in rows)
+        flops = 4 * d * heads * pairs
+        sample = f"oracle.attn_rows on {len(rows)} query rows x {heads} heads"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="wan13b_stream_step",
+                    choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal"])
+    ap.add_argument("--cpu-heads", type=int, default=12,
+                    help="heads of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the attention shards by head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from causal_attention_frame_amd import inputs as gen
+    from causal_attention_frame_amd import rtr
+
+    rtr.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = gen.WORKLOADS[args.workload]
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kpf, H, d = w["k"], w["H"], w["d"]
+    stream = torch.cuda.current_stream(dev)
+    if args.workload.endswith("stream_step"):
+        C, W, R = w["C"], w["W"], w["R"]
+        x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"],
+                              outlier_frac=w.get("outlier_frac", 0.0),
+                              outlier_scale=w.get("outlier_scale", 1.0))
+        kr = torch.empty((W, kpf, H, d), dtype=torch.bfloat16, device=dev)
+        vr = torch.empty_like(kr)
+        kf = torch.empty((R, kpf, H, d), dtype=torch.bfloat16, device=dev)
+        vf = torch.empty_like(kf)
+        kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+        rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, to_dev(x["ref_k"]), to_dev(x["ref_v"]), R, -1)
+        rtr.rtr_kv_append_evict(kv, to_dev(x["ring_k"]), to_dev(x["ring_v"]), W)
+        q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+        o = torch.empty_like(q)
+        frames = C
+        flops = 4 * d * H * stream_pairs_per_head(kpf, C, R + W)
+        append_bytes = 2 * 2 * C * kpf * H * d * 2     # K and V, read + write
+        config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
+                  "chunk_frames": C, "window_frames": W, "ref_frames": R,
+                  "query_tokens": C * kpf, "key_tokens": (R + W + C) * kpf}
+
+        def attention():
+            rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o)
+
+        def commit():
+            rtr.rtr_kv_append_evict(kv, k, v, C)
+    else:
+        F = w["frames"]
+        T = kpf * F
+        x = dict(zip("qkv", gen.full_sequence_inputs(T, H, d, "bf16", base_seed=0, wid=w["wid"])))
+        q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+        o = torch.empty_like(q)
+        frames = F - 1   # latent frames, the reference frame excluded
+        flops = 4 * d * H * full_pairs_per_head(T, kpf)
+        append_bytes = 0
+        config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
+                  "frames": F, "tokens": T}
+
+        def attention():
+            rtr.rtr_attn_block_causal(q, k, v, kpf, o=o)
+
+        def commit():
+            pass
+
+    for _ in range(args.warmup):
+        attention()
+        commit()
+    torch.cuda.synchronize(dev)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        attention()
+        ev[i][1].record(stream)
+        evc[i][0].record(stream)
+        commit()
+        evc[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+
+    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    commit_ms = np.array([a.elapsed_time(b) for a, b in evc])
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    achieved = flops / attn_avg_s / 1e12
+    traffic = read_traffic(args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "latent_frames_per_s_per_layer": round(frames / (ms_per_step * 1e-3), 1),
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_fwd_bf16",
+            "kernel_avg_us": round(attn_avg_s * 1e6, 2),
+            "kernel_min_us": round(float(attn_ms.min()) * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
+        },
+    }
+    if append_bytes:
+        cs = float(np.median(commit_ms)) * 1e-3
+        out["kv_append"] = {"bound": "hbm", "median_us": round(cs * 1e6, 2),
+                            "achieved": round(append_bytes / cs / 1e9, 1), "unit": "GB/s",
+                            "peak": PEAK_HBM_GBS,
+                            "frac": round(append_bytes / cs / 1e9 / PEAK_HBM_GBS, 4),
+                            "algorithmic_bytes": append_bytes}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, x, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
