@@ -28,6 +28,7 @@
 // thread), used where float32 accuracy is required; not tuned.
 
 #include <cmath>
+#include <type_traits>
 
 #include "rtr_internal.h"
 
@@ -48,6 +49,7 @@ struct KArgs {
     float *lse;
     const void *kseg[kMaxKeyFrames];
     const void *vseg[kMaxKeyFrames];
+    int32_t nseg;        // segments in the table
     int32_t seg_len;     // keys per segment (all keys when there is one segment)
     float inv_seg_len;   // 1 / seg_len, for the segment lookup
     int32_t Tq, Tk, kpf, prefix;
@@ -95,13 +97,45 @@ __device__ inline long key_offset(int j, const KArgs &a, int &f) {
     return (long)j * a.ld;
 }
 
-__device__ inline float wave_shfl_xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Value of the same register in lane (lane ^ 32), combined with this lane's
+// by max or sum: v_permlane32_swap exchanges the two 32-lane halves in place.
+__device__ inline float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// 16-byte load through a global (not flat) address.
+__device__ inline u32x4 gload16(const uint16_t *p) { return *(const global_u32x4 *)p; }
+
+// Key addressing modes of the bf16 kernel.
+enum SegMode : int {
+    kContiguous = 0,  // one segment holds every key
+    kSegAligned = 1,  // frame segments whose length is a multiple of 4 keys
+    kSegGeneric = 2,  // frame segments of any length
+};
 
 // ---------------------------------------------------------------------------
 // bf16 inputs, MFMA path.
 // ---------------------------------------------------------------------------
-template <int D, bool SEG>
-__global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
+
+// Online-softmax rescaling threshold in log2 units.  A row's reference max m is
+// raised (and its O and l rescaled) only when a tile's row max exceeds m by
+// more than this, so P = exp2((s - m) * scale * log2 e) < 2^8.  The softmax is
+// unchanged (O and l share the reference); only rounding differs, and the
+// O/l rescale, which touches every accumulator register, runs a few times per
+// row instead of once per tile.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D, int SEGMODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_bf16(const KArgs a) {
+    constexpr bool SEG = SEGMODE != kContiguous;
     constexpr int BM = 128;         // query rows per workgroup (4 waves x 32)
     constexpr int BN = 64;          // keys per tile
     constexpr int KP = D + 8;       // LDS pitch of a K row (elements)
@@ -111,9 +145,13 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
     constexpr int NT = D / 32;      // 32-wide column blocks of O^T
     constexpr int ITEMS = (BN / 4) * DC;  // loader items: 4 keys x 16 bytes
     static_assert(ITEMS <= 256, "tile loader needs at most one item per thread");
+    static_assert(BN == 64, "the V^T swizzle assumes 8 blocks of 8 keys per row");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VP];
+    // Double-buffered K and V^T tiles: tile t lives in buffer t & 1.
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * VP];
+    __shared__ const uint16_t *sSegK[SEG ? kMaxKeyFrames : 1];
+    __shared__ const uint16_t *sSegV[SEG ? kMaxKeyFrames : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -128,9 +166,16 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
     const bool qvalid = qi < a.Tq;
     const int qc = qvalid ? qi : a.Tq - 1;
     const int lim = key_limit(qc, a);
+    const int lim_wg_lo = key_limit(q0, a);
     const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
-    const int wlim_lo = key_limit(min(q0 + wave * 32, a.Tq - 1), a);
     const int wlim_hi = key_limit(min(q0 + wave * 32 + 31, a.Tq - 1), a);
+
+    if (SEG) {
+        for (int f = tid; f < a.nseg; f += 256) {
+            sSegK[f] = (const uint16_t *)a.kseg[f];
+            sSegV[f] = (const uint16_t *)a.vseg[f];
+        }
+    }
 
     // Q^T as the B operand: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
     bf16x8 qf[NS];
@@ -142,6 +187,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
             qf[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
+    if (SEG) __syncthreads();  // segment table visible to the loader
 
     // Tile loader: item (a4, ch) moves keys 4*a4 .. 4*a4+3, 16-byte chunk ch.
     const bool loader = tid < ITEMS;
@@ -149,30 +195,70 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
     u32x4 kreg[4], vreg[4];
 
     auto load_tile = [&](int j0) {
+        const int jb = j0 + 4 * a4;
+        if (SEGMODE == kSegGeneric) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = j0 + 4 * a4 + r;
-            if (loader && j < a.Tk) {
-                int f;
-                const long off = key_offset<SEG>(j, a, f) + hoff + ch * 8;
-                kreg[r] = *(const u32x4 *)((const uint16_t *)a.kseg[f] + off);
-                vreg[r] = *(const u32x4 *)((const uint16_t *)a.vseg[f] + off);
-            } else {
-                kreg[r] = u32x4{0, 0, 0, 0};
-                vreg[r] = u32x4{0, 0, 0, 0};
+            for (int r = 0; r < 4; ++r) {
+                const int j = jb + r;
+                if (loader && j < a.Tk) {
+                    const int f = seg_of(j, a);
+                    const long o = (long)(j - f * a.seg_len) * a.ld + hoff + ch * 8;
+                    kreg[r] = gload16(sSegK[f] + o);
+                    vreg[r] = gload16(sSegV[f] + o);
+                } else {
+                    kreg[r] = u32x4{0, 0, 0, 0};
+                    vreg[r] = u32x4{0, 0, 0, 0};
+                }
+            }
+            return;
+        }
+        // The 4 rows jb .. jb+3 lie in one segment (segments are multiples of
+        // 4 keys, jb is a multiple of 4).
+        const uint16_t *kb, *vb;
+        long o;
+        if (SEGMODE == kSegAligned) {
+            const int f = min(seg_of(jb, a), a.nseg - 1);
+            kb = sSegK[f];
+            vb = sSegV[f];
+            o = (long)(jb - f * a.seg_len) * a.ld + hoff + ch * 8;
+        } else {
+            kb = (const uint16_t *)a.kseg[0];
+            vb = (const uint16_t *)a.vseg[0];
+            o = (long)jb * a.ld + hoff + ch * 8;
+        }
+        if (loader && jb + 3 < a.Tk) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                kreg[r] = gload16(kb + o + r * a.ld);
+                vreg[r] = gload16(vb + o + r * a.ld);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (loader && jb + r < a.Tk) {
+                    kreg[r] = gload16(kb + o + r * a.ld);
+                    vreg[r] = gload16(vb + o + r * a.ld);
+                } else {
+                    kreg[r] = u32x4{0, 0, 0, 0};
+                    vreg[r] = u32x4{0, 0, 0, 0};
+                }
             }
         }
     };
 
-    auto store_tile = [&]() {
+    auto store_tile = [&](int buf) {
         if (!loader) return;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *(u32x4 *)&sK[(4 * a4 + r) * KP + ch * 8] = kreg[r];
+        for (int r = 0; r < 4; ++r) *(u32x4 *)&sK[buf][(4 * a4 + r) * KP + ch * 8] = kreg[r];
         // V^T with keys permuted inside each 16-key group: key group a (4 keys)
         // goes to position ((a&1)<<3)|((a>>1)<<2), so that lane half g of the
         // MFMA B operand finds its 8 keys {4g..4g+3, 8+4g..8+4g+3} contiguous.
+        // Each row's eight 8-key blocks are XOR-swizzled by (row / 8) mod 8 so
+        // the 16 threads writing rows 8 apart spread over the LDS banks; reads
+        // of 8 consecutive rows stay conflict-free through the row padding.
         const int a = a4 & 3;
-        const int pos = (a4 >> 2) * 16 + (((a & 1) << 3) | ((a >> 1) << 2));
+        const int blk = ((a4 >> 2) * 2 + (a & 1)) ^ (ch & 7);
+        const int pos = blk * 8 + (a >> 1) * 4;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int w = e >> 1, sh = (e & 1) * 16;
@@ -180,7 +266,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
             const uint32_t x1 = (vreg[1][w] >> sh) & 0xffffu;
             const uint32_t x2 = (vreg[2][w] >> sh) & 0xffffu;
             const uint32_t x3 = (vreg[3][w] >> sh) & 0xffffu;
-            *(u32x2 *)&sVt[(ch * 8 + e) * VP + pos] = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+            *(u32x2 *)&sVt[buf][(ch * 8 + e) * VP + pos] = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
         }
     };
 
@@ -189,31 +275,27 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
     for (int t = 0; t < NT; ++t) acc[t] = f32x16{};
     float m = -INFINITY, l = 0.f;
     const float c = a.c;
+    const float grow_thr = kRescaleLog2 / c;
 
-    const int ntiles = (lim_wg + BN - 1) / BN;
-    load_tile(0);
-    for (int it = 0; it < ntiles; ++it) {
+    // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+    auto step = [&](auto masked, int it) {
+        constexpr bool MASK = decltype(masked)::value;
         const int j0 = it * BN;
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (it + 1 < ntiles) load_tile(j0 + BN);
-        if (j0 >= wlim_hi) continue;  // every row of this wave is past its limit
-        const bool partial = j0 + BN > wlim_lo;
-
-        // S^T = K Q^T : lane holds query n, keys 32 kt + 8 (r/4) + 4 g + (r%4).
+        const uint16_t *Kt = sK[it & 1];
+        const uint16_t *Vt = sVt[it & 1];
+        // lane holds query n and keys 32 kt + 8 (r/4) + 4 g + (r%4)
         f32x16 s[BN / 32];
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt) {
             s[kt] = f32x16{};
 #pragma unroll
             for (int st = 0; st < NS; ++st) {
-                const u32x4 raw = *(const u32x4 *)&sK[(32 * kt + n) * KP + 16 * st + 8 * g];
+                const u32x4 raw = *(const u32x4 *)&Kt[(32 * kt + n) * KP + 16 * st + 8 * g];
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, raw), qf[st], s[kt], 0, 0, 0);
             }
         }
-        if (partial) {
+        if (MASK) {
 #pragma unroll
             for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
@@ -222,44 +304,68 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16(const KArgs a) {
                     if (j >= lim) s[kt][r] = -INFINITY;
                 }
         }
-
         float mx = s[0][0];
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, wave_shfl_xor32(mx));
-        const float m_new = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-        m = m_new;
-        const float mc = m_new * c;
-
+        mx = pair_max(mx);
+        // The branch is taken by the whole wave when any row needs it, but
+        // only rows that crossed the threshold change their reference (the
+        // others multiply by exactly 1), so each row's result depends on its
+        // own keys only.
+        const bool grow = mx > m + grow_thr;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float m_new = grow ? fmaxf(m, mx) : m;
+            const float alpha = grow ? __builtin_amdgcn_exp2f((m - m_new) * c) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[t] *= alpha;
+            m = m_new;
+        }
+        const float mc = m * c;
         bf16x8 pf[BN / 16];
-        float rs = 0.f;
 #pragma unroll
         for (int kt = 0; kt < BN / 32; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -mc));
-                rs += p;
+                l += p;
                 pf[2 * kt + (r >> 3)][r & 7] = (__bf16)p;
             }
-        l = l * alpha + rs;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[t] *= alpha;
-
-        // O^T += V^T P^T
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int st = 0; st < BN / 16; ++st) {
-                const u32x4 raw = *(const u32x4 *)&sVt[(32 * t + n) * VP + 16 * st + 8 * g];
+                const int row = 32 * t + n;
+                const int blk = (2 * st + g) ^ ((row >> 3) & 7);
+                const u32x4 raw = *(const u32x4 *)&Vt[row * VP + blk * 8];
                 acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(bf16x8, raw), pf[st], acc[t], 0, 0, 0);
             }
+    };
+
+    const int ntiles = (lim_wg + BN - 1) / BN;
+    const int nfull = min(ntiles, lim_wg_lo / BN);  // tiles visible to every row here
+    load_tile(0);
+    store_tile(0);
+    if (ntiles > 1) load_tile(BN);
+    __syncthreads();
+    int it = 0;
+    for (; it < nfull; ++it) {
+        if (it + 1 < ntiles) store_tile((it + 1) & 1);
+        if (it + 2 < ntiles) load_tile((it + 2) * BN);
+        step(std::false_type{}, it);
+        __syncthreads();
+    }
+    for (; it < ntiles; ++it) {
+        if (it + 1 < ntiles) store_tile((it + 1) & 1);
+        if (it + 2 < ntiles) load_tile((it + 2) * BN);
+        if (it * BN < wlim_hi) step(std::true_type{}, it);  // wave-uniform
+        __syncthreads();
     }
 
-    const float lt = l + wave_shfl_xor32(l);
+    const float lt = pair_sum(l);
     const float inv = 1.f / lt;
     if (qvalid) {
         const long obase = (long)qi * a.ld + hoff;
@@ -370,7 +476,12 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
     if (p.in_dtype == RTR_BF16) {
         k.nqb = (int)((p.Tq + 127) / 128);
         k.nwg = k.nqb * p.H;
-        hipLaunchKernelGGL((attn_fwd_bf16<D, SEG>), dim3(k.nwg), dim3(256), 0, stream, k);
+        if (!SEG)
+            hipLaunchKernelGGL((attn_fwd_bf16<D, kContiguous>), dim3(k.nwg), dim3(256), 0, stream, k);
+        else if (k.seg_len % 4 == 0)
+            hipLaunchKernelGGL((attn_fwd_bf16<D, kSegAligned>), dim3(k.nwg), dim3(256), 0, stream, k);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16<D, kSegGeneric>), dim3(k.nwg), dim3(256), 0, stream, k);
     } else {
         k.nqb = (int)((p.Tq + 63) / 64);
         k.nwg = k.nqb * p.H;
@@ -390,6 +501,7 @@ hipError_t launch_attention(const AttnProblem &p, hipStream_t stream) {
         k.kseg[f] = p.kseg[f];
         k.vseg[f] = p.vseg[f];
     }
+    k.nseg = p.nseg;
     k.seg_len = (int32_t)p.seg_len;
     k.inv_seg_len = 1.0f / (float)p.seg_len;
     k.Tq = (int32_t)p.Tq;
