@@ -116,7 +116,9 @@ __device__ inline u32x4 gload16(const uint16_t *p) { return *(const global_u32x4
 // Key addressing modes of the bf16 kernel.
 enum SegMode : int {
     kContiguous = 0,  // one segment holds every key
-    kSegAligned = 1,  // frame segments whose length is a multiple of 4 keys
+    kSegAligned = 1,  // frame segments long enough for the kernel's fast path
+                      // (>= 4 keys and a multiple of 4 for the 64-query-block
+                      // kernel; >= 32 keys for the head_dim-128 kernel)
     kSegGeneric = 2,  // frame segments of any length
 };
 
@@ -391,6 +393,415 @@ void attn_fwd_bf16(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 inputs, head_dim 128: 64 query rows per wave, K/V staged by LDS DMA.
+// ---------------------------------------------------------------------------
+// A workgroup is 4 waves x 64 query rows; each wave owns two 32-row MFMA
+// blocks, so every K/V fragment read from LDS feeds two MFMAs.  Keys advance in
+// 32-key tiles held in a 3-stage LDS ring that global_load_lds fills two tiles
+// ahead of the compute (16 bytes per lane go straight from global memory to
+// LDS: no staging registers, no VALU).  Layout of a stage (row-major, 256 B
+// per key row):
+//   K: the 16-byte chunks of row r are XOR-swizzled by r mod 8, which spreads
+//      the ds_read_b128 of the MFMA A operand (lane n reads row n) over banks;
+//   V: the 32-byte chunk pairs of row r are XOR-swizzled by r mod 4 and the
+//      tile is read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
+//      lane one d column over 4 keys -- the V^T A operand of the PV MFMA in the
+//      key order of the S^T accumulator, with no transposed copy anywhere.
+// Synchronisation: one s_barrier per tile, after each wave has waited for its
+// own DMA of that tile (vmcnt), so later prefetches stay in flight.
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+
+// A zero key/value row: out-of-range keys of the last tile are loaded from it.
+__device__ __attribute__((aligned(16))) const uint16_t kZeroRow[128] = {};
+
+__device__ inline void lds_dma16(const uint16_t *src, uint16_t *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                     (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+}
+
+__device__ inline v4i16 lds_tr16(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4): all but this wave's 4 newest loads done
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+template <int SEGMODE>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
+    constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
+    constexpr bool SEG = SEGMODE != kContiguous;
+    // Four LDS stages, each a separate array so that the compiler can tell a
+    // DMA into one stage from reads of another (and does not drain the
+    // prefetches before every read).  Tile t lives in stage t mod 4.
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[BN * D], sK1[BN * D], sK2[BN * D], sK3[BN * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[BN * D], sV1[BN * D], sV2[BN * D], sV3[BN * D];
+    __shared__ const uint16_t *sSegK[SEG ? kMaxKeyFrames : 1];
+    __shared__ const uint16_t *sSegV[SEG ? kMaxKeyFrames : 1];
+    __shared__ int sRedo;
+
+    auto kst = [&](auto S) -> uint16_t * {
+        constexpr int v = decltype(S)::value & 3;
+        if constexpr (v == 0) return sK0;
+        else if constexpr (v == 1) return sK1;
+        else if constexpr (v == 2) return sK2;
+        else return sK3;
+    };
+    auto vst = [&](auto S) -> uint16_t * {
+        constexpr int v = decltype(S)::value & 3;
+        if constexpr (v == 0) return sV0;
+        else if constexpr (v == 1) return sV1;
+        else if constexpr (v == 2) return sV2;
+        else return sV3;
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+
+    int head, qb;
+    map_block(blockIdx.x, a.nwg, a.nqb, head, qb);
+    const int q0 = qb * BM;
+    const long hoff = (long)head * D;
+
+    int qi[2], lim[2];
+    bool qv[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        qi[b] = q0 + 64 * wave + 32 * b + n;
+        qv[b] = qi[b] < a.Tq;
+        lim[b] = key_limit(qv[b] ? qi[b] : a.Tq - 1, a);
+    }
+    const int lim_wg_lo = key_limit(q0, a);
+    const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
+
+    if (SEG) {
+        for (int f = tid; f < a.nseg; f += 256) {
+            sSegK[f] = (const uint16_t *)a.kseg[f];
+            sSegV[f] = (const uint16_t *)a.vseg[f];
+        }
+    }
+    if (tid == 0) sRedo = 0;
+    __syncthreads();
+
+    // Q^T B operands of both blocks: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
+    bf16x8 qf[2][NS];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const uint16_t *qrow = (const uint16_t *)a.q + (long)(qv[b] ? qi[b] : a.Tq - 1) * a.ld + hoff;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u32x4 raw = qv[b] ? gload16(qrow + 16 * s + 8 * g) : u32x4{0, 0, 0, 0};
+            qf[b][s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+
+    // DMA: this lane fills rows lrow + 4 i (i = 0, 1) of each tile, physical
+    // 16-byte chunk pch; it fetches the logical chunk that the swizzle puts there.
+    const int lrow = 8 * wave + (lane >> 4);
+    const int pch = lane & 15;
+    int kch[2], vch[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = lrow + 4 * i;
+        kch[i] = pch ^ (r & 7);
+        vch[i] = (((pch >> 1) ^ (r & 3)) << 1) | (pch & 1);
+    }
+
+    // Key cursor of the next tile to prefetch (tiles are prefetched in order
+    // within a sweep): frame segment cf and key offset co inside it.  Both are
+    // wave-uniform, so the per-lane address work is a select and a multiply-add.
+    int cf = 0, co = 0;
+    auto reset_cursor = [&]() {
+        cf = 0;
+        co = 0;
+    };
+    auto issue = [&](int tile, auto S) {
+        const int j0 = tile * BN;
+        if (SEGMODE == kSegGeneric) {  // frames shorter than a tile: per-lane lookup
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = j0 + lrow + 4 * i;
+                const uint16_t *kp = kZeroRow + kch[i] * 8;
+                const uint16_t *vp = kZeroRow + vch[i] * 8;
+                if (j < a.Tk) {
+                    const int f = seg_of(j, a);
+                    const long o = (long)(j - f * a.seg_len) * a.ld + hoff;
+                    kp = sSegK[f] + o + kch[i] * 8;
+                    vp = sSegV[f] + o + vch[i] * 8;
+                }
+                lds_dma16(kp, kst(S) + (8 * wave + 4 * i) * D);
+                lds_dma16(vp, vst(S) + (8 * wave + 4 * i) * D);
+            }
+            return;
+        }
+        const uint16_t *kb0, *kb1, *vb0, *vb1;
+        int bnd;  // rows >= bnd of this tile lie in the next segment
+        long srow;  // element offset of the tile's first row inside its segment, plus the head
+        if (SEGMODE == kSegAligned) {
+            const int f1 = min(cf + 1, a.nseg - 1);
+            kb0 = (const uint16_t *)a.kseg[cf];
+            vb0 = (const uint16_t *)a.vseg[cf];
+            kb1 = (const uint16_t *)a.kseg[f1];
+            vb1 = (const uint16_t *)a.vseg[f1];
+            bnd = a.seg_len - co;
+            srow = (long)co * a.ld + hoff;
+            co += BN;  // advance to the next tile (a segment holds >= BN keys)
+            if (co >= a.seg_len) {
+                co -= a.seg_len;
+                cf = min(cf + 1, a.nseg - 1);
+            }
+        } else {
+            kb0 = kb1 = (const uint16_t *)a.kseg[0];
+            vb0 = vb1 = (const uint16_t *)a.vseg[0];
+            bnd = 1 << 30;
+            srow = (long)j0 * a.ld + hoff;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = lrow + 4 * i;
+            const bool nxt = r >= bnd;
+            const int rr = nxt ? r - a.seg_len : r;
+            const long o = srow + (long)rr * a.ld;
+            const bool ok = j0 + r < a.Tk;
+            const uint16_t *kp = ok ? (nxt ? kb1 : kb0) + o + kch[i] * 8 : kZeroRow + kch[i] * 8;
+            const uint16_t *vp = ok ? (nxt ? vb1 : vb0) + o + vch[i] * 8 : kZeroRow + vch[i] * 8;
+            lds_dma16(kp, kst(S) + (8 * wave + 4 * i) * D);
+            lds_dma16(vp, vst(S) + (8 * wave + 4 * i) * D);
+        }
+    };
+
+    // Per-lane LDS offsets (elements) that do not depend on the tile.
+    int koff[NS];
+#pragma unroll
+    for (int st = 0; st < NS; ++st) koff[st] = n * D + (((2 * st + g) ^ (n & 7)) << 3);
+    const int G = lane >> 4, sl = lane & 15;
+    const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 st + 8 h
+    int voff[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) voff[t] = vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+
+    // Softmax with a fixed per-row exponent reference (log2 units): P =
+    // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
+    // P <= 1 there; later tiles may exceed it, which is harmless while the
+    // running sum stays far from the fp32 range.  A row whose sum ends above
+    // 2^64 (or overflows) is recomputed in a second pass with its exact row max
+    // as reference.  The accumulators are therefore touched only by MFMAs inside
+    // the key loop.  Each row's result depends on its own scores only.
+    f32x16 acc[2][NT];
+    float mref[2] = {0.f, 0.f}, l[2] = {0.f, 0.f}, mmax[2] = {-INFINITY, -INFINITY};
+    const float c = a.c;
+
+    const int ntiles = (lim_wg + BN - 1) / BN;
+    const int nfull = min(ntiles, lim_wg_lo / BN);  // tiles visible to every row here
+
+    // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
+    // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
+    // transposed 8-byte reads each).
+    auto read_k = [&](auto S, bf16x8 *kf) {
+        const uint16_t *Kt = kst(S);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(const u32x4 *)&Kt[koff[st]]);
+    };
+    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
+        const uint16_t *Vt = vst(S);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                vf[t][st][0] = lds_tr16(&Vt[voff[t] + (16 * st) * D]);
+                vf[t][st][1] = lds_tr16(&Vt[voff[t] + (16 * st + 8) * D]);
+            }
+    };
+    // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
+    auto qk = [&](const bf16x8 *kf, f32x16 *s) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], s[1], 0, 0, 0);
+        }
+    };
+    auto apply_mask = [&](f32x16 *s, int tile) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (tile * BN + 8 * (r >> 2) + 4 * g + (r & 3) >= lim[b]) s[b][r] = -INFINITY;
+    };
+    auto rowmax = [&](const f32x16 &s) {
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return pair_max(mx);
+    };
+    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2]) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -mref[b]));
+                l[b] += p;
+                pf[b][r >> 3][r & 7] = (__bf16)p;
+            }
+    };
+    // O^T += V^T P^T.
+    auto pv = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2]) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const bf16x8 v = __builtin_bit_cast(
+                    bf16x8, (v8i16)__builtin_shufflevector(vf[t][st][0], vf[t][st][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[0][st], acc[0][t], 0, 0, 0);
+                acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[1][st], acc[1][t], 0, 0, 0);
+            }
+    };
+
+    // Software pipeline over key tiles.  Step t (stage t mod 4): wait until
+    // this wave's DMA of tile t+1 has landed (tile t+2 may still be in
+    // flight), barrier (every wave's DMA of t+1 has landed; every wave is done
+    // with tile t-1, whose stage takes tile t+3), prefetch tile t+3, then in one
+    // basic block: S(t+1) on the matrix cores while the VALU turns S(t) into P,
+    // followed by O += V(t) P.  Steps past the last tile are fully masked (P =
+    // 0) and only keep the DMA counts static.
+    f32x16 scur[2];
+    auto step = [&](int t, auto S, auto masked, auto maxonly) {
+        constexpr bool MASK = decltype(masked)::value;
+        constexpr bool MAXONLY = decltype(maxonly)::value;
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        // All fragment reads first (K of tile t+1, V of tile t), so their LDS
+        // latency hides behind the MFMAs and VALU work that follows.
+        bf16x8 kf[NS];
+        v4i16 vf[NT][2][2];
+        read_k(std::integral_constant<int, (decltype(S)::value + 1) & 3>{}, kf);
+        if (!MAXONLY) read_v(S, vf);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 snext[2];
+        qk(kf, snext);
+        if (MASK) apply_mask(scur, t);
+        if (MAXONLY) {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+        } else {
+            bf16x8 pf[2][2];
+            softmax(scur, pf);
+            pv(vf, pf);
+        }
+        issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+    };
+    auto sweep = [&](bool first_sweep, auto maxonly) {
+        reset_cursor();
+        issue(0, I0{});
+        issue(1, I1{});
+        issue(2, I2{});
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 landed
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        {
+            bf16x8 kf[NS];
+            read_k(I0{}, kf);
+            qk(kf, scur);
+        }
+        if (first_sweep) {
+            if (0 >= nfull) apply_mask(scur, 0);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) mref[b] = rowmax(scur[b]) * c;
+        }
+        // Groups of four steps (static stages): unmasked while the whole group
+        // is visible to every row, masked from there on.
+        int base = 0;
+#pragma unroll 1
+        for (; base + 4 <= nfull; base += 4) {
+            step(base, I0{}, std::false_type{}, maxonly);
+            step(base + 1, I1{}, std::false_type{}, maxonly);
+            step(base + 2, I2{}, std::false_type{}, maxonly);
+            step(base + 3, I3{}, std::false_type{}, maxonly);
+        }
+#pragma unroll 1
+        for (; base < ntiles; base += 4) {
+            step(base, I0{}, std::true_type{}, maxonly);
+            step(base + 1, I1{}, std::true_type{}, maxonly);
+            step(base + 2, I2{}, std::true_type{}, maxonly);
+            step(base + 3, I3{}, std::true_type{}, maxonly);
+        }
+        // drain the look-ahead tiles before the stages are reused
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        compiler_fence();
+    };
+
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
+    sweep(true, std::false_type{});
+
+    // Rare second pass for rows whose sum left the safe range.
+    const float kSafeSum = 18446744073709551616.f;  // 2^64
+    bool redo[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
+    if (__builtin_amdgcn_ballot_w64(redo[0] || redo[1]) && lane == 0) sRedo = 1;
+    __syncthreads();
+    if (sRedo) {
+        asm volatile("");
+        sweep(false, std::true_type{});  // exact row maxima
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (redo[b]) mref[b] = mmax[b] * c;
+            l[b] = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
+        }
+        sweep(false, std::false_type{});
+    }
+
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const float lt = pair_sum(l[b]);
+        const float inv = 1.f / lt;
+        if (!qv[b]) continue;
+        const long obase = (long)qi[b] * a.ld + hoff;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int dcol = 32 * t + 8 * i + 4 * g;
+                const float o0 = acc[b][t][4 * i + 0] * inv, o1 = acc[b][t][4 * i + 1] * inv;
+                const float o2 = acc[b][t][4 * i + 2] * inv, o3 = acc[b][t][4 * i + 3] * inv;
+                if (a.out_f32) {
+                    *(f32x4 *)((float *)a.o + obase + dcol) = f32x4{o0, o1, o2, o3};
+                } else {
+                    const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)o0);
+                    const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)o1);
+                    const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)o2);
+                    const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)o3);
+                    *(u32x2 *)((uint16_t *)a.o + obase + dcol) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+                }
+            }
+        if (g == 0 && a.lse) a.lse[(long)head * a.Tq + qi[b]] = mref[b] / kLog2e + logf(lt);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs, VALU path: one query row per thread, 32-key tiles in LDS.
 // ---------------------------------------------------------------------------
 template <int D, bool SEG>
@@ -473,7 +884,16 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const KArgs a) {
 template <int D, bool SEG>
 hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
     KArgs k = ka;
-    if (p.in_dtype == RTR_BF16) {
+    if (p.in_dtype == RTR_BF16 && D == 128) {
+        k.nqb = (int)((p.Tq + 255) / 256);
+        k.nwg = k.nqb * p.H;
+        if (!SEG)
+            hipLaunchKernelGGL((attn_fwd_bf16_d128<kContiguous>), dim3(k.nwg), dim3(256), 0, stream, k);
+        else if (k.seg_len >= 32)
+            hipLaunchKernelGGL((attn_fwd_bf16_d128<kSegAligned>), dim3(k.nwg), dim3(256), 0, stream, k);
+        else
+            hipLaunchKernelGGL((attn_fwd_bf16_d128<kSegGeneric>), dim3(k.nwg), dim3(256), 0, stream, k);
+    } else if (p.in_dtype == RTR_BF16) {
         k.nqb = (int)((p.Tq + 127) / 128);
         k.nwg = k.nqb * p.H;
         if (!SEG)

@@ -331,3 +331,26 @@ def test_full_size_stream_closed_form_labels():
                                                 device="cuda"), vch.view(C, kpf, H, d), C)
         ref.append(np.zeros((C, 1)), np.zeros((C, 1)))
         fid += C
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_softmax_reference_fallback_rows(out):
+    # Rows whose scores grow far beyond their first key tile's maximum (here
+    # by 512 / sqrt(128) natural units, i.e. a factor 2^65 in the softmax
+    # numerator) take the exact-maximum second pass; rows of the same
+    # workgroup with flat scores do not.  Both must match the oracle.
+    T, H, d = 600, 2, 128
+    rng = np.random.default_rng(7)
+    q = np.zeros((T, H, d), dtype=np.float32)
+    q[::2] = 1.0                                   # even rows: large growth, odd rows: flat
+    k = np.zeros((T, H, d), dtype=np.float32)
+    k[40:] = 4.0                                   # first 32-key tile scores 0, later 512
+    k[300:310] = -4.0
+    v = rng.standard_normal((T, H, d)).astype(np.float32)
+    q, k, v = (gen.from_values(gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x)), "bf16")
+               for x in (q, k, v))
+    for kpf in (T, 100):
+        o, lse = _run_full(q, k, v, kpf, TORCH_DT[out])
+        ro, rl = oracle.attn_block_causal(q.values, k.values, v.values, kpf)
+        assert_bf16_close(o, ro, f"o k={kpf}")
+        assert_bf16_close(lse, rl, f"lse k={kpf}")
