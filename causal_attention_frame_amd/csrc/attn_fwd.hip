@@ -548,11 +548,14 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         int bnd;  // rows >= bnd of this tile lie in the next segment
         long srow;  // element offset of the tile's first row inside its segment, plus the head
         if (SEGMODE == kSegAligned) {
+            // The LDS copy of the segment table, not the kernel arguments:
+            // scalar loads return out of order and would make every LDS wait
+            // in the loop a full drain.
             const int f1 = min(cf + 1, a.nseg - 1);
-            kb0 = (const uint16_t *)a.kseg[cf];
-            vb0 = (const uint16_t *)a.vseg[cf];
-            kb1 = (const uint16_t *)a.kseg[f1];
-            vb1 = (const uint16_t *)a.vseg[f1];
+            kb0 = sSegK[cf];
+            vb0 = sSegV[cf];
+            kb1 = sSegK[f1];
+            vb1 = sSegV[f1];
             bnd = a.seg_len - co;
             srow = (long)co * a.ld + hoff;
             co += BN;  // advance to the next tile (a segment holds >= BN keys)
@@ -689,8 +692,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         bf16x8 kf[NS];
         v4i16 vf[NT][2][2];
         read_k(std::integral_constant<int, (decltype(S)::value + 1) & 3>{}, kf);
+        __builtin_amdgcn_sched_barrier(0);  // the K reads go first
         if (!MAXONLY) read_v(S, vf);
-        __builtin_amdgcn_sched_barrier(0);
         f32x16 snext[2];
         qk(kf, snext);
         if (MASK) apply_mask(scur, t);
@@ -703,6 +706,24 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
             pv(vf, pf);
         }
         issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
+        if (!MAXONLY) {
+            // Schedule after the K reads (LDS reads are counted by a 4-bit
+            // lgkmcnt, so keep few outstanding for precise waits): the QK(t+1)
+            // MFMAs interleaved with the softmax VALU of tile t and one V read
+            // each, then the PV(t) MFMAs interleaved with the prefetch address
+            // VALU.
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
+        }
         scur[0] = snext[0];
         scur[1] = snext[1];
     };
