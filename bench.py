@@ -235,7 +235,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_bf16",
+            "kernel": "attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16",
             "kernel_avg_us": round(attn_avg_s * 1e6, 2),
             "kernel_min_us": round(float(attn_ms.min()) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
