@@ -47,8 +47,10 @@ struct KArgs {
     const void *q;
     void *o;
     float *lse;
-    const void *kseg[kMaxKeyFrames];
-    const void *vseg[kMaxKeyFrames];
+    // Segment base pointers; entry nseg repeats entry nseg - 1, so that a
+    // segment and its successor can be read as one pair.
+    const void *kseg[kMaxKeyFrames + 1];
+    const void *vseg[kMaxKeyFrames + 1];
     int32_t nseg;        // segments in the table
     int32_t seg_len;     // keys per segment (all keys when there is one segment)
     float inv_seg_len;   // 1 / seg_len, for the segment lookup
@@ -397,10 +399,10 @@ void attn_fwd_bf16(const KArgs a) {
 // ---------------------------------------------------------------------------
 // A workgroup is 4 waves x 64 query rows; each wave owns two 32-row MFMA
 // blocks, so every K/V fragment read from LDS feeds two MFMAs.  Keys advance in
-// 32-key tiles held in a 3-stage LDS ring that global_load_lds fills two tiles
-// ahead of the compute (16 bytes per lane go straight from global memory to
-// LDS: no staging registers, no VALU).  Layout of a stage (row-major, 256 B
-// per key row):
+// 32-key tiles held in a 4-stage LDS ring that global_load_lds fills three
+// tiles ahead of the compute (16 bytes per lane go straight from global memory
+// to LDS: no staging registers, no VALU).  Layout of a stage (row-major, 256 B
+// per key row, K tile then V tile):
 //   K: the 16-byte chunks of row r are XOR-swizzled by r mod 8, which spreads
 //      the ds_read_b128 of the MFMA A operand (lane n reads row n) over banks;
 //   V: the 32-byte chunk pairs of row r are XOR-swizzled by r mod 4 and the
@@ -409,63 +411,103 @@ void attn_fwd_bf16(const KArgs a) {
 //      key order of the S^T accumulator, with no transposed copy anywhere.
 // Synchronisation: one s_barrier per tile, after each wave has waited for its
 // own DMA of that tile (vmcnt), so later prefetches stay in flight.
+//
+// The DMA is issued from inline assembly.  The compiler models a
+// global-to-LDS load as touching both the vector-memory and the LDS counters
+// and, while one is in flight, turns every LDS wait into a full drain; issued
+// this way it is invisible to that model, the fragment reads get exact
+// lgkmcnt waits, and the kernel waits for the DMA itself (vmcnt, in order).
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-// A zero key/value row: out-of-range keys of the last tile are loaded from it.
+// A zero key/value row: keys past the end of a ragged key range are loaded from it.
 __device__ __attribute__((aligned(16))) const uint16_t kZeroRow[128] = {};
 
-__device__ inline void lds_dma16(const uint16_t *src, uint16_t *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                     (__attribute__((address_space(3))) void *)lds_wave_base, 16, 0, 0);
+__device__ inline uint32_t lds_addr(const lds_u16 *p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ inline v4i16 lds_tr16(const lds_u16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
 }
 
-__device__ inline v4i16 lds_tr16(const uint16_t *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16 *)p);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber is still honoured
+// 16 bytes per lane from global memory to LDS byte address m0 + 16 * lane.
+// Source: a wave-uniform 64-bit base in SGPRs plus a per-lane 32-bit offset.
+// The s_nop covers the wait states after an m0 write and after a VALU write of
+// an SGPR that a vector memory instruction reads.
+__device__ inline void dma16_sbase(uint64_t sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+// Same, from a per-lane 64-bit address.
+__device__ inline void dma16_vaddr(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Segment base pointers kseg[f], kseg[f + 1], vseg[f], vseg[f + 1], read from
+// the kernel arguments by the scalar unit and waited for in the same statement.
+struct SegPtrs {
+    uint64_t k0, k1, v0, v1;
+};
+__device__ inline SegPtrs load_seg_ptrs(int f) {
+    const char *ka = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
+    const uint32_t ko = (uint32_t)offsetof(KArgs, kseg) + 8u * (uint32_t)f;
+    const uint32_t vo = (uint32_t)offsetof(KArgs, vseg) + 8u * (uint32_t)f;
+    u64x2 k, v;
+    asm volatile("s_load_dwordx4 %0, %2, %3\n\ts_load_dwordx4 %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
+                 : "=s"(k), "=s"(v)
+                 : "s"(ka), "s"(ko), "s"(vo)
+                 : "memory");
+    return {k[0], k[1], v[0], v[1]};
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4): all but this wave's 4 newest loads done
+constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
-template <int SEGMODE>
+// DMA addressing of the head_dim-128 kernel.
+enum DmaMode : int {
+    kDmaFast = 0,  // segments of >= 32 keys, a multiple of 4 (one segment = contiguous keys):
+                   // every 4-row DMA group lies in one segment, wave-uniform base
+    kDmaLane = 1,  // anything else: per-lane segment lookup, zero rows past the end
+};
+
+template <int MODE>
 __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
-    constexpr bool SEG = SEGMODE != kContiguous;
-    // Four LDS stages, each a separate array so that the compiler can tell a
-    // DMA into one stage from reads of another (and does not drain the
-    // prefetches before every read).  Tile t lives in stage t mod 4.
-    __shared__ __attribute__((aligned(16))) uint16_t sK0[BN * D], sK1[BN * D], sK2[BN * D], sK3[BN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV0[BN * D], sV1[BN * D], sV2[BN * D], sV3[BN * D];
-    __shared__ const uint16_t *sSegK[SEG ? kMaxKeyFrames : 1];
-    __shared__ const uint16_t *sSegV[SEG ? kMaxKeyFrames : 1];
+    constexpr int TILE = BN * D, STAGE = 2 * TILE;  // elements
+    constexpr bool FAST = MODE == kDmaFast;
+    // Tile t lives in stage t mod 4: K at STAGE * (t mod 4), V right after it.
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[4 * STAGE];
+    __shared__ const uint16_t *sSegK[FAST ? 1 : kMaxKeyFrames];
+    __shared__ const uint16_t *sSegV[FAST ? 1 : kMaxKeyFrames];
     __shared__ int sRedo;
+    lds_u16 *const sbase = (lds_u16 *)sKV;
 
-    auto kst = [&](auto S) -> uint16_t * {
-        constexpr int v = decltype(S)::value & 3;
-        if constexpr (v == 0) return sK0;
-        else if constexpr (v == 1) return sK1;
-        else if constexpr (v == 2) return sK2;
-        else return sK3;
-    };
-    auto vst = [&](auto S) -> uint16_t * {
-        constexpr int v = decltype(S)::value & 3;
-        if constexpr (v == 0) return sV0;
-        else if constexpr (v == 1) return sV1;
-        else if constexpr (v == 2) return sV2;
-        else return sV3;
-    };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
 
     int head, qb;
@@ -484,7 +526,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     const int lim_wg_lo = key_limit(q0, a);
     const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
 
-    if (SEG) {
+    if (!FAST) {
         for (int f = tid; f < a.nseg; f += 256) {
             sSegK[f] = (const uint16_t *)a.kseg[f];
             sSegV[f] = (const uint16_t *)a.vseg[f];
@@ -505,32 +547,57 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         }
     }
 
-    // DMA: this lane fills rows lrow + 4 i (i = 0, 1) of each tile, physical
-    // 16-byte chunk pch; it fetches the logical chunk that the swizzle puts there.
-    const int lrow = 8 * wave + (lane >> 4);
-    const int pch = lane & 15;
+    // DMA: in group i (i = 0, 1) this wave fills tile rows 8 wave + 4 i + lr,
+    // lane (lr, pch) the physical 16-byte chunk pch, fetching the logical chunk
+    // that the swizzle puts there.
+    const int lr = lane >> 4, pch = lane & 15;
     int kch[2], vch[2];
+    uint32_t kvo[2], vvo[2];  // per-lane byte offsets from the group's first row
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r = lrow + 4 * i;
-        kch[i] = pch ^ (r & 7);
-        vch[i] = (((pch >> 1) ^ (r & 3)) << 1) | (pch & 1);
+        kch[i] = pch ^ (4 * i + lr);                       // (row mod 8) = 4 i + lr
+        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);     // (row mod 4) = lr
+        kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
+        vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
+    const uint32_t lds0 = lds_addr(sbase);
+    auto m0k = [&](int S, int i) { return lds0 + (uint32_t)((S * STAGE + (8 * wave + 4 * i) * D) * 2); };
 
     // Key cursor of the next tile to prefetch (tiles are prefetched in order
-    // within a sweep): frame segment cf and key offset co inside it.  Both are
-    // wave-uniform, so the per-lane address work is a select and a multiply-add.
+    // within a sweep): segment cf and key offset co inside it, wave-uniform.
+    // Past the last segment it wraps inside the last one, so look-ahead tiles
+    // beyond the keys still read valid (finite) rows, which the mask discards.
     int cf = 0, co = 0;
+    SegPtrs sp{};
     auto reset_cursor = [&]() {
         cf = 0;
         co = 0;
     };
+    auto load_ptrs = [&]() {
+        if constexpr (FAST) sp = load_seg_ptrs(cf);
+    };
     auto issue = [&](int tile, auto S) {
-        const int j0 = tile * BN;
-        if (SEGMODE == kSegGeneric) {  // frames shorter than a tile: per-lane lookup
+        constexpr int st = decltype(S)::value & 3;
+        if constexpr (FAST) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int j = j0 + lrow + 4 * i;
+                const int row = co + 8 * wave + 4 * i;
+                const bool nxt = row >= a.seg_len;
+                const long rr = nxt ? row - a.seg_len : row;
+                const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
+                dma16_sbase((nxt ? sp.k1 : sp.k0) + off, kvo[i], m0k(st, i));
+                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0k(st, i) + TILE * 2);
+            }
+            co += BN;
+            if (co >= a.seg_len) {
+                co -= a.seg_len;
+                cf = min(cf + 1, a.nseg - 1);
+            }
+        } else {
+            const int j0 = tile * BN;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = j0 + 8 * wave + 4 * i + lr;
                 const uint16_t *kp = kZeroRow + kch[i] * 8;
                 const uint16_t *vp = kZeroRow + vch[i] * 8;
                 if (j < a.Tk) {
@@ -539,59 +606,23 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
                     kp = sSegK[f] + o + kch[i] * 8;
                     vp = sSegV[f] + o + vch[i] * 8;
                 }
-                lds_dma16(kp, kst(S) + (8 * wave + 4 * i) * D);
-                lds_dma16(vp, vst(S) + (8 * wave + 4 * i) * D);
+                dma16_vaddr(kp, m0k(st, i));
+                dma16_vaddr(vp, m0k(st, i) + TILE * 2);
             }
-            return;
-        }
-        const uint16_t *kb0, *kb1, *vb0, *vb1;
-        int bnd;  // rows >= bnd of this tile lie in the next segment
-        long srow;  // element offset of the tile's first row inside its segment, plus the head
-        if (SEGMODE == kSegAligned) {
-            // The LDS copy of the segment table, not the kernel arguments:
-            // scalar loads return out of order and would make every LDS wait
-            // in the loop a full drain.
-            const int f1 = min(cf + 1, a.nseg - 1);
-            kb0 = sSegK[cf];
-            vb0 = sSegV[cf];
-            kb1 = sSegK[f1];
-            vb1 = sSegV[f1];
-            bnd = a.seg_len - co;
-            srow = (long)co * a.ld + hoff;
-            co += BN;  // advance to the next tile (a segment holds >= BN keys)
-            if (co >= a.seg_len) {
-                co -= a.seg_len;
-                cf = min(cf + 1, a.nseg - 1);
-            }
-        } else {
-            kb0 = kb1 = (const uint16_t *)a.kseg[0];
-            vb0 = vb1 = (const uint16_t *)a.vseg[0];
-            bnd = 1 << 30;
-            srow = (long)j0 * a.ld + hoff;
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = lrow + 4 * i;
-            const bool nxt = r >= bnd;
-            const int rr = nxt ? r - a.seg_len : r;
-            const long o = srow + (long)rr * a.ld;
-            const bool ok = j0 + r < a.Tk;
-            const uint16_t *kp = ok ? (nxt ? kb1 : kb0) + o + kch[i] * 8 : kZeroRow + kch[i] * 8;
-            const uint16_t *vp = ok ? (nxt ? vb1 : vb0) + o + vch[i] * 8 : kZeroRow + vch[i] * 8;
-            lds_dma16(kp, kst(S) + (8 * wave + 4 * i) * D);
-            lds_dma16(vp, vst(S) + (8 * wave + 4 * i) * D);
         }
     };
 
-    // Per-lane LDS offsets (elements) that do not depend on the tile.
-    int koff[NS];
+    // Per-lane LDS pointers of the fragment reads in stage 0; the stage, the
+    // upper half of d and the key steps are immediate offsets.
+    const lds_u16 *kfp[4];
 #pragma unroll
-    for (int st = 0; st < NS; ++st) koff[st] = n * D + (((2 * st + g) ^ (n & 7)) << 3);
+    for (int s = 0; s < 4; ++s) kfp[s] = sbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
     const int G = lane >> 4, sl = lane & 15;
-    const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 st + 8 h
-    int voff[NT];
+    const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
+    const lds_u16 *vfp[2];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) voff[t] = vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+    for (int t = 0; t < 2; ++t)
+        vfp[t] = sbase + TILE + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
 
     // Softmax with a fixed per-row exponent reference (log2 units): P =
     // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
@@ -599,7 +630,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // running sum stays far from the fp32 range.  A row whose sum ends above
     // 2^64 (or overflows) is recomputed in a second pass with its exact row max
     // as reference.  The accumulators are therefore touched only by MFMAs inside
-    // the key loop.  Each row's result depends on its own scores only.
+    // the key loop.  Each row's result depends on its own scores only.  The row
+    // sum adds the bf16-rounded P that the PV product uses.
     f32x16 acc[2][NT];
     float mref[2] = {0.f, 0.f}, l[2] = {0.f, 0.f}, mmax[2] = {-INFINITY, -INFINITY};
     const float c = a.c;
@@ -611,18 +643,19 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
     // transposed 8-byte reads each).
     auto read_k = [&](auto S, bf16x8 *kf) {
-        const uint16_t *Kt = kst(S);
+        constexpr int st = decltype(S)::value & 3;
 #pragma unroll
-        for (int st = 0; st < NS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(const u32x4 *)&Kt[koff[st]]);
+        for (int s = 0; s < NS; ++s)
+            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * STAGE + (s >> 2) * 64));
     };
     auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
-        const uint16_t *Vt = vst(S);
+        constexpr int st = decltype(S)::value & 3;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                vf[t][st][0] = lds_tr16(&Vt[voff[t] + (16 * st) * D]);
-                vf[t][st][1] = lds_tr16(&Vt[voff[t] + (16 * st + 8) * D]);
+            for (int s = 0; s < 2; ++s) {
+                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s + 8) * D);
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
@@ -648,14 +681,20 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         return pair_max(mx);
     };
-    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2]) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -mref[b]));
-                l[b] += p;
-                pf[b][r >> 3][r & 7] = (__bf16)p;
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pf[b][h][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b][8 * h + j], c, -mr[b]));
+                const bf16x8 &p8 = pf[b][h];
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, l[b], false);
             }
     };
     // O^T += V^T P^T.
@@ -678,15 +717,34 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // basic block: S(t+1) on the matrix cores while the VALU turns S(t) into P,
     // followed by O += V(t) P.  Steps past the last tile are fully masked (P =
     // 0) and only keep the DMA counts static.
+    //
+    // Masked steps: a row whose limit lies at or below the tile start takes an
+    // infinite exponent reference (P = 0); the element-wise mask runs only when
+    // some row's limit falls inside the tile, at most a few tiles per block.
     f32x16 scur[2];
     auto step = [&](int t, auto S, auto masked, auto maxonly) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
+        load_ptrs();  // segment pointers of tile t + 3
         __builtin_amdgcn_s_waitcnt(kWaitVm4);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
+        float mr[2] = {mref[0], mref[1]};
+        if (MASK) {
+            const int t0 = t * BN;
+            bool part = false;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                part = part || (lim[b] > t0 && lim[b] < t0 + BN);
+                mr[b] = lim[b] <= t0 ? INFINITY : mref[b];
+            }
+            if (MAXONLY || __builtin_amdgcn_ballot_w64(part)) {
+                asm volatile("");
+                apply_mask(scur, t);
+            }
+        }
         // All fragment reads first (K of tile t+1, V of tile t), so their LDS
         // latency hides behind the MFMAs and VALU work that follows.
         bf16x8 kf[NS];
@@ -696,32 +754,28 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         if (!MAXONLY) read_v(S, vf);
         f32x16 snext[2];
         qk(kf, snext);
-        if (MASK) apply_mask(scur, t);
         if (MAXONLY) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
         } else {
             bf16x8 pf[2][2];
-            softmax(scur, pf);
+            softmax(scur, pf, mr);
             pv(vf, pf);
         }
         issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
         if (!MAXONLY) {
-            // Schedule after the K reads (LDS reads are counted by a 4-bit
-            // lgkmcnt, so keep few outstanding for precise waits): the QK(t+1)
-            // MFMAs interleaved with the softmax VALU of tile t and one V read
-            // each, then the PV(t) MFMAs interleaved with the prefetch address
-            // VALU.
+            // The QK(t+1) MFMAs interleaved with the softmax VALU of tile t and
+            // one V read each, then the PV(t) MFMAs interleaved with the rest.
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
             }
         }
         scur[0] = snext[0];
@@ -729,10 +783,13 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     };
     auto sweep = [&](bool first_sweep, auto maxonly) {
         reset_cursor();
+        load_ptrs();
         issue(0, I0{});
+        load_ptrs();
         issue(1, I1{});
+        load_ptrs();
         issue(2, I2{});
-        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 landed
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -908,12 +965,10 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
     if (p.in_dtype == RTR_BF16 && D == 128) {
         k.nqb = (int)((p.Tq + 255) / 256);
         k.nwg = k.nqb * p.H;
-        if (!SEG)
-            hipLaunchKernelGGL((attn_fwd_bf16_d128<kContiguous>), dim3(k.nwg), dim3(256), 0, stream, k);
-        else if (k.seg_len >= 32)
-            hipLaunchKernelGGL((attn_fwd_bf16_d128<kSegAligned>), dim3(k.nwg), dim3(256), 0, stream, k);
+        if (k.seg_len >= 32 && k.seg_len % 4 == 0)
+            hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(256), 0, stream, k);
         else
-            hipLaunchKernelGGL((attn_fwd_bf16_d128<kSegGeneric>), dim3(k.nwg), dim3(256), 0, stream, k);
+            hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(256), 0, stream, k);
     } else if (p.in_dtype == RTR_BF16) {
         k.nqb = (int)((p.Tq + 127) / 128);
         k.nwg = k.nqb * p.H;
@@ -942,6 +997,8 @@ hipError_t launch_attention(const AttnProblem &p, hipStream_t stream) {
         k.kseg[f] = p.kseg[f];
         k.vseg[f] = p.vseg[f];
     }
+    k.kseg[p.nseg] = p.kseg[p.nseg - 1];
+    k.vseg[p.nseg] = p.vseg[p.nseg - 1];
     k.nseg = p.nseg;
     k.seg_len = (int32_t)p.seg_len;
     k.inv_seg_len = 1.0f / (float)p.seg_len;
