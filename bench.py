@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split", action="store_true",
+                    help="split-K schedule with a workspace (default: one workgroup per "
+                         "(head, query block), the faster schedule on these shapes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -139,6 +142,7 @@ def main():
 
     kpf, H, d = w["k"], w["H"], w["d"]
     stream = torch.cuda.current_stream(dev)
+    ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
     if args.workload.endswith("stream_step"):
         C, W, R = w["C"], w["W"], w["R"]
         x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"],
@@ -161,7 +165,7 @@ def main():
                   "query_tokens": C * kpf, "key_tokens": (R + W + C) * kpf}
 
         def attention():
-            rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o)
+            rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o, workspace=ws)
 
         def commit():
             rtr.rtr_kv_append_evict(kv, k, v, C)
@@ -178,7 +182,7 @@ def main():
                   "frames": F, "tokens": T}
 
         def attention():
-            rtr.rtr_attn_block_causal(q, k, v, kpf, o=o)
+            rtr.rtr_attn_block_causal(q, k, v, kpf, o=o, workspace=ws)
 
         def commit():
             pass
@@ -235,7 +239,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16",
+            "kernel": ("attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16")
+                      + ("" if ws is None else " + attn_combine_d128"),
+            "schedule": "plain" if ws is None else "split-K",
             "kernel_avg_us": round(attn_avg_s * 1e6, 2),
             "kernel_min_us": round(float(attn_ms.min()) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,

@@ -27,7 +27,12 @@
 // fp32 kernel: a plain VALU path for float32 inputs (one query row per
 // thread), used where float32 accuracy is required; not tuned.
 
+#include <algorithm>
+#include <atomic>
+#include <vector>
+#include <climits>
 #include <cmath>
+#include <cstddef>
 #include <type_traits>
 
 #include "rtr_internal.h"
@@ -60,16 +65,29 @@ struct KArgs {
     float c;             // scale * log2(e)
     float scale;
     int32_t out_f32;
+    // Split launch of the head_dim-128 kernel (nprog > 0): workspace of
+    // partial-result slots, workgroups in the grid, units (heads x query
+    // blocks), the common cut of the mains, spare workgroups and the tail tiles
+    // they share.
+    float *ws;
+    int32_t nprog;
+    int32_t units;
+    int32_t cut;
+    int32_t nspare;
+    int32_t tail_total;
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
 // Give every XCD one contiguous range of work items so the query blocks of one
 // head (which read the same K/V) share an L2; inside a head, the latest (most
 // keys) query block goes first.
-__device__ inline void map_block(int b, int nwg, int nqb, int &head, int &qb) {
+__device__ inline int xcd_order(int b, int nwg) {
     const int x = b & 7, i = b >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
-    const int w = x * q8 + (x < r8 ? x : r8) + i;
+    return x * q8 + (x < r8 ? x : r8) + i;
+}
+__device__ inline void map_block(int b, int nwg, int nqb, int &head, int &qb) {
+    const int w = xcd_order(b, nwg);
     head = w / nqb;
     qb = nqb - 1 - (w - head * nqb);
 }
@@ -481,6 +499,11 @@ constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// An empty volatile statement that reads an MFMA accumulator: the MFMAs that
+// produce it stay in front of it in program order (MFMAs have no side
+// effects, so without a use they may be sunk past later barriers).
+__device__ inline void pin(const f32x16 &x) { asm volatile("" ::"a"(x)); }
+
 // DMA addressing of the head_dim-128 kernel.
 enum DmaMode : int {
     kDmaFast = 0,  // segments of >= 32 keys, a multiple of 4 (one segment = contiguous keys):
@@ -879,6 +902,646 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     }
 }
 
+// Work decomposition of the head_dim-128 kernel.  A unit is one (head, query
+// block of 256 rows), head-major (u = head * nqb + qb); it covers the key tiles
+// [0, n(qb)), n(qb) the tiles up to the block's largest key limit.
+//
+// Plain launch (attn_fwd_bf16_d128 above): one workgroup per unit.
+//
+// Split launch (attn_fwd_bf16_d128_split below, with a workspace), for U units
+// on G > U workgroups: the same tile pipeline run on pieces of units.  It is a
+// kernel of its own so that the plain kernel's instruction schedule, which is
+// sensitive to any change of the surrounding code, stays as tuned.  Every unit
+// still has one
+// "main" workgroup, and the mains all walk the keys from tile 0 in step, so the
+// query blocks of one head share each K/V tile through L2; but a main stops at
+// a common cut T.  The tails [T, n) of the longer units are laid end to end and
+// shared evenly over the G - U spare workgroups; T is the smallest cut for
+// which a spare's share of the tails is at most T tiles.  Pieces that are not
+// whole units leave unnormalised partial results in the workspace: the main of
+// unit u in slot u, the tail piece holding the start of u's tail in slot U + u,
+// and a spare's first piece, when it continues a tail begun by the spare
+// before it, in slot 2U + s.  The combine kernel then merges the pieces of each
+// split unit in that fixed order.
+constexpr int kD128BM = 256, kD128BN = 32;
+constexpr int kMaxSplitUnits = 256;                       // units of a split launch
+constexpr int kSlotFloats = kD128BM * 128 + 2 * kD128BM;  // partial O, reference, sum
+
+__device__ inline int block_tiles(int qb, const KArgs &a) {
+    const int last = min(qb * kD128BM + kD128BM - 1, a.Tq - 1);
+    return (key_limit(last, a) + kD128BN - 1) / kD128BN;
+}
+
+// sTail[u] = tail tiles of units 0 .. u-1 (u = 0 .. U), built by the 256
+// threads of the workgroup, one unit each.
+__device__ __forceinline__ void build_tail_prefix(const KArgs &a, int *sTail, int *sTmp) {
+    const int tid = threadIdx.x;
+    sTmp[tid] = tid < a.units ? max(0, block_tiles(tid % a.nqb, a) - a.cut) : 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
+        const int v = tid >= off ? sTmp[tid - off] : 0;
+        __syncthreads();
+        sTmp[tid] += v;
+        __syncthreads();
+    }
+    sTail[tid + 1] = sTmp[tid];
+    if (tid == 0) sTail[0] = 0;
+    __syncthreads();
+}
+
+// First tail position of spare s, and the spare holding tail position x.
+__device__ inline int spare_start(int s, const KArgs &a) {
+    return (int)(((long)s * a.tail_total) / a.nspare);
+}
+__device__ inline int spare_of(int x, const KArgs &a) {
+    int s = (int)(((long)x * a.nspare) / a.tail_total);
+    while (s + 1 < a.nspare && spare_start(s + 1, a) <= x) ++s;
+    while (s > 0 && spare_start(s, a) > x) --s;
+    return s;
+}
+
+// Largest u with sTail[u] <= x among units with a tail (sTail non-decreasing).
+__device__ inline int find_tail_unit(const int *sTail, int U, int x) {
+    int lo = 0, hi = U;  // sTail[lo] <= x < sTail[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sTail[mid] <= x) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Role of workgroup b in a split launch.  Workgroup b runs on XCD b mod 8;
+// each XCD gets a contiguous head-major run of units (so the mains of one head
+// share that XCD's L2), and its remaining workgroups are spares.
+__device__ inline void split_role(int b, const KArgs &a, int &unit, int &spare) {
+    const int x = b & 7, i = b >> 3;
+    const int ulo = x * a.units / 8, un = (x + 1) * a.units / 8 - ulo;
+    unit = -1;
+    spare = -1;
+    if (i < un) {
+        unit = ulo + i;
+        return;
+    }
+    int s = 0;
+    for (int y = 0; y < x; ++y) s += (a.nprog - y + 7) / 8 - ((y + 1) * a.units / 8 - y * a.units / 8);
+    spare = s + i - un;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
+    constexpr int D = 128, BM = kD128BM, BN = kD128BN, NS = D / 16, NT = D / 32;
+    constexpr int TILE = BN * D, STAGE = 2 * TILE;  // elements
+    constexpr bool FAST = MODE == kDmaFast;
+    // Tile t of a piece lives in stage (t - first tile) mod 4: K at STAGE *
+    // stage, V right after it.
+    __shared__ __attribute__((aligned(16))) uint16_t sKV[4 * STAGE];
+    __shared__ const uint16_t *sSegK[FAST ? 1 : kMaxKeyFrames];
+    __shared__ const uint16_t *sSegV[FAST ? 1 : kMaxKeyFrames];
+    __shared__ int sTail[kMaxSplitUnits + 1];
+    __shared__ int sTmp[256];
+    __shared__ int sRedo;
+    lds_u16 *const sbase = (lds_u16 *)sKV;
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+
+    if (!FAST) {
+        for (int f = tid; f < a.nseg; f += 256) {
+            sSegK[f] = (const uint16_t *)a.kseg[f];
+            sSegV[f] = (const uint16_t *)a.vseg[f];
+        }
+    }
+
+    // DMA: in group i (i = 0, 1) this wave fills tile rows 8 wave + 4 i + lr,
+    // lane (lr, pch) the physical 16-byte chunk pch, fetching the logical chunk
+    // that the swizzle puts there.
+    const int lr = lane >> 4, pch = lane & 15;
+    int kch[2], vch[2];
+    uint32_t kvo[2], vvo[2];  // per-lane byte offsets from the group's first row
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        kch[i] = pch ^ (4 * i + lr);                    // (row mod 8) = 4 i + lr
+        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
+        kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
+        vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
+    }
+    const uint32_t lds0 = lds_addr(sbase);
+    auto m0k = [&](int S, int i) __attribute__((always_inline)) { return lds0 + (uint32_t)((S * STAGE + (8 * wave + 4 * i) * D) * 2); };
+
+    // Per-piece state.
+    long hoff = 0;
+    int qi[2], lim[2];
+    bool qv[2];
+    bf16x8 qf[2][NS];
+    int nfull = 0;
+
+    // Key cursor of the next tile to prefetch (tiles are prefetched in order
+    // within a sweep): segment cf and key offset co inside it, wave-uniform.
+    // Past the last segment it wraps inside the last one, so look-ahead tiles
+    // beyond the keys still read valid (finite) rows, which the mask discards.
+    int cf = 0, co = 0;
+    SegPtrs sp{};
+    auto reset_cursor = [&](int tile) __attribute__((always_inline)) {
+        if constexpr (FAST) {
+            const int j0 = tile * BN;
+            cf = __builtin_amdgcn_readfirstlane(seg_of(j0, a));
+            co = j0 - cf * a.seg_len;
+        }
+    };
+    auto load_ptrs = [&]() __attribute__((always_inline)) {
+        if constexpr (FAST) sp = load_seg_ptrs(cf);
+    };
+    auto issue = [&](int tile, auto S) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value & 3;
+        if constexpr (FAST) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = co + 8 * wave + 4 * i;
+                const bool nxt = row >= a.seg_len;
+                const long rr = nxt ? row - a.seg_len : row;
+                const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
+                dma16_sbase((nxt ? sp.k1 : sp.k0) + off, kvo[i], m0k(st, i));
+                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0k(st, i) + TILE * 2);
+            }
+            co += BN;
+            if (co >= a.seg_len) {
+                co -= a.seg_len;
+                cf = min(cf + 1, a.nseg - 1);
+            }
+        } else {
+            const int j0 = tile * BN;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = j0 + 8 * wave + 4 * i + lr;
+                const uint16_t *kp = kZeroRow + kch[i] * 8;
+                const uint16_t *vp = kZeroRow + vch[i] * 8;
+                if (j < a.Tk) {
+                    const int f = seg_of(j, a);
+                    const long o = (long)(j - f * a.seg_len) * a.ld + hoff;
+                    kp = sSegK[f] + o + kch[i] * 8;
+                    vp = sSegV[f] + o + vch[i] * 8;
+                }
+                dma16_vaddr(kp, m0k(st, i));
+                dma16_vaddr(vp, m0k(st, i) + TILE * 2);
+            }
+        }
+    };
+
+    // Per-lane LDS pointers of the fragment reads in stage 0; the stage, the
+    // upper half of d and the key steps are immediate offsets.
+    const lds_u16 *kfp[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kfp[s] = sbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
+    const int G = lane >> 4, sl = lane & 15;
+    const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
+    const lds_u16 *vfp[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        vfp[t] = sbase + TILE + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+
+    // Softmax with a fixed per-row exponent reference (log2 units): P =
+    // exp2(s * c - mref).  mref is the row max of the row's first key tile (of
+    // the piece), so P <= 1 there; later tiles may exceed it, which is harmless
+    // while the running sum stays far from the fp32 range.  A row whose sum
+    // ends above 2^64 (or overflows) is recomputed in a second pass with its
+    // exact row max as reference.  The accumulators are therefore touched only
+    // by MFMAs inside the key loop.  Each row's result depends on its own
+    // scores only.  The row sum adds the bf16-rounded P that the PV product uses.
+    f32x16 acc[2][NT];
+    float mref[2] = {0.f, 0.f}, l[2] = {0.f, 0.f}, mmax[2] = {-INFINITY, -INFINITY};
+    const float c = a.c;
+
+    // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
+    // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
+    // transposed 8-byte reads each).
+    // The K reads are issued in the order the QK MFMA chain consumes them
+    // (the fences keep the scheduler from regrouping them by base register,
+    // which would make the first MFMAs wait for nearly all eight).
+    auto read_k = [&](auto S, bf16x8 *kf) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value & 3;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * STAGE + (s >> 2) * 64));
+            compiler_fence();
+        }
+    };
+    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value & 3;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s + 8) * D);
+            }
+    };
+    // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
+    auto qk = [&](const bf16x8 *kf, f32x16 *s) __attribute__((always_inline)) {
+        s[0] = f32x16{};
+        s[1] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], s[1], 0, 0, 0);
+        }
+    };
+    auto apply_mask = [&](f32x16 *s, int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (tile * BN + 8 * (r >> 2) + 4 * g + (r & 3) >= lim[b]) s[b][r] = -INFINITY;
+    };
+    auto rowmax = [&](const f32x16 &s) __attribute__((always_inline)) {
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        return pair_max(mx);
+    };
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // P for keys 8 h .. 8 h + 7 of the lane's 16 (block b), and its row sum.
+    auto softmax_part = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr, int b, int h)
+                            __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            pf[b][h][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b][8 * h + j], c, -mr[b]));
+        const bf16x8 &p8 = pf[b][h];
+        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), ones, l[b], false);
+        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, l[b], false);
+        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, l[b], false);
+        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, l[b], false);
+    };
+    // O^T += V^T P^T for block b.
+    auto pv_block = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2], int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)  // consecutive MFMAs write different accumulators
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const bf16x8 v = __builtin_bit_cast(
+                    bf16x8, (v8i16)__builtin_shufflevector(vf[t][st][0], vf[t][st][1], 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[b][st], acc[b][t], 0, 0, 0);
+            }
+    };
+
+    // Software pipeline over key tiles.  Step t (stage t mod 4 relative to the
+    // piece's first tile): wait until this wave's DMA of tile t+1 has landed
+    // (tile t+2 may still be in flight), barrier (every wave's DMA of t+1 has
+    // landed; every wave is done with tile t-1, whose stage takes tile t+3),
+    // then in one basic block: S(t+1) on the matrix cores while the VALU turns
+    // S(t) into P, followed by O += V(t) P and the prefetch of tile t+3.  The
+    // loop leaves after the piece's last tile (its S(t+1) is never used); the
+    // look-ahead tiles past it read valid rows (the key cursor wraps inside the
+    // last segment) and are drained before the stages are reused.
+    //
+    // Masked steps: a row whose limit lies at or below the tile start takes an
+    // infinite exponent reference (P = 0); the element-wise mask runs only when
+    // some row's limit falls inside the tile, at most a few tiles per block.
+    f32x16 scur[2];
+    auto step = [&](int t, auto S, auto masked, auto maxonly) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(masked)::value;
+        constexpr bool MAXONLY = decltype(maxonly)::value;
+        load_ptrs();  // segment pointers of tile t + 3
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile t+2 may stay in flight
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        float mr[2] = {mref[0], mref[1]};
+        if (MASK) {
+            const int t0 = t * BN;
+            bool part = false;
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                part = part || (lim[b] > t0 && lim[b] < t0 + BN);
+                mr[b] = lim[b] <= t0 ? INFINITY : mref[b];
+            }
+            if (MAXONLY || __builtin_amdgcn_ballot_w64(part)) {
+                asm volatile("");
+                apply_mask(scur, t);
+            }
+        }
+        // All fragment reads first (K of tile t+1, V of tile t), so their LDS
+        // latency hides behind the MFMAs and VALU work that follows.
+        bf16x8 kf[NS];
+        v4i16 vf[NT][2][2];
+        read_k(std::integral_constant<int, (decltype(S)::value + 1) & 3>{}, kf);
+        __builtin_amdgcn_sched_barrier(0);  // the K reads go first
+        f32x16 snext[2];
+        if (MAXONLY) {
+            qk(kf, snext);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+        } else {
+            // Three scheduling regions, so that no PV MFMA waits in the QK
+            // stream for a V fragment read just before it:
+            //   QK(t+1) MFMAs | V reads, softmax of block 0 and half of block 1;
+            //   PV(t) of block 0 | the other half of block 1's softmax;
+            //   PV(t) of block 1 | the prefetch.
+            bf16x8 pf[2][2];
+            read_v(S, vf);
+            qk(kf, snext);
+            softmax_part(scur, pf, mr, 0, 0);
+            softmax_part(scur, pf, mr, 0, 1);
+            softmax_part(scur, pf, mr, 1, 0);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            pin(snext[0]);
+            pin(snext[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_block(vf, pf, 0);
+            softmax_part(scur, pf, mr, 1, 1);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) pin(acc[0][t]);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_block(vf, pf, 1);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) pin(acc[1][t]);
+        }
+        // Prefetch tile t+3 into the stage of tile t-1 (every wave finished
+        // with it before this step's barrier), while the PV MFMAs drain.
+        issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
+        scur[0] = snext[0];
+        scur[1] = snext[1];
+    };
+    // One pass over the tiles [tb, te) of the current piece.
+    auto sweep = [&](bool first_sweep, int tb, int te, auto maxonly) __attribute__((always_inline)) {
+        reset_cursor(tb);
+        load_ptrs();
+        issue(tb, I0{});
+        load_ptrs();
+        issue(tb + 1, I1{});
+        load_ptrs();
+        issue(tb + 2, I2{});
+        // Tile tb landed, and so did every older vector-memory operation (the
+        // previous piece's stores may still be in flight, and stores and loads
+        // need not complete in order).
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+        {
+            bf16x8 kf[NS];
+            read_k(I0{}, kf);
+            qk(kf, scur);
+        }
+        if (first_sweep) {
+            if (tb >= nfull) apply_mask(scur, tb);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const float m = rowmax(scur[b]);
+                mref[b] = m == -INFINITY ? 0.f : m * c;  // no key of the piece: P = 0 throughout
+            }
+        }
+        // Groups of four steps (static stages): unmasked while the whole group
+        // is visible to every row, masked from there on.
+        int base = tb;
+#pragma unroll 1
+        for (; base + 4 <= nfull; base += 4) {
+            step(base, I0{}, std::false_type{}, maxonly);
+            step(base + 1, I1{}, std::false_type{}, maxonly);
+            step(base + 2, I2{}, std::false_type{}, maxonly);
+            step(base + 3, I3{}, std::false_type{}, maxonly);
+        }
+#pragma unroll 1
+        for (; base < te; base += 4) {
+            step(base, I0{}, std::true_type{}, maxonly);
+            if (base + 1 >= te) break;
+            step(base + 1, I1{}, std::true_type{}, maxonly);
+            if (base + 2 >= te) break;
+            step(base + 2, I2{}, std::true_type{}, maxonly);
+            if (base + 3 >= te) break;
+            step(base + 3, I3{}, std::true_type{}, maxonly);
+        }
+        // drain the look-ahead tiles before the stages are reused
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        compiler_fence();
+    };
+
+    // Tiles [tb, te) of unit (head, qb).  slot < 0: the whole unit, write O
+    // (and LSE); else write the partial result to workspace slot `slot`.
+    auto do_piece = [&](int head, int qb, int tb, int te, int slot) __attribute__((always_inline)) {
+        const int q0 = qb * BM;
+        hoff = (long)head * D;
+        const int lim_end = te * BN;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            qi[b] = q0 + 64 * wave + 32 * b + n;
+            qv[b] = qi[b] < a.Tq;
+            lim[b] = min(key_limit(qv[b] ? qi[b] : a.Tq - 1, a), lim_end);
+        }
+        nfull = min(te, min(key_limit(q0, a), lim_end) / BN);  // tiles visible to every row
+        if (tid == 0) sRedo = 0;
+
+        // Q^T B operands of both blocks: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const uint16_t *qrow = (const uint16_t *)a.q + (long)(qv[b] ? qi[b] : a.Tq - 1) * a.ld + hoff;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const u32x4 raw = qv[b] ? gload16(qrow + 16 * s + 8 * g) : u32x4{0, 0, 0, 0};
+                qf[b][s] = __builtin_bit_cast(bf16x8, raw);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            l[b] = 0.f;
+            mmax[b] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
+        }
+        sweep(true, tb, te, std::false_type{});
+
+        // Rare second pass for rows whose sum left the safe range.
+        const float kSafeSum = 18446744073709551616.f;  // 2^64
+        bool redo[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
+        if (__builtin_amdgcn_ballot_w64(redo[0] || redo[1]) && lane == 0) sRedo = 1;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(sRedo)) {
+            asm volatile("");
+            sweep(false, tb, te, std::true_type{});  // exact row maxima
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                if (redo[b]) mref[b] = mmax[b] * c;
+                l[b] = 0.f;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
+            }
+            sweep(false, tb, te, std::false_type{});
+        }
+
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const float lt = pair_sum(l[b]);
+            if (!qv[b]) continue;
+            if (slot >= 0) {
+                const int row = 64 * wave + 32 * b + n;
+                float *ps = a.ws + (long)slot * kSlotFloats;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(f32x4 *)(ps + row * D + 32 * t + 8 * i + 4 * g) =
+                            f32x4{acc[b][t][4 * i], acc[b][t][4 * i + 1], acc[b][t][4 * i + 2], acc[b][t][4 * i + 3]};
+                if (g == 0) {
+                    ps[BM * D + row] = mref[b];
+                    ps[BM * D + BM + row] = lt;
+                }
+                continue;
+            }
+            const float inv = 1.f / lt;
+            const long obase = (long)qi[b] * a.ld + hoff;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dcol = 32 * t + 8 * i + 4 * g;
+                    const float o0 = acc[b][t][4 * i + 0] * inv, o1 = acc[b][t][4 * i + 1] * inv;
+                    const float o2 = acc[b][t][4 * i + 2] * inv, o3 = acc[b][t][4 * i + 3] * inv;
+                    if (a.out_f32) {
+                        *(f32x4 *)((float *)a.o + obase + dcol) = f32x4{o0, o1, o2, o3};
+                    } else {
+                        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)o0);
+                        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)o1);
+                        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)o2);
+                        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)o3);
+                        *(u32x2 *)((uint16_t *)a.o + obase + dcol) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+                    }
+                }
+            if (g == 0 && a.lse) a.lse[(long)head * a.Tq + qi[b]] = mref[b] / kLog2e + logf(lt);
+        }
+        // Every wave is done with the stages and sRedo; the stores above may
+        // stay in flight (the next piece waits for them before its first read).
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        compiler_fence();
+        __builtin_amdgcn_s_barrier();
+        compiler_fence();
+    };
+
+    int unit, spare;
+    split_role(blockIdx.x, a, unit, spare);
+    if (unit >= 0) {  // main: tiles [0, min(n, T)) of its unit
+        const int head = unit / a.nqb, qb = unit - head * a.nqb;
+        const int n = block_tiles(qb, a);
+        __syncthreads();
+        do_piece(head, qb, 0, min(n, a.cut), n > a.cut ? unit : -1);
+        return;
+    }
+    // spare: tail positions [spare_start(s), spare_start(s + 1))
+    build_tail_prefix(a, sTail, sTmp);
+    const int p1 = spare_start(spare + 1, a);
+    int p = spare_start(spare, a);
+#pragma unroll 1
+    while (p < p1) {
+        const int u = __builtin_amdgcn_readfirstlane(find_tail_unit(sTail, a.units, p));
+        const int t0 = __builtin_amdgcn_readfirstlane(sTail[u]);
+        const int tn = __builtin_amdgcn_readfirstlane(sTail[u + 1]) - t0;
+        const int off = p - t0, end = min(tn, p1 - t0);
+        if (off < 0 || end <= off) break;  // cannot happen with a consistent prefix table
+        const int head = u / a.nqb, qb = u - head * a.nqb;
+        const int slot = off == 0 ? a.units + u : 2 * a.units + spare;
+        do_piece(head, qb, a.cut + off, a.cut + end, slot);
+        p = t0 + end;
+    }
+}
+
+// Merges the pieces of every split unit of a split launch: with piece s holding
+// acc_s (unnormalised O), reference m_s and sum l_s per row, M = max m_s over
+// the pieces that saw keys, L = sum 2^(m_s - M) l_s, O = sum 2^(m_s - M) acc_s / L
+// and LSE = M ln 2 + ln L.  Pieces are taken in a fixed order (main, tail
+// start, continuations), so the result does not depend on timing.  One
+// workgroup per unit; units that were not split return at once.
+__global__ __launch_bounds__(256) void attn_combine_d128(const KArgs a) {
+    constexpr int D = 128, BM = kD128BM, C4 = D / 4, ITEMS = BM * C4 / 256;
+    __shared__ int sTail[kMaxSplitUnits + 1];
+    __shared__ int sTmp[256];
+    __shared__ float sM[BM], sW[BM], sInv[BM];
+    const int tid = threadIdx.x;
+    const int u = blockIdx.x;
+    const int head = u / a.nqb, qb = u - head * a.nqb;
+    if (block_tiles(qb, a) <= a.cut) return;
+    build_tail_prefix(a, sTail, sTmp);
+    const int t0 = sTail[u], tn = sTail[u + 1] - t0;
+    const int sa = spare_of(t0, a), sb = spare_of(t0 + tn - 1, a);
+    const int npieces = 2 + sb - sa;
+    auto slot_of = [&](int k) {
+        return k == 0 ? u : k == 1 ? a.units + u : 2 * a.units + sa + k - 1;
+    };
+
+    // Per row: largest reference among pieces that saw keys, and 1 / L.
+    {
+        float M = -INFINITY;
+        for (int k = 0; k < npieces; ++k) {
+            const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
+            if (ps[BM * D + BM + tid] > 0.f) M = fmaxf(M, ps[BM * D + tid]);
+        }
+        float L = 0.f;
+        for (int k = 0; k < npieces; ++k) {
+            const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
+            const float ls = ps[BM * D + BM + tid];
+            if (ls > 0.f) L += exp2f(ps[BM * D + tid] - M) * ls;
+        }
+        sM[tid] = M;
+        sInv[tid] = 1.f / L;
+        const int row = qb * BM + tid;
+        if (a.lse && row < a.Tq) a.lse[(long)head * a.Tq + row] = M / kLog2e + logf(L);
+    }
+    // Thread tid owns column chunk tid % 32 of rows tid / 32 + 8 k.
+    const int c4 = tid % C4, r0 = tid / C4;
+    f32x4 o[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < npieces; ++k) {
+        const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
+        __syncthreads();
+        const float ls = ps[BM * D + BM + tid];
+        sW[tid] = ls > 0.f ? exp2f(ps[BM * D + tid] - sM[tid]) : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const int row = r0 + 8 * j;
+            const f32x4 v = *(const f32x4 *)(ps + row * D + 4 * c4);
+            o[j] += sW[row] * v;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const int row = r0 + 8 * j;
+        const int qrow = qb * BM + row;
+        if (qrow >= a.Tq) continue;
+        const f32x4 v = o[j] * sInv[row];
+        const long off = (long)qrow * a.ld + (long)head * D + 4 * c4;
+        if (a.out_f32) {
+            *(f32x4 *)((float *)a.o + off) = v;
+        } else {
+            const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)v[0]);
+            const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)v[1]);
+            const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)v[2]);
+            const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)v[3]);
+            *(u32x2 *)((uint16_t *)a.o + off) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs, VALU path: one query row per thread, 32-key tiles in LDS.
 // ---------------------------------------------------------------------------
@@ -959,16 +1622,94 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const KArgs a) {
     }
 }
 
+// Host mirror of block_tiles: key tiles of query block qb of the head_dim-128 kernel.
+int64_t host_block_tiles(int64_t qb, const KArgs &k) {
+    const int64_t last = std::min<int64_t>(qb * kD128BM + kD128BM - 1, k.Tq - 1);
+    const int64_t lim = std::min<int64_t>((int64_t)k.prefix + (last / k.kpf + 1) * k.kpf, k.Tk);
+    return (lim + kD128BN - 1) / kD128BN;
+}
+
+// Smallest share of key tiles a split range gets (fewer ranges than compute
+// units for small problems).
+constexpr int64_t kMinRangeTiles = 8;
+
+// Compute units of the current device, cached per device.
+hipError_t cu_count(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (const hipError_t e = hipGetDevice(&dev)) return e;
+    if (dev >= 0 && dev < 64 && cache[dev].load() > 0) {
+        *out = cache[dev].load();
+        return hipSuccess;
+    }
+    int n = 0;
+    if (const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev)) return e;
+    if (dev >= 0 && dev < 64) cache[dev].store(n);
+    *out = n;
+    return hipSuccess;
+}
+
 template <int D, bool SEG>
 hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
     KArgs k = ka;
     if (p.in_dtype == RTR_BF16 && D == 128) {
         k.nqb = (int)((p.Tq + 255) / 256);
         k.nwg = k.nqb * p.H;
-        if (k.seg_len >= 32 && k.seg_len % 4 == 0)
-            hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(256), 0, stream, k);
-        else
-            hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(256), 0, stream, k);
+        k.ws = nullptr;
+        k.nprog = 0;
+        const int64_t U = (int64_t)k.nqb * p.H;
+        if (p.ws && U < kMaxSplitUnits) {
+            int cu = 0;
+            if (const hipError_t e = cu_count(&cu)) return e;
+            std::vector<int64_t> nq(k.nqb);
+            int64_t total = 0, nmax = 0;
+            for (int64_t qb = 0; qb < k.nqb; ++qb) {
+                nq[qb] = host_block_tiles(qb, k);
+                total += nq[qb] * p.H;
+                nmax = std::max(nmax, nq[qb]);
+            }
+            const int64_t G = std::min<int64_t>(std::min<int64_t>(cu, kMaxSplitUnits),
+                                                std::max<int64_t>(U + 1, total / kMinRangeTiles));
+            if (G > U) {
+                const int64_t S = G - U;
+                auto tails = [&](int64_t T) {
+                    int64_t t = 0;
+                    for (int64_t n : nq) t += std::max<int64_t>(0, n - T) * p.H;
+                    return t;
+                };
+                int64_t lo = 1, hi = nmax;  // smallest cut T with tails(T) <= S * T
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi) / 2;
+                    if (tails(mid) <= S * mid) hi = mid;
+                    else lo = mid + 1;
+                }
+                const int64_t tt = tails(lo);
+                bool fit = true;  // every XCD has a workgroup for each of its mains
+                for (int64_t x = 0; x < 8; ++x)
+                    fit = fit && (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
+                if (tt > 0 && fit && tt < INT32_MAX) {
+                    k.ws = (float *)p.ws;
+                    k.nprog = (int32_t)G;
+                    k.units = (int32_t)U;
+                    k.cut = (int32_t)lo;
+                    k.nspare = (int32_t)S;
+                    k.tail_total = (int32_t)tt;
+                }
+            }
+        }
+        const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;
+        if (k.nprog == 0) {
+            if (fast)
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(256), 0, stream, k);
+            else
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(256), 0, stream, k);
+        } else {
+            if (fast)
+                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(256), 0, stream, k);
+            else
+                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaLane>), dim3(k.nprog), dim3(256), 0, stream, k);
+            hipLaunchKernelGGL(attn_combine_d128, dim3(k.units), dim3(256), 0, stream, k);
+        }
     } else if (p.in_dtype == RTR_BF16) {
         k.nqb = (int)((p.Tq + 127) / 128);
         k.nwg = k.nqb * p.H;
@@ -987,6 +1728,15 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t attention_workspace_bytes(int32_t d, rtr_dtype in_dtype, size_t *bytes) {
+    *bytes = 0;
+    if (d != 128 || in_dtype != RTR_BF16) return hipSuccess;
+    int cu = 0;
+    if (const hipError_t e = cu_count(&cu)) return e;
+    *bytes = (size_t)2 * std::min(cu, kMaxSplitUnits) * kSlotFloats * sizeof(float);
+    return hipSuccess;
+}
 
 hipError_t launch_attention(const AttnProblem &p, hipStream_t stream) {
     KArgs k{};

@@ -117,6 +117,25 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(RTR_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Checks a split-K workspace against the requirement of the current device and
+// the call's other buffers; *use is the pointer to hand to the launch (NULL when
+// none is given or the configuration never splits).
+int check_workspace(void *ws, size_t ws_bytes, int32_t d, rtr_dtype dt, const void *const *bufs,
+                    const int64_t *sizes, int nbufs, void **use) {
+    *use = nullptr;
+    if (!ws) return RTR_OK;
+    if (!aligned16(ws)) return fail(RTR_EINVAL, "workspace must be 16-byte aligned");
+    for (int i = 0; i < nbufs; ++i)
+        if (overlaps(ws, (int64_t)ws_bytes, bufs[i], sizes[i]))
+            return fail(RTR_EINVAL, "workspace overlaps an input, output or cache buffer");
+    size_t need = 0;
+    if (const hipError_t e = rtr::attention_workspace_bytes(d, dt, &need)) return hip_fail(e, "workspace size");
+    if (ws_bytes < need)
+        return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed on this device", ws_bytes, need);
+    *use = need ? ws : nullptr;
+    return RTR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -136,10 +155,19 @@ const char *rtr_status_string(int code) {
     }
 }
 
+int rtr_attn_workspace_size(int32_t d, rtr_dtype in_dtype, size_t *bytes) {
+    if (!bytes) return fail(RTR_EINVAL, "bytes is NULL");
+    *bytes = 0;
+    if (!valid_dtype(in_dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (d != 64 && d != 128) return fail(RTR_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (const hipError_t e = rtr::attention_workspace_bytes(d, in_dtype, bytes)) return hip_fail(e, "workspace size");
+    return ok();
+}
+
 int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, float *lse,
                           int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
                           rtr_dtype in_dtype, rtr_dtype out_dtype, float scale,
-                          rtr_stream stream) {
+                          void *workspace, size_t workspace_bytes, rtr_stream stream) {
     if (T < 0 || T > kMaxTokens) return fail(RTR_EINVAL, "T=%lld out of range [0, 2^30]", (long long)T);
     if (H < 1) return fail(RTR_EINVAL, "H=%d must be >= 1", H);
     if (tokens_per_frame < 1) return fail(RTR_EINVAL, "tokens_per_frame must be >= 1");
@@ -160,8 +188,15 @@ int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, 
         if (overlaps(lse, lse_bytes, x, in_bytes)) return fail(RTR_EINVAL, "lse overlaps an input");
     }
     if (overlaps(lse, lse_bytes, o, out_bytes)) return fail(RTR_EINVAL, "lse overlaps o");
+    void *ws = nullptr;
+    {
+        const void *bufs[5] = {q, k, v, o, lse};
+        const int64_t sizes[5] = {in_bytes, in_bytes, in_bytes, out_bytes, lse ? lse_bytes : 0};
+        if (int rc = check_workspace(workspace, workspace_bytes, d, in_dtype, bufs, sizes, 5, &ws)) return rc;
+    }
 
     rtr::AttnProblem p;
+    p.ws = ws;
     p.q = q;
     p.o = o;
     p.lse = lse;
@@ -368,7 +403,8 @@ int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, con
 
 int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
-                         float scale, rtr_stream stream) {
+                         float scale, void *workspace, size_t workspace_bytes,
+                         rtr_stream stream) {
     if (int rc = check_cache(kv)) return rc;
     if (chunk_frames < 1 || chunk_frames > RTR_MAX_CHUNK)
         return fail(RTR_EUNSUPPORTED, "chunk_frames=%d outside [1, %d]", chunk_frames, RTR_MAX_CHUNK);
@@ -391,8 +427,16 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
         if (overlaps(lse, lse_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "lse overlaps an input or the cache");
     }
     if (overlaps(lse, lse_b, o, out_b)) return fail(RTR_EINVAL, "lse overlaps o");
+    void *ws = nullptr;
+    {
+        const void *bufs[9] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, o, lse};
+        const int64_t sizes[9] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap,
+                                  out_b, lse ? lse_b : 0};
+        if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws)) return rc;
+    }
 
     rtr::AttnProblem p;
+    p.ws = ws;
     int nseg = 0;
     for (int r = 0; r < kv->ref_frames; ++r) {
         p.kseg[nseg] = (const char *)kv->k_ref + r * fb;

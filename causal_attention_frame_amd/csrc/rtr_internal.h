@@ -38,9 +38,17 @@ struct AttnProblem {
     int32_t H = 0, d = 0;
     float scale = 0.f;
     rtr_dtype in_dtype = RTR_BF16, out_dtype = RTR_BF16;
+    // Split-K workspace (attention_workspace_bytes() bytes) or null: with it the
+    // head_dim-128 bf16 kernel balances the key tiles over the compute units
+    // and a second kernel merges the partial results.
+    void *ws = nullptr;
 };
 
 hipError_t launch_attention(const AttnProblem &p, hipStream_t stream);
+
+// Split-K workspace the attention launch needs on the current device for this
+// head dim and input type (0: the launch never splits).
+hipError_t attention_workspace_bytes(int32_t d, rtr_dtype in_dtype, size_t *bytes);
 
 // Copies of whole [k, H, d] frames (16-byte multiples, 16-byte aligned).
 struct CopyJobs {

@@ -44,7 +44,9 @@ class rtr_kv_state(ctypes.Structure):
 # name -> (restype, argtypes); mirrors include/rtr_attn.h
 _SIGNATURES = {
     "rtr_attn_block_causal": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i32, _c_i32,
-                                             _c_i64, ctypes.c_int, ctypes.c_int, _c_f32, _vp]),
+                                             _c_i64, ctypes.c_int, ctypes.c_int, _c_f32, _vp,
+                                             ctypes.c_size_t, _vp]),
+    "rtr_attn_workspace_size": (ctypes.c_int, [_c_i32, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "rtr_kv_create": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _c_i32, _c_i32,
                                      _c_i64, _c_i32, _c_i32, ctypes.c_int]),
     "rtr_kv_destroy": (ctypes.c_int, [_vp]),
@@ -52,7 +54,7 @@ _SIGNATURES = {
     "rtr_kv_next_slots": (ctypes.c_int, [_vp, _c_i32, ctypes.POINTER(_c_i32)]),
     "rtr_kv_commit_inplace": (ctypes.c_int, [_vp, _c_i32]),
     "rtr_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, ctypes.c_int,
-                                            _c_f32, _vp]),
+                                            _c_f32, _vp, ctypes.c_size_t, _vp]),
     "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
     "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
     "rtr_kv_set_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
@@ -121,9 +123,31 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _workspace(ws):
+    """(pointer, bytes) of an optional split-K workspace tensor."""
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def rtr_attn_workspace_size(d, dtype=RTR_BF16):
+    """Bytes of split-K workspace the current device needs (0: never splits)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().rtr_attn_workspace_size(int(d), int(dtype), ctypes.byref(n)), "rtr_attn_workspace_size")
+    return n.value
+
+
+def new_workspace(d, dtype=RTR_BF16, device="cuda"):
+    """A device byte tensor sized for rtr_attn_workspace_size, or None when
+    the configuration never splits."""
+    import torch
+    n = rtr_attn_workspace_size(d, dtype)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 # ---------------------------------------------------------------- full form
 def rtr_attn_block_causal(q, k, v, tokens_per_frame, o=None, lse=None, scale=0.0,
-                          out_dtype=None, want_lse=False, stream=None):
+                          out_dtype=None, want_lse=False, workspace=None, stream=None):
     """Frame-block-causal attention over one [T, H, d] sequence.
     Returns (o, lse or None)."""
     import torch
@@ -133,9 +157,10 @@ def rtr_attn_block_causal(q, k, v, tokens_per_frame, o=None, lse=None, scale=0.0
         o = torch.empty((T, H, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(workspace)
     _check(lib().rtr_attn_block_causal(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), T, H, d,
                                        int(tokens_per_frame), _dtype_code(q), _dtype_code(o),
-                                       float(scale), _stream(stream, q.device)),
+                                       float(scale), ws, ws_bytes, _stream(stream, q.device)),
            "rtr_attn_block_causal")
     return o, lse
 
@@ -204,7 +229,7 @@ def rtr_kv_commit_inplace(kv, n_frames):
 
 
 def rtr_attn_stream_step(kv, q, k, v, chunk_frames, o=None, lse=None, scale=0.0, out_dtype=None,
-                         want_lse=False, stream=None):
+                         want_lse=False, workspace=None, stream=None):
     """One streaming step for a chunk of `chunk_frames` frames.  Returns (o, lse or None)."""
     import torch
     Tq, H, d = q.shape
@@ -213,8 +238,9 @@ def rtr_attn_stream_step(kv, q, k, v, chunk_frames, o=None, lse=None, scale=0.0,
         o = torch.empty((Tq, H, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(workspace)
     _check(lib().rtr_attn_stream_step(kv.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                      int(chunk_frames), _dtype_code(o), float(scale),
+                                      int(chunk_frames), _dtype_code(o), float(scale), ws, ws_bytes,
                                       _stream(stream, q.device)),
            "rtr_attn_stream_step")
     return o, lse

@@ -93,12 +93,36 @@ typedef struct {
  *   tokens_per_frame : k >= 1; k >= T gives the unmasked bidirectional teacher
  *   d       : 64 or 128
  *   scale   : logit scale; <= 0 selects 1/sqrt(d)
+ *   workspace, workspace_bytes : split-K scratch (see rtr_attn_workspace_size)
+ *             or NULL, 0
  * T == 0 is a no-op.  Returns RTR_OK or a negative rtr_status.
  * ---------------------------------------------------------------------- */
 int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, float *lse,
                           int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
                           rtr_dtype in_dtype, rtr_dtype out_dtype, float scale,
-                          rtr_stream stream);
+                          void *workspace, size_t workspace_bytes, rtr_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Split-K workspace.  Without one, each (head, block of query rows) is one
+ * workgroup that walks all its visible keys, and the longest such unit bounds
+ * the call.  With one (bf16 input, d == 128; otherwise it is accepted and
+ * unused), the visible key tiles of all units are shared out evenly over the
+ * GPU's compute units: a unit cut between two of them leaves unnormalised
+ * partial results (fp32 O, exponent reference and row sum per query) in the
+ * workspace, and a second kernel on the same stream merges them in a fixed
+ * order, O = sum_s w_s O_s / sum_s w_s l_s with w_s the softmax weights of
+ * the parts (the exact softmax over the union of their keys).  The result is
+ * deterministic and equals the unsplit one up to fp32 rounding.
+ *
+ * rtr_attn_workspace_size stores in *bytes the size the current HIP device
+ * needs (it depends on its compute-unit count, not on the token count; 0 when
+ * the configuration never splits).  The workspace is caller-owned device
+ * memory, 16-byte aligned, uninitialised on entry, clobbered on exit, and
+ * must not overlap any input, output or cache buffer.  Calls that may run
+ * concurrently need separate workspaces.  A workspace smaller than required
+ * is RTR_EINVAL.
+ * ---------------------------------------------------------------------- */
+int rtr_attn_workspace_size(int32_t d, rtr_dtype in_dtype, size_t *bytes);
 
 /* ------------------------------------------------------------------------
  * KV cache of one attention layer over caller-owned device buffers
@@ -139,10 +163,12 @@ int rtr_kv_commit_inplace(rtr_kv_cache *kv, int32_t n_frames);
  * placed after the cached frames).  The cache is only read; commit the chunk
  * afterwards with rtr_kv_append_evict.  o: [C*k, H, d] out_dtype; lse: [H, C*k]
  * float32 or NULL.  1 <= C <= RTR_MAX_CHUNK; scale <= 0 selects 1/sqrt(d).
+ * workspace, workspace_bytes: split-K scratch as for rtr_attn_block_causal.
  * ---------------------------------------------------------------------- */
 int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
-                         float scale, rtr_stream stream);
+                         float scale, void *workspace, size_t workspace_bytes,
+                         rtr_stream stream);
 
 /* Condition switch (Key Designs 4).  First the reference: KEEP leaves it,
  * REPLACE anchors ref_frames (1..R_cap) new frames k_ref, v_ref

@@ -48,11 +48,12 @@ def test_status_strings():
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE + MB, v=FAKE + 2 * MB, o=FAKE + 3 * MB, lse=None, T=64, H=2, d=128,
-             kpf=16, ind=rtr.RTR_BF16, outd=rtr.RTR_BF16, scale=0.0, stream=None)
+             kpf=16, ind=rtr.RTR_BF16, outd=rtr.RTR_BF16, scale=0.0, ws=None, ws_bytes=0,
+             stream=None)
     a.update(kw)
     return rtr.lib().rtr_attn_block_causal(a["q"], a["k"], a["v"], a["o"], a["lse"], a["T"],
                                            a["H"], a["d"], a["kpf"], a["ind"], a["outd"],
-                                           a["scale"], a["stream"])
+                                           a["scale"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,10 +72,22 @@ def _attn(**kw):
     (dict(o=FAKE + 64), rtr.RTR_EINVAL),              # o overlaps q
     (dict(lse=FAKE + 3 * MB), rtr.RTR_EINVAL),        # lse overlaps o
     (dict(scale=float("inf")), rtr.RTR_EINVAL),
+    (dict(ws=FAKE + 8 * MB + 8, ws_bytes=MB), rtr.RTR_EINVAL),  # misaligned workspace
+    (dict(ws=FAKE + 2 * MB, ws_bytes=MB), rtr.RTR_EINVAL),      # workspace overlaps v
 ])
 def test_block_causal_rejects_before_launch(kw, code):
     assert _attn(**kw) == code
     assert rtr.lib().rtr_last_error()
+
+
+def test_workspace_size_args():
+    L = rtr.lib()
+    n = ctypes.c_size_t(7)
+    assert L.rtr_attn_workspace_size(64, rtr.RTR_BF16, ctypes.byref(n)) == rtr.RTR_OK and n.value == 0
+    assert L.rtr_attn_workspace_size(128, rtr.RTR_F32, ctypes.byref(n)) == rtr.RTR_OK and n.value == 0
+    assert L.rtr_attn_workspace_size(96, rtr.RTR_BF16, ctypes.byref(n)) == rtr.RTR_EUNSUPPORTED
+    assert L.rtr_attn_workspace_size(128, 9, ctypes.byref(n)) == rtr.RTR_EINVAL
+    assert L.rtr_attn_workspace_size(128, rtr.RTR_BF16, None) == rtr.RTR_EINVAL
 
 
 def test_block_causal_empty_is_noop():
@@ -127,13 +140,16 @@ def test_failed_calls_change_nothing():
     assert L.rtr_kv_reset_ref(h, rtr.RTR_REF_REPLACE, FAKE + 900 * MB, None, 1, 1, None) == rtr.RTR_EINVAL
     assert L.rtr_kv_reset_ref(h, rtr.RTR_REF_KEEP, None, None, 0, -2, None) == rtr.RTR_EINVAL
     assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
-                                  FAKE + 903 * MB, None, 0, 0, 0.0, None) == rtr.RTR_EUNSUPPORTED
+                                  FAKE + 903 * MB, None, 0, 0, 0.0, None, 0, None) == rtr.RTR_EUNSUPPORTED
     assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
-                                  FAKE, None, 1, 0, 0.0, None) == rtr.RTR_EINVAL  # o over ring
+                                  FAKE, None, 1, 0, 0.0, None, 0, None) == rtr.RTR_EINVAL  # o over ring
+    assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
+                                  FAKE + 903 * MB, None, 1, 0, 0.0, FAKE + 1024, MB,
+                                  None) == rtr.RTR_EINVAL  # workspace over the ring
     assert L.rtr_attn_stream_step(h, None, FAKE + 901 * MB, FAKE + 902 * MB,
-                                  FAKE + 903 * MB, None, 1, 0, 0.0, None) == rtr.RTR_EINVAL
+                                  FAKE + 903 * MB, None, 1, 0, 0.0, None, 0, None) == rtr.RTR_EINVAL
     assert L.rtr_attn_stream_step(None, FAKE, FAKE, FAKE, FAKE, None, 1, 0, 0.0,
-                                  None) == rtr.RTR_EINVAL
+                                  None, 0, None) == rtr.RTR_EINVAL
     bad = rtr.rtr_kv_get_state(kv)
     bad.count = 2
     bad.frame_id[1] = bad.frame_id[0]          # ids must increase

@@ -24,14 +24,26 @@ TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 RTR_DT = {"bf16": rtr.RTR_BF16, "f32": rtr.RTR_F32}
 
 
-def _run_full(q, k, v, kpf, out_dtype, scale=0.0):
+def _workspace(d, dtype=rtr.RTR_BF16):
+    """A split-K workspace inside guard bands (None when the configuration
+    never splits), and the check that nothing was written outside it."""
+    n = rtr.rtr_attn_workspace_size(d, dtype)
+    if n == 0:
+        return None, lambda: None
+    return guarded_empty((n,), torch.uint8)
+
+
+def _run_full(q, k, v, kpf, out_dtype, scale=0.0, split=False):
     T, H, d = q.shape
     o, chk_o = guarded_empty((T, H, d), out_dtype)
     lse, chk_l = guarded_empty((H, T), torch.float32)
-    rtr.rtr_attn_block_causal(dev(q), dev(k), dev(v), kpf, o=o, lse=lse, scale=scale)
+    ws, chk_w = _workspace(d, RTR_DT["bf16"] if q.dtype == "bf16" else RTR_DT["f32"]) if split \
+        else (None, lambda: None)
+    rtr.rtr_attn_block_causal(dev(q), dev(k), dev(v), kpf, o=o, lse=lse, scale=scale, workspace=ws)
     torch.cuda.synchronize()
     chk_o()
     chk_l()
+    chk_w()
     return host(o), host(lse)
 
 
@@ -79,9 +91,10 @@ def _as_values(bits_or_vals, dtype):
 
 
 def _stream_rollout(kpf, H, d, C, W, R, steps, dtype, switches=(), seed=0, out_dtype=None,
-                    check_bytes=True):
+                    check_bytes=True, split=False):
     """Drive the library and the ListKV oracle in lockstep; returns worst errors."""
     kv, kr, vr, kf, vf = _make_cache(W, R, kpf, H, d, dtype)
+    ws, chk_w = _workspace(d, RTR_DT[dtype]) if split else (None, lambda: None)
     ref = ListKV(W)
     out_dtype = out_dtype or TORCH_DT[dtype]
     worst = []
@@ -102,10 +115,11 @@ def _stream_rollout(kpf, H, d, C, W, R, steps, dtype, switches=(), seed=0, out_d
         o, chk = guarded_empty((C * kpf, H, d), out_dtype)
         lse, chk2 = guarded_empty((H, C * kpf), torch.float32)
         kd, vd = dev(k), dev(v)
-        rtr.rtr_attn_stream_step(kv, dev(q), kd, vd, C, o=o, lse=lse)
+        rtr.rtr_attn_stream_step(kv, dev(q), kd, vd, C, o=o, lse=lse, workspace=ws)
         torch.cuda.synchronize()
         chk()
         chk2()
+        chk_w()
         pk, pv = ref.prefix(kpf, H, d, dtype=k.storage().dtype)
         ro, rl = oracle.attn_stream_step(_as_values(pk, dtype), _as_values(pv, dtype), q.values,
                                          k.values, v.values, kpf)
@@ -145,9 +159,10 @@ FULL_CASES = [
 
 @pytest.mark.parametrize("T,kpf,H,d", FULL_CASES)
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_bf16_full_form(T, kpf, H, d, out):
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_bf16_full_form(T, kpf, H, d, out, split):
     q, k, v = gen.full_sequence_inputs(T, H, d, "bf16", base_seed=1, wid=30, step=T + kpf)
-    o, lse = _run_full(q, k, v, kpf, TORCH_DT[out])
+    o, lse = _run_full(q, k, v, kpf, TORCH_DT[out], split=split)
     ro, rl = oracle.attn_block_causal(q.values, k.values, v.values, kpf)
     assert_bf16_close(o, ro, "o")
     assert_bf16_close(lse, rl, "lse")
@@ -162,11 +177,12 @@ def test_fp32_full_form_several_tiles(T, kpf):
     assert_f32_close(lse, rl, "lse")
 
 
-def test_bf16_stream_with_switches():
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_bf16_stream_with_switches(split):
     sw = {0: (REF_REPLACE, -1), 4: (REF_REPLACE, 1), 6: (REF_KEEP, 2), 8: (REF_CLEAR, 0),
           9: (REF_REPLACE, -1)}
     _stream_rollout(kpf=100, H=2, d=128, C=2, W=3, R=1, steps=11, dtype="bf16",
-                    switches=sw.items())
+                    switches=sw.items(), split=split)
 
 
 @pytest.mark.parametrize("kpf,H,d,C,W,R,steps", [
@@ -176,10 +192,11 @@ def test_bf16_stream_with_switches():
     (24, 1, 128, 16, 4, 1, 2),    # largest chunk
     (8, 1, 64, 1, 64, 1, 66),     # largest window, wraps around
 ])
-def test_bf16_stream_edges(kpf, H, d, C, W, R, steps):
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_bf16_stream_edges(kpf, H, d, C, W, R, steps, split):
     sw = {0: (REF_REPLACE, -1)} if R else {}
     _stream_rollout(kpf=kpf, H=H, d=d, C=C, W=W, R=R, steps=steps, dtype="bf16",
-                    switches=sw.items())
+                    switches=sw.items(), split=split)
 
 
 def test_stream_f32_output_of_bf16_cache():
@@ -188,12 +205,14 @@ def test_stream_f32_output_of_bf16_cache():
 
 
 # ------------------------------------------------------------ invariants on the GPU
-def test_causality_bitwise_and_determinism():
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_causality_bitwise_and_determinism(split):
     T, H, d, kpf = 1560 * 4, 2, 128, 1560
     q, k, v = gen.full_sequence_inputs(T, H, d, "bf16", base_seed=3, wid=32)
     qd, kd, vd = dev(q), dev(k), dev(v)
-    o1, l1 = rtr.rtr_attn_block_causal(qd, kd, vd, kpf, want_lse=True)
-    o2, l2 = rtr.rtr_attn_block_causal(qd, kd, vd, kpf, want_lse=True)
+    ws = rtr.new_workspace(d) if split else None
+    o1, l1 = rtr.rtr_attn_block_causal(qd, kd, vd, kpf, want_lse=True, workspace=ws)
+    o2, l2 = rtr.rtr_attn_block_causal(qd, kd, vd, kpf, want_lse=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
@@ -202,14 +221,15 @@ def test_causality_bitwise_and_determinism():
     kd2[cut:] = -kd2[cut:] * 4
     vd2[cut:] = vd2[cut:] + 3
     qd2[cut:] = qd2[cut:] * 2
-    o3, l3 = rtr.rtr_attn_block_causal(qd2, kd2, vd2, kpf, want_lse=True)
+    o3, l3 = rtr.rtr_attn_block_causal(qd2, kd2, vd2, kpf, want_lse=True, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(o1[:cut].view(torch.int16), o3[:cut].view(torch.int16))
     assert torch.equal(l1[:, :cut], l3[:, :cut])
     assert not torch.equal(o1[cut:], o3[cut:])
 
 
-def test_full_shape_closed_form_frame_mean():
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_full_shape_closed_form_frame_mean(split):
     # Full block-causal workload shape (22 frames x 1560 tokens, 12 heads,
     # head_dim 128): Q = 0 makes all visible logits 0, and V_j = floor(j/k)
     # gives O_i = floor(i/k)/2 exactly and LSE_i = ln(k (floor(i/k) + 1)).
@@ -219,7 +239,8 @@ def test_full_shape_closed_form_frame_mean():
     kk = torch.randn((T, H, d), device="cuda").to(torch.bfloat16) * 0
     fr = torch.arange(T, device="cuda") // kpf
     v = fr[:, None, None].expand(T, H, d).to(torch.bfloat16).contiguous()
-    o, lse = rtr.rtr_attn_block_causal(q, kk, v, kpf, want_lse=True)
+    ws = rtr.new_workspace(d) if split else None
+    o, lse = rtr.rtr_attn_block_causal(q, kk, v, kpf, want_lse=True, workspace=ws)
     torch.cuda.synchronize()
     expect = (fr.float() / 2)[:, None, None].expand(T, H, d)
     assert torch.equal(o.float(), expect)
@@ -252,16 +273,20 @@ def _stream_workload(name, seed=0):
 
 
 @pytest.mark.parametrize("name", ["wan13b_stream_step", "wan14b_stream_step"])
-def test_full_size_stream_step_sampled(name):
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_full_size_stream_step_sampled(name, split):
     w, x, kv, bufs = _stream_workload(name)
     kpf, H, d, C = w["k"], w["H"], w["d"], w["C"]
     Tq = C * kpf
     o, chk = guarded_empty((Tq, H, d), torch.bfloat16)
     lse, chk2 = guarded_empty((H, Tq), torch.float32)
-    rtr.rtr_attn_stream_step(kv, dev(x["q"]), dev(x["k"]), dev(x["v"]), C, o=o, lse=lse)
+    ws, chk_w = _workspace(d) if split else (None, lambda: None)
+    rtr.rtr_attn_stream_step(kv, dev(x["q"]), dev(x["k"]), dev(x["v"]), C, o=o, lse=lse,
+                             workspace=ws)
     torch.cuda.synchronize()
     chk()
     chk2()
+    chk_w()
     # prefix in logical order: reference, then the W window frames oldest first
     pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
     pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
@@ -277,17 +302,20 @@ def test_full_size_stream_step_sampled(name):
     assert bool(torch.isfinite(o.float()).all())
 
 
-def test_full_size_block_causal_sampled():
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_full_size_block_causal_sampled(split):
     w = gen.WORKLOADS["full_block_causal"]
     kpf, H, d, F = w["k"], w["H"], w["d"], w["frames"]
     T = kpf * F
     q, k, v = gen.full_sequence_inputs(T, H, d, "bf16", base_seed=0, wid=w["wid"])
     o, chk = guarded_empty((T, H, d), torch.bfloat16)
     lse, chk2 = guarded_empty((H, T), torch.float32)
-    rtr.rtr_attn_block_causal(dev(q), dev(k), dev(v), kpf, o=o, lse=lse)
+    ws, chk_w = _workspace(d) if split else (None, lambda: None)
+    rtr.rtr_attn_block_causal(dev(q), dev(k), dev(v), kpf, o=o, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     chk()
     chk2()
+    chk_w()
     rows = _sample_rows(T, kpf, 16, seed=6)[::3]
     heads = [0, 7]
     ro, rl = oracle.attn_rows(q.values, k.values, v.values, kpf, rows, heads)
@@ -333,8 +361,37 @@ def test_full_size_stream_closed_form_labels():
         fid += C
 
 
+def test_split_matches_plain_at_full_size():
+    # The split schedule changes the order of the fp32 additions and, since
+    # each piece rounds P to bf16 relative to its own exponent reference, the
+    # bf16 rounding of individual weights (relative 2^-9, averaged over ~1.5e4
+    # keys per row).  Against the one-workgroup-per-unit launch it must stay
+    # an order of magnitude inside the bf16 bar on the max and mean.
+    w, x, kv, bufs = _stream_workload("wan13b_stream_step", seed=3)
+    C = w["C"]
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    o1, l1 = rtr.rtr_attn_stream_step(kv, q, k, v, C, want_lse=True, out_dtype=torch.float32)
+    o2, l2 = rtr.rtr_attn_stream_step(kv, q, k, v, C, want_lse=True, out_dtype=torch.float32,
+                                      workspace=rtr.new_workspace(w["d"]))
+    torch.cuda.synchronize()
+    d = (o1 - o2).abs()
+    assert float(d.max()) < 2e-3 and float(d.mean()) < 1e-4
+    assert float((l1 - l2).abs().max()) < 1e-3   # row sums of bf16-rounded weights
+
+
+def test_split_workspace_too_small_is_rejected():
+    q = torch.zeros((512, 1, 128), dtype=torch.bfloat16, device="cuda")
+    need = rtr.rtr_attn_workspace_size(128)
+    assert need > 0
+    small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.rtr_attn_block_causal(q, q, q, 64, workspace=small)
+    assert e.value.code == rtr.RTR_EINVAL
+
+
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_softmax_reference_fallback_rows(out):
+@pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
+def test_softmax_reference_fallback_rows(out, split):
     # Rows whose scores grow far beyond their first key tile's maximum (here
     # by 512 / sqrt(128) natural units, i.e. a factor 2^65 in the softmax
     # numerator) take the exact-maximum second pass; rows of the same
@@ -350,7 +407,7 @@ def test_softmax_reference_fallback_rows(out):
     q, k, v = (gen.from_values(gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(x)), "bf16")
                for x in (q, k, v))
     for kpf in (T, 100):
-        o, lse = _run_full(q, k, v, kpf, TORCH_DT[out])
+        o, lse = _run_full(q, k, v, kpf, TORCH_DT[out], split=split)
         ro, rl = oracle.attn_block_causal(q.values, k.values, v.values, kpf)
         assert_bf16_close(o, ro, f"o k={kpf}")
         assert_bf16_close(lse, rl, f"lse k={kpf}")
