@@ -514,19 +514,25 @@ enum DmaMode : int {
 template <int MODE>
 __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
-    constexpr int TILE = BN * D, STAGE = 2 * TILE;  // elements
+    constexpr int TILE = BN * D;  // elements of one K or V tile
+    constexpr int NSTG = 5;       // LDS ring depth
     constexpr bool FAST = MODE == kDmaFast;
-    // Tile t lives in stage t mod 4: K at STAGE * (t mod 4), V right after it.
-    __shared__ __attribute__((aligned(16))) uint16_t sKV[4 * STAGE];
+    // Tile t lives in stage (t mod 5): K tiles in one region and V tiles in
+    // another, so every fragment read is a per-lane base plus an immediate
+    // offset below 64 KB.
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[NSTG * TILE];
     __shared__ const uint16_t *sSegK[FAST ? 1 : kMaxKeyFrames];
     __shared__ const uint16_t *sSegV[FAST ? 1 : kMaxKeyFrames];
     __shared__ int sRedo;
-    lds_u16 *const sbase = (lds_u16 *)sKV;
+    lds_u16 *const kbase = (lds_u16 *)sK;
+    lds_u16 *const vbase = (lds_u16 *)sV;
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -555,6 +561,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
             sSegV[f] = (const uint16_t *)a.vseg[f];
         }
     }
+    // The V stage that holds "tile -1" when a sweep starts is read by the
+    // first step's (zero-weight) PV: make it finite.
+    for (int i = tid; i < TILE / 8; i += 256) *(u32x4 *)&sV[(NSTG - 1) * TILE + 8 * i] = u32x4{0, 0, 0, 0};
     if (tid == 0) sRedo = 0;
     __syncthreads();
 
@@ -578,13 +587,14 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     uint32_t kvo[2], vvo[2];  // per-lane byte offsets from the group's first row
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        kch[i] = pch ^ (4 * i + lr);                       // (row mod 8) = 4 i + lr
-        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);     // (row mod 4) = lr
+        kch[i] = pch ^ (4 * i + lr);                    // (row mod 8) = 4 i + lr
+        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
         kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
-    const uint32_t lds0 = lds_addr(sbase);
-    auto m0k = [&](int S, int i) { return lds0 + (uint32_t)((S * STAGE + (8 * wave + 4 * i) * D) * 2); };
+    const uint32_t k_lds = lds_addr(kbase), v_lds = lds_addr(vbase);
+    auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (8 * wave + 4 * i) * D) * 2); };
+    auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (8 * wave + 4 * i) * D) * 2); };
 
     // Key cursor of the next tile to prefetch (tiles are prefetched in order
     // within a sweep): segment cf and key offset co inside it, wave-uniform.
@@ -600,7 +610,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         if constexpr (FAST) sp = load_seg_ptrs(cf);
     };
     auto issue = [&](int tile, auto S) {
-        constexpr int st = decltype(S)::value & 3;
+        constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -609,7 +619,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
                 const long rr = nxt ? row - a.seg_len : row;
                 const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
                 dma16_sbase((nxt ? sp.k1 : sp.k0) + off, kvo[i], m0k(st, i));
-                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0k(st, i) + TILE * 2);
+                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0v(st, i));
             }
             co += BN;
             if (co >= a.seg_len) {
@@ -630,7 +640,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
                     vp = sSegV[f] + o + vch[i] * 8;
                 }
                 dma16_vaddr(kp, m0k(st, i));
-                dma16_vaddr(vp, m0k(st, i) + TILE * 2);
+                dma16_vaddr(vp, m0v(st, i));
             }
         }
     };
@@ -639,13 +649,13 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // upper half of d and the key steps are immediate offsets.
     const lds_u16 *kfp[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kfp[s] = sbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
+    for (int s = 0; s < 4; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
     const int G = lane >> 4, sl = lane & 15;
     const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
     const lds_u16 *vfp[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-        vfp[t] = sbase + TILE + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+        vfp[t] = vbase + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
 
     // Softmax with a fixed per-row exponent reference (log2 units): P =
     // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
@@ -666,19 +676,19 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
     // transposed 8-byte reads each).
     auto read_k = [&](auto S, bf16x8 *kf) {
-        constexpr int st = decltype(S)::value & 3;
+        constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * STAGE + (s >> 2) * 64));
+            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * TILE + (s >> 2) * 64));
     };
     auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
-        constexpr int st = decltype(S)::value & 3;
+        constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s) * D);
-                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s + 8) * D);
+                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s + 8) * D);
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
@@ -733,19 +743,24 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
             }
     };
 
-    // Software pipeline over key tiles.  Step t (stage t mod 4): wait until
-    // this wave's DMA of tile t+1 has landed (tile t+2 may still be in
-    // flight), barrier (every wave's DMA of t+1 has landed; every wave is done
-    // with tile t-1, whose stage takes tile t+3), prefetch tile t+3, then in one
-    // basic block: S(t+1) on the matrix cores while the VALU turns S(t) into P,
-    // followed by O += V(t) P.  Steps past the last tile are fully masked (P =
-    // 0) and only keep the DMA counts static.
+    // Software pipeline over key tiles, PV one tile behind the softmax.  Step
+    // t (stage s(t) = t mod 5): wait until this wave's DMA of tile t+1 has
+    // landed (t+2 may still be in flight), barrier (every wave's DMA of t+1 has
+    // landed; every wave is done with step t-1, so the stage of tile t-2 is
+    // free), then in one basic block: S(t+1) = K(t+1) Q^T and O += V(t-1)
+    // P(t-1) on the matrix cores while the VALU turns S(t) into P(t) (the
+    // softmax needs only registers, so it starts right after the barrier while
+    // the fragment reads are in flight), and the prefetch of tile t+3 into the
+    // stage of tile t-2.  The step after the last tile only adds the last PV
+    // (its tile is past every row's limit, so its P is 0).
     //
     // Masked steps: a row whose limit lies at or below the tile start takes an
     // infinite exponent reference (P = 0); the element-wise mask runs only when
     // some row's limit falls inside the tile, at most a few tiles per block.
     f32x16 scur[2];
+    bf16x8 pprev[2][2];
     auto step = [&](int t, auto S, auto masked, auto maxonly) {
+        constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
         load_ptrs();  // segment pointers of tile t + 3
@@ -768,13 +783,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
                 apply_mask(scur, t);
             }
         }
-        // All fragment reads first (K of tile t+1, V of tile t), so their LDS
-        // latency hides behind the MFMAs and VALU work that follows.
         bf16x8 kf[NS];
         v4i16 vf[NT][2][2];
-        read_k(std::integral_constant<int, (decltype(S)::value + 1) & 3>{}, kf);
+        read_k(std::integral_constant<int, (s0 + 1) % NSTG>{}, kf);
         __builtin_amdgcn_sched_barrier(0);  // the K reads go first
-        if (!MAXONLY) read_v(S, vf);
+        if (!MAXONLY) read_v(std::integral_constant<int, (s0 + NSTG - 1) % NSTG>{}, vf);
         f32x16 snext[2];
         qk(kf, snext);
         if (MAXONLY) {
@@ -783,22 +796,26 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         } else {
             bf16x8 pf[2][2];
             softmax(scur, pf, mr);
-            pv(vf, pf);
+            pv(vf, pprev);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) pprev[b][h] = pf[b][h];
         }
-        issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
+        issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
         if (!MAXONLY) {
-            // The QK(t+1) MFMAs interleaved with the softmax VALU of tile t and
-            // one V read each, then the PV(t) MFMAs interleaved with the rest.
+            // 32 MFMAs (QK of t+1, PV of t-1) carry the 128 softmax VALU of tile
+            // t and the 16 V fragment reads.
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
             }
         }
         scur[0] = snext[0];
@@ -826,22 +843,33 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
 #pragma unroll
             for (int b = 0; b < 2; ++b) mref[b] = rowmax(scur[b]) * c;
         }
-        // Groups of four steps (static stages): unmasked while the whole group
-        // is visible to every row, masked from there on.
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pprev[b][h] = bf16x8{};
+        // Groups of five steps (static stages): unmasked while the whole group
+        // is visible to every row, masked from there on, up to the step after
+        // the last tile (which only adds the last PV).
         int base = 0;
 #pragma unroll 1
-        for (; base + 4 <= nfull; base += 4) {
+        for (; base + 5 <= nfull; base += 5) {
             step(base, I0{}, std::false_type{}, maxonly);
             step(base + 1, I1{}, std::false_type{}, maxonly);
             step(base + 2, I2{}, std::false_type{}, maxonly);
             step(base + 3, I3{}, std::false_type{}, maxonly);
+            step(base + 4, I4{}, std::false_type{}, maxonly);
         }
 #pragma unroll 1
-        for (; base < ntiles; base += 4) {
+        for (; base <= ntiles; base += 5) {
             step(base, I0{}, std::true_type{}, maxonly);
+            if (base + 1 > ntiles) break;
             step(base + 1, I1{}, std::true_type{}, maxonly);
+            if (base + 2 > ntiles) break;
             step(base + 2, I2{}, std::true_type{}, maxonly);
+            if (base + 3 > ntiles) break;
             step(base + 3, I3{}, std::true_type{}, maxonly);
+            if (base + 4 > ntiles) break;
+            step(base + 4, I4{}, std::true_type{}, maxonly);
         }
         // drain the look-ahead tiles before the stages are reused
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -861,7 +889,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     for (int b = 0; b < 2; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
     if (__builtin_amdgcn_ballot_w64(redo[0] || redo[1]) && lane == 0) sRedo = 1;
     __syncthreads();
-    if (sRedo) {
+    if (__builtin_amdgcn_readfirstlane(sRedo)) {
         asm volatile("");
         sweep(false, std::true_type{});  // exact row maxima
         __syncthreads();
