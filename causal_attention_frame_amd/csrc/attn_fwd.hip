@@ -465,6 +465,22 @@ __device__ inline void dma16_sbase(uint64_t sbase, uint32_t voff, uint32_t m0) {
                  : "v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
 }
+// Four such loads in one statement: (K, V) of row group 0, then of group 1.
+// Every SGPR operand is written before the statement, so one 5-wait-state
+// guard covers them all; each later m0 write needs one wait state.
+__device__ inline void dma16x4_sbase(uint64_t kb0, uint64_t vb0, uint64_t kb1, uint64_t vb1, uint32_t ko0,
+                                     uint32_t vo0, uint32_t ko1, uint32_t vo1, uint32_t mk0, uint32_t mv0,
+                                     uint32_t mk1, uint32_t mv1) {
+    asm volatile(
+        "s_mov_b32 m0, %4\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %8\n\t"
+        "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\t"
+        "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
+        "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %11"
+        :
+        : "v"(ko0), "v"(vo0), "v"(ko1), "v"(vo1), "s"(mk0), "s"(mv0), "s"(mk1), "s"(mv1), "s"(kb0), "s"(vb0),
+          "s"(kb1), "s"(vb1)
+        : "memory", "m0");
+}
 // Same, from a per-lane 64-bit address.
 __device__ inline void dma16_vaddr(const void *src, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
@@ -612,15 +628,18 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     auto issue = [&](int tile, auto S) {
         constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
+            uint64_t kb[2], vb[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int row = co + 8 * wave + 4 * i;
                 const bool nxt = row >= a.seg_len;
                 const long rr = nxt ? row - a.seg_len : row;
                 const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-                dma16_sbase((nxt ? sp.k1 : sp.k0) + off, kvo[i], m0k(st, i));
-                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0v(st, i));
+                kb[i] = (nxt ? sp.k1 : sp.k0) + off;
+                vb[i] = (nxt ? sp.v1 : sp.v0) + off;
             }
+            dma16x4_sbase(kb[0], vb[0], kb[1], vb[1], kvo[0], vvo[0], kvo[1], vvo[1], m0k(st, 0), m0v(st, 0),
+                          m0k(st, 1), m0v(st, 1));
             co += BN;
             if (co >= a.seg_len) {
                 co -= a.seg_len;
