@@ -413,16 +413,19 @@ void attn_fwd_bf16(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 inputs, head_dim 128: 64 query rows per wave, K/V staged by LDS DMA.
+// bf16 inputs, head_dim 128: 8 waves x 32 query rows, K/V staged by LDS DMA.
 // ---------------------------------------------------------------------------
-// A workgroup is 4 waves x 64 query rows; each wave owns two 32-row MFMA
-// blocks, so every K/V fragment read from LDS feeds two MFMAs.  Keys advance in
-// 32-key tiles held in a 4-stage LDS ring that global_load_lds fills three
-// tiles ahead of the compute (16 bytes per lane go straight from global memory
-// to LDS: no staging registers, no VALU).  Layout of a stage (row-major, 256 B
-// per key row, K tile then V tile):
-//   K: the 16-byte chunks of row r are XOR-swizzled by r mod 8, which spreads
-//      the ds_read_b128 of the MFMA A operand (lane n reads row n) over banks;
+// A workgroup is 8 waves x 32 query rows of one head, two waves per SIMD: at
+// 256 registers a wave, one wave's softmax VALU issues while the other's MFMAs
+// run (a single wave per SIMD issues a VALU op only every ~7 cycles, so its
+// softmax, not the matrix cores, set the pace).  Keys advance in 32-key tiles
+// held in a 5-stage LDS ring that global_load_lds fills three tiles ahead of
+// the compute (16 bytes per lane go straight from global memory to LDS: no
+// staging registers, no VALU).  Layout of a stage (row-major, 256 B per key
+// row; K tiles in one region, V tiles in another):
+//   K: the 16-byte chunks of row r are XOR-swizzled by r mod 16: a
+//      ds_read_b128 serves 16 lanes (rows n..n+15 of the MFMA A operand) per
+//      pass over the 64 banks, and the swizzle gives them 16 distinct chunks;
 //   V: the 32-byte chunk pairs of row r are XOR-swizzled by r mod 4 and the
 //      tile is read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
 //      lane one d column over 4 keys -- the V^T A operand of the PV MFMA in the
@@ -465,20 +468,15 @@ __device__ inline void dma16_sbase(uint64_t sbase, uint32_t voff, uint32_t m0) {
                  : "v"(voff), "s"(sbase), "s"(m0)
                  : "memory", "m0");
 }
-// Four such loads in one statement: (K, V) of row group 0, then of group 1.
-// Every SGPR operand is written before the statement, so one 5-wait-state
-// guard covers them all; each later m0 write needs one wait state.
-__device__ inline void dma16x4_sbase(uint64_t kb0, uint64_t vb0, uint64_t kb1, uint64_t vb1, uint32_t ko0,
-                                     uint32_t vo0, uint32_t ko1, uint32_t vo1, uint32_t mk0, uint32_t mv0,
-                                     uint32_t mk1, uint32_t mv1) {
+// Two such loads in one statement (the K and the V row group of a tile); every
+// SGPR operand is written before the statement, so one 5-wait-state guard
+// covers both, and the second m0 write needs one wait state.
+__device__ inline void dma16x2_sbase(uint64_t kb, uint64_t vb, uint32_t ko, uint32_t vo, uint32_t mk, uint32_t mv) {
     asm volatile(
-        "s_mov_b32 m0, %4\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %8\n\t"
-        "s_mov_b32 m0, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %9\n\t"
-        "s_mov_b32 m0, %6\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %10\n\t"
-        "s_mov_b32 m0, %7\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %11"
+        "s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5"
         :
-        : "v"(ko0), "v"(vo0), "v"(ko1), "v"(vo1), "s"(mk0), "s"(mv0), "s"(mk1), "s"(mv1), "s"(kb0), "s"(vb0),
-          "s"(kb1), "s"(vb1)
+        : "v"(ko), "v"(vo), "s"(mk), "s"(mv), "s"(kb), "s"(vb)
         : "memory", "m0");
 }
 // Same, from a per-lane 64-bit address.
@@ -509,8 +507,8 @@ __device__ inline SegPtrs load_seg_ptrs(int f) {
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
-constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4): all but this wave's 4 newest loads done
-constexpr int kWaitVm8 = 0x0F78;    // vmcnt(8)
+constexpr int kWaitVm2 = 0x0F72;    // vmcnt(2): all but this wave's 2 newest loads done
+constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
@@ -528,8 +526,9 @@ enum DmaMode : int {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
+__global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
+    constexpr int NB = 1;  // 32-row query blocks per wave (8 waves)
     constexpr int TILE = BN * D;  // elements of one K or V tile
     constexpr int NSTG = 5;       // LDS ring depth
     constexpr bool FAST = MODE == kDmaFast;
@@ -560,11 +559,11 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
 
-    int qi[2], lim[2];
-    bool qv[2];
+    int qi[NB], lim[NB];
+    bool qv[NB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        qi[b] = q0 + 64 * wave + 32 * b + n;
+    for (int b = 0; b < NB; ++b) {
+        qi[b] = q0 + 32 * NB * wave + 32 * b + n;
         qv[b] = qi[b] < a.Tq;
         lim[b] = key_limit(qv[b] ? qi[b] : a.Tq - 1, a);
     }
@@ -572,21 +571,18 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
 
     if (!FAST) {
-        for (int f = tid; f < a.nseg; f += 256) {
+        for (int f = tid; f < a.nseg; f += 512) {
             sSegK[f] = (const uint16_t *)a.kseg[f];
             sSegV[f] = (const uint16_t *)a.vseg[f];
         }
     }
-    // The V stage that holds "tile -1" when a sweep starts is read by the
-    // first step's (zero-weight) PV: make it finite.
-    for (int i = tid; i < TILE / 8; i += 256) *(u32x4 *)&sV[(NSTG - 1) * TILE + 8 * i] = u32x4{0, 0, 0, 0};
     if (tid == 0) sRedo = 0;
     __syncthreads();
 
-    // Q^T B operands of both blocks: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
-    bf16x8 qf[2][NS];
+    // Q^T B operands: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
+    bf16x8 qf[NB][NS];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const uint16_t *qrow = (const uint16_t *)a.q + (long)(qv[b] ? qi[b] : a.Tq - 1) * a.ld + hoff;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -595,22 +591,22 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         }
     }
 
-    // DMA: in group i (i = 0, 1) this wave fills tile rows 8 wave + 4 i + lr,
-    // lane (lr, pch) the physical 16-byte chunk pch, fetching the logical chunk
-    // that the swizzle puts there.
+    // DMA: this wave fills tile rows 4 wave + lr of K and of V, lane (lr, pch)
+    // the physical 16-byte chunk pch, fetching the logical chunk that the
+    // swizzle puts there.
     const int lr = lane >> 4, pch = lane & 15;
-    int kch[2], vch[2];
-    uint32_t kvo[2], vvo[2];  // per-lane byte offsets from the group's first row
+    int kch[1], vch[1];
+    uint32_t kvo[1], vvo[1];  // per-lane byte offsets from the group's first row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        kch[i] = pch ^ (4 * i + lr);                    // (row mod 8) = 4 i + lr
+    for (int i = 0; i < 1; ++i) {
+        kch[i] = pch ^ (4 * (wave & 3) + lr);           // (row mod 16) = 4 (wave mod 4) + lr
         vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
         kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
     const uint32_t k_lds = lds_addr(kbase), v_lds = lds_addr(vbase);
-    auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (8 * wave + 4 * i) * D) * 2); };
-    auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (8 * wave + 4 * i) * D) * 2); };
+    auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
+    auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
 
     // Key cursor of the next tile to prefetch (tiles are prefetched in order
     // within a sweep): segment cf and key offset co inside it, wave-uniform.
@@ -628,18 +624,12 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     auto issue = [&](int tile, auto S) {
         constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
-            uint64_t kb[2], vb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = co + 8 * wave + 4 * i;
-                const bool nxt = row >= a.seg_len;
-                const long rr = nxt ? row - a.seg_len : row;
-                const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-                kb[i] = (nxt ? sp.k1 : sp.k0) + off;
-                vb[i] = (nxt ? sp.v1 : sp.v0) + off;
-            }
-            dma16x4_sbase(kb[0], vb[0], kb[1], vb[1], kvo[0], vvo[0], kvo[1], vvo[1], m0k(st, 0), m0v(st, 0),
-                          m0k(st, 1), m0v(st, 1));
+            const int row = co + 4 * wave;
+            const bool nxt = row >= a.seg_len;
+            const long rr = nxt ? row - a.seg_len : row;
+            const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
+            dma16x2_sbase((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
+                          m0v(st, 0));
             co += BN;
             if (co >= a.seg_len) {
                 co -= a.seg_len;
@@ -648,8 +638,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         } else {
             const int j0 = tile * BN;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int j = j0 + 8 * wave + 4 * i + lr;
+            for (int i = 0; i < 1; ++i) {
+                const int j = j0 + 4 * wave + 4 * i + lr;
                 const uint16_t *kp = kZeroRow + kch[i] * 8;
                 const uint16_t *vp = kZeroRow + vch[i] * 8;
                 if (j < a.Tk) {
@@ -666,9 +656,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
 
     // Per-lane LDS pointers of the fragment reads in stage 0; the stage, the
     // upper half of d and the key steps are immediate offsets.
-    const lds_u16 *kfp[4];
+    const lds_u16 *kfp[NS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
+    for (int s = 0; s < NS; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 15)) << 3);
     const int G = lane >> 4, sl = lane & 15;
     const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
     const lds_u16 *vfp[2];
@@ -684,8 +674,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // as reference.  The accumulators are therefore touched only by MFMAs inside
     // the key loop.  Each row's result depends on its own scores only.  The row
     // sum adds the bf16-rounded P that the PV product uses.
-    f32x16 acc[2][NT];
-    float mref[2] = {0.f, 0.f}, l[2] = {0.f, 0.f}, mmax[2] = {-INFINITY, -INFINITY};
+    f32x16 acc[NB][NT];
+    float mref[NB] = {0.f}, l[NB] = {0.f}, mmax[NB] = {-INFINITY};
     const float c = a.c;
 
     const int ntiles = (lim_wg + BN - 1) / BN;
@@ -698,7 +688,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * TILE + (s >> 2) * 64));
+            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s] + st * TILE));
     };
     auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
         constexpr int st = decltype(S)::value;
@@ -713,16 +703,12 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
     auto qk = [&](const bf16x8 *kf, f32x16 *s) {
         s[0] = f32x16{};
-        s[1] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], s[1], 0, 0, 0);
-        }
+        for (int st = 0; st < NS; ++st) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
     };
     auto apply_mask = [&](f32x16 *s, int tile) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (tile * BN + 8 * (r >> 2) + 4 * g + (r & 3) >= lim[b]) s[b][r] = -INFINITY;
@@ -736,7 +722,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
     auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -758,7 +744,6 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
                 const bf16x8 v = __builtin_bit_cast(
                     bf16x8, (v8i16)__builtin_shufflevector(vf[t][st][0], vf[t][st][1], 0, 1, 2, 3, 4, 5, 6, 7));
                 acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[0][st], acc[0][t], 0, 0, 0);
-                acc[1][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[1][st], acc[1][t], 0, 0, 0);
             }
     };
 
@@ -766,34 +751,36 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     // t (stage s(t) = t mod 5): wait until this wave's DMA of tile t+1 has
     // landed (t+2 may still be in flight), barrier (every wave's DMA of t+1 has
     // landed; every wave is done with step t-1, so the stage of tile t-2 is
-    // free), then in one basic block: S(t+1) = K(t+1) Q^T and O += V(t-1)
-    // P(t-1) on the matrix cores while the VALU turns S(t) into P(t) (the
-    // softmax needs only registers, so it starts right after the barrier while
-    // the fragment reads are in flight), and the prefetch of tile t+3 into the
-    // stage of tile t-2.  The step after the last tile only adds the last PV
-    // (its tile is past every row's limit, so its P is 0).
+    // free), then in one basic block: the K(t+1) fragment reads; O += V(t-1)
+    // P(t-1) from registers, each MFMA followed by the transposed reads of the
+    // V(t) fragments that take over its A operand's registers (they feed the
+    // PV of step t+1); then S(t+1) = K(t+1) Q^T; the VALU turns S(t) into P(t)
+    // under both; last the prefetch of tile t+3 into the stage of tile t-2.
+    // The step after the last tile only adds the last PV (its tile is past
+    // every row's limit, so its P is 0).
     //
     // Masked steps: a row whose limit lies at or below the tile start takes an
     // infinite exponent reference (P = 0); the element-wise mask runs only when
     // some row's limit falls inside the tile, at most a few tiles per block.
-    f32x16 scur[2];
-    bf16x8 pprev[2][2];
+    f32x16 scur[NB];
+    bf16x8 pprev[NB][2];
+    v4i16 vcur[NT][2][2];  // V^T fragments of the tile whose PV runs next
     auto step = [&](int t, auto S, auto masked, auto maxonly) {
         constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
         load_ptrs();  // segment pointers of tile t + 3
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        float mr[2] = {mref[0], mref[1]};
+        float mr[NB] = {mref[0]};
         if (MASK) {
             const int t0 = t * BN;
             bool part = false;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 part = part || (lim[b] > t0 && lim[b] < t0 + BN);
                 mr[b] = lim[b] <= t0 ? INFINITY : mref[b];
             }
@@ -803,42 +790,38 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
             }
         }
         bf16x8 kf[NS];
-        v4i16 vf[NT][2][2];
         read_k(std::integral_constant<int, (s0 + 1) % NSTG>{}, kf);
         __builtin_amdgcn_sched_barrier(0);  // the K reads go first
-        if (!MAXONLY) read_v(std::integral_constant<int, (s0 + NSTG - 1) % NSTG>{}, vf);
-        f32x16 snext[2];
-        qk(kf, snext);
+        f32x16 snext[NB];
         if (MAXONLY) {
+            qk(kf, snext);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+            for (int b = 0; b < NB; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+            issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
         } else {
-            bf16x8 pf[2][2];
+            bf16x8 pf[NB][2];
+            pv(vcur, pprev);
+            read_v(std::integral_constant<int, s0>{}, vcur);
             softmax(scur, pf, mr);
-            pv(vf, pprev);
+            qk(kf, snext);
+            issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) pprev[b][h] = pf[b][h];
         }
-        issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
-        if (!MAXONLY) {
-            // 32 MFMAs (QK of t+1, PV of t-1) carry the 128 softmax VALU of tile
-            // t and the 16 V fragment reads.
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            }
-        }
         scur[0] = snext[0];
-        scur[1] = snext[1];
     };
     auto sweep = [&](bool first_sweep, auto maxonly) {
         reset_cursor();
@@ -848,7 +831,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         issue(1, I1{});
         load_ptrs();
         issue(2, I2{});
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);  // tile 0 landed
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -860,12 +843,16 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
         if (first_sweep) {
             if (0 >= nfull) apply_mask(scur, 0);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) mref[b] = rowmax(scur[b]) * c;
+            for (int b = 0; b < NB; ++b) mref[b] = rowmax(scur[b]) * c;
         }
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int h = 0; h < 2; ++h) pprev[b][h] = bf16x8{};
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) vcur[tt][ss][0] = vcur[tt][ss][1] = v4i16{0, 0, 0, 0};
         // Groups of five steps (static stages): unmasked while the whole group
         // is visible to every row, masked from there on, up to the step after
         // the last tile (which only adds the last PV).
@@ -896,24 +883,24 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     };
 
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
     sweep(true, std::false_type{});
 
     // Rare second pass for rows whose sum left the safe range.
     const float kSafeSum = 18446744073709551616.f;  // 2^64
-    bool redo[2];
+    bool redo[NB];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
-    if (__builtin_amdgcn_ballot_w64(redo[0] || redo[1]) && lane == 0) sRedo = 1;
+    for (int b = 0; b < NB; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
+    if (__builtin_amdgcn_ballot_w64(redo[0]) && lane == 0) sRedo = 1;
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(sRedo)) {
         asm volatile("");
         sweep(false, std::true_type{});  // exact row maxima
         __syncthreads();
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             if (redo[b]) mref[b] = mmax[b] * c;
             l[b] = 0.f;
 #pragma unroll
@@ -923,7 +910,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128(const KArgs a) {
     }
 
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const float lt = pair_sum(l[b]);
         const float inv = 1.f / lt;
         if (!qv[b]) continue;
@@ -1747,9 +1734,9 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;
         if (k.nprog == 0) {
             if (fast)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(256), 0, stream, k);
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(512), 0, stream, k);
             else
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(256), 0, stream, k);
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(512), 0, stream, k);
         } else {
             if (fast)
                 hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(256), 0, stream, k);
