@@ -9,23 +9,21 @@
 // so the mask is a per-row key limit, and whole key tiles beyond a
 // workgroup's largest limit are never loaded.
 //
-// bf16 kernel (the hot path): one workgroup = 4 waves x 32 query rows of one
-// head.  Per 64-key tile, K and V are staged through LDS from coalesced 16-byte
-// global loads (prefetched into registers one tile ahead), then per wave:
-//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, K from LDS (A), Q^T held in
-//                    registers for the whole kernel (B), fp32 accumulate;
-//   online softmax   each lane owns one query column and 16 of every 32 keys,
-//                    so the row max needs one cross-lane step (lane ^ 32);
-//                    exp2 with scale*log2(e) folded into one FMA; P -> bf16 RNE;
-//   O^T += V^T P^T   P^T comes straight out of the S^T accumulator registers
-//                    (no shuffles) because V^T is written to LDS with its keys
-//                    permuted inside each 16-key group to match the MFMA
-//                    accumulator row order.
-// The O^T accumulator puts one query per lane, so the softmax rescale is one
-// scalar per lane.
-//
-// fp32 kernel: a plain VALU path for float32 inputs (one query row per
-// thread), used where float32 accuracy is required; not tuned.
+// Kernels:
+//   attn_fwd_bf16_d128        bf16, head_dim 128 (the hot path): 8 waves x 32
+//                             query rows, K/V tiles staged into an LDS ring by
+//                             global-to-LDS DMA, PV one tile behind the softmax;
+//   attn_fwd_bf16_d128_split  the same work cut into pieces spread over idle
+//                             workgroups (caller workspace), plus
+//   attn_combine_d128         the fixed-order merge of the pieces;
+//   attn_fwd_bf16             bf16, head_dim 64: 4 waves x 32 query rows, 64-key
+//                             tiles staged through registers, V^T written to
+//                             LDS with the MFMA accumulator's key order;
+//   attn_fwd_f32              float32 inputs: one query row per thread, plain
+//                             VALU, used where float32 accuracy is required.
+// Every bf16 kernel computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q^T in
+// registers for the whole kernel), the softmax in fp32 with exp2 and the scale
+// folded into one FMA, P rounded to bf16 (RNE), and O^T += V^T P^T.
 
 #include <algorithm>
 #include <atomic>
