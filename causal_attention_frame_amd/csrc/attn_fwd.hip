@@ -27,6 +27,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 #include <climits>
 #include <cmath>
@@ -65,14 +66,15 @@ struct KArgs {
     int32_t out_f32;
     // Split launch of the head_dim-128 kernel (nprog > 0): workspace of
     // partial-result slots, workgroups in the grid, units (heads x query
-    // blocks), the common cut of the mains, spare workgroups and the tail tiles
-    // they share.
+    // blocks), the common cut of the mains, spare workgroups, tail pieces in
+    // all and tiles per tail piece.
     float *ws;
     int32_t nprog;
     int32_t units;
     int32_t cut;
     int32_t nspare;
     int32_t tail_total;
+    int32_t piece;
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
@@ -941,20 +943,17 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
 // Plain launch (attn_fwd_bf16_d128 above): one workgroup per unit.
 //
 // Split launch (attn_fwd_bf16_d128_split below, with a workspace), for U units
-// on G > U workgroups: the same tile pipeline run on pieces of units.  It is a
-// kernel of its own so that the plain kernel's instruction schedule, which is
-// sensitive to any change of the surrounding code, stays as tuned.  Every unit
-// still has one
-// "main" workgroup, and the mains all walk the keys from tile 0 in step, so the
-// query blocks of one head share each K/V tile through L2; but a main stops at
-// a common cut T.  The tails [T, n) of the longer units are laid end to end and
-// shared evenly over the G - U spare workgroups; T is the smallest cut for
-// which a spare's share of the tails is at most T tiles.  Pieces that are not
-// whole units leave unnormalised partial results in the workspace: the main of
-// unit u in slot u, the tail piece holding the start of u's tail in slot U + u,
-// and a spare's first piece, when it continues a tail begun by the spare
-// before it, in slot 2U + s.  The combine kernel then merges the pieces of each
-// split unit in that fixed order.
+// on G > U workgroups: every unit keeps one "main" workgroup, and the mains
+// all walk the keys from tile 0 in step, so the query blocks of one head share
+// each K/V tile through L2; but a main stops at a common cut T.  The tail [T,
+// n) of a longer unit is cut into pieces of P tiles (unit-major order, piece k
+// of K), and the S = G - U spare workgroups share them evenly by count (spare
+// s: pieces [s K / S, (s + 1) K / S)) while the mains run.  T and P come from
+// the host, which simulates this schedule for the problem's unit lengths and
+// picks the shortest.  Pieces that are not whole units leave
+// unnormalised partial results in the workspace: the main of unit u in slot u,
+// tail piece k in slot U + k; the combine kernel merges each split unit's
+// pieces in that fixed order.
 constexpr int kD128BM = 256, kD128BN = 32;
 constexpr int kMaxSplitUnits = 256;                       // units of a split launch
 constexpr int kSlotFloats = kD128BM * 128 + 2 * kD128BM;  // partial O, reference, sum
@@ -964,40 +963,35 @@ __device__ inline int block_tiles(int qb, const KArgs &a) {
     return (key_limit(last, a) + kD128BN - 1) / kD128BN;
 }
 
-// sTail[u] = tail tiles of units 0 .. u-1 (u = 0 .. U), built by the 256
-// threads of the workgroup, one unit each.
-__device__ __forceinline__ void build_tail_prefix(const KArgs &a, int *sTail, int *sTmp) {
+// Tail pieces of unit u.
+__device__ inline int unit_pieces(int u, const KArgs &a) {
+    const int r = block_tiles(u % a.nqb, a) - a.cut;
+    return r > 0 ? (r + a.piece - 1) / a.piece : 0;
+}
+
+// sPre[u] = tail pieces of units 0 .. u-1 (u = 0 .. U), built by the first 256
+// threads of the workgroup, one unit each; every thread takes the barriers.
+__device__ __forceinline__ void build_piece_prefix(const KArgs &a, int *sPre, int *sTmp) {
     const int tid = threadIdx.x;
-    sTmp[tid] = tid < a.units ? max(0, block_tiles(tid % a.nqb, a) - a.cut) : 0;
+    if (tid < 256) sTmp[tid] = tid < a.units ? unit_pieces(tid, a) : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
-        const int v = tid >= off ? sTmp[tid - off] : 0;
+        const int v = (tid < 256 && tid >= off) ? sTmp[tid - off] : 0;
         __syncthreads();
-        sTmp[tid] += v;
+        if (tid < 256) sTmp[tid] += v;
         __syncthreads();
     }
-    sTail[tid + 1] = sTmp[tid];
-    if (tid == 0) sTail[0] = 0;
+    if (tid < 256) sPre[tid + 1] = sTmp[tid];
+    if (tid == 0) sPre[0] = 0;
     __syncthreads();
 }
 
-// First tail position of spare s, and the spare holding tail position x.
-__device__ inline int spare_start(int s, const KArgs &a) {
-    return (int)(((long)s * a.tail_total) / a.nspare);
-}
-__device__ inline int spare_of(int x, const KArgs &a) {
-    int s = (int)(((long)x * a.nspare) / a.tail_total);
-    while (s + 1 < a.nspare && spare_start(s + 1, a) <= x) ++s;
-    while (s > 0 && spare_start(s, a) > x) --s;
-    return s;
-}
-
-// Largest u with sTail[u] <= x among units with a tail (sTail non-decreasing).
-__device__ inline int find_tail_unit(const int *sTail, int U, int x) {
-    int lo = 0, hi = U;  // sTail[lo] <= x < sTail[hi]
+// Largest u with sPre[u] <= x (sPre non-decreasing).
+__device__ inline int find_tail_unit(const int *sPre, int U, int x) {
+    int lo = 0, hi = U;  // sPre[lo] <= x < sPre[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (sTail[mid] <= x) lo = mid;
+        if (sPre[mid] <= x) lo = mid;
         else hi = mid;
     }
     return lo;
@@ -1021,24 +1015,30 @@ __device__ inline void split_role(int b, const KArgs &a, int &unit, int &spare) 
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
-    constexpr int D = 128, BM = kD128BM, BN = kD128BN, NS = D / 16, NT = D / 32;
-    constexpr int TILE = BN * D, STAGE = 2 * TILE;  // elements
+__global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
+    constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
+    constexpr int NB = 1;  // 32-row query blocks per wave (8 waves)
+    constexpr int TILE = BN * D;  // elements of one K or V tile
+    constexpr int NSTG = 5;       // LDS ring depth
     constexpr bool FAST = MODE == kDmaFast;
-    // Tile t of a piece lives in stage (t - first tile) mod 4: K at STAGE *
-    // stage, V right after it.
-    __shared__ __attribute__((aligned(16))) uint16_t sKV[4 * STAGE];
+    // Tile t of a piece starting at tile tb lives in stage ((t - tb) mod 5): K
+    // tiles in one region and V tiles in another, so every fragment read is a
+    // per-lane base plus an immediate offset below 64 KB.
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[NSTG * TILE];
     __shared__ const uint16_t *sSegK[FAST ? 1 : kMaxKeyFrames];
     __shared__ const uint16_t *sSegV[FAST ? 1 : kMaxKeyFrames];
-    __shared__ int sTail[kMaxSplitUnits + 1];
-    __shared__ int sTmp[256];
     __shared__ int sRedo;
-    lds_u16 *const sbase = (lds_u16 *)sKV;
+    __shared__ int sPre[kMaxSplitUnits + 1];
+    __shared__ int sTmp[256];
+    lds_u16 *const kbase = (lds_u16 *)sK;
+    lds_u16 *const vbase = (lds_u16 *)sV;
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1046,34 +1046,36 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
     const int n = lane & 31, g = lane >> 5;
 
     if (!FAST) {
-        for (int f = tid; f < a.nseg; f += 256) {
+        for (int f = tid; f < a.nseg; f += 512) {
             sSegK[f] = (const uint16_t *)a.kseg[f];
             sSegV[f] = (const uint16_t *)a.vseg[f];
         }
     }
+    build_piece_prefix(a, sPre, sTmp);  // ends with a barrier
 
-    // DMA: in group i (i = 0, 1) this wave fills tile rows 8 wave + 4 i + lr,
-    // lane (lr, pch) the physical 16-byte chunk pch, fetching the logical chunk
-    // that the swizzle puts there.
+    // Per-piece state.
+    long hoff = 0;
+    int qi[NB], lim[NB];
+    bool qv[NB];
+    bf16x8 qf[NB][NS];
+    int nfull = 0, ntiles = 0;
+
+    // DMA: this wave fills tile rows 4 wave + lr of K and of V, lane (lr, pch)
+    // the physical 16-byte chunk pch, fetching the logical chunk that the
+    // swizzle puts there.
     const int lr = lane >> 4, pch = lane & 15;
-    int kch[2], vch[2];
-    uint32_t kvo[2], vvo[2];  // per-lane byte offsets from the group's first row
+    int kch[1], vch[1];
+    uint32_t kvo[1], vvo[1];  // per-lane byte offsets from the group's first row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        kch[i] = pch ^ (4 * i + lr);                    // (row mod 8) = 4 i + lr
+    for (int i = 0; i < 1; ++i) {
+        kch[i] = pch ^ (4 * (wave & 3) + lr);           // (row mod 16) = 4 (wave mod 4) + lr
         vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
         kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
-    const uint32_t lds0 = lds_addr(sbase);
-    auto m0k = [&](int S, int i) __attribute__((always_inline)) { return lds0 + (uint32_t)((S * STAGE + (8 * wave + 4 * i) * D) * 2); };
-
-    // Per-piece state.
-    long hoff = 0;
-    int qi[2], lim[2];
-    bool qv[2];
-    bf16x8 qf[2][NS];
-    int nfull = 0;
+    const uint32_t k_lds = lds_addr(kbase), v_lds = lds_addr(vbase);
+    auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
+    auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
 
     // Key cursor of the next tile to prefetch (tiles are prefetched in order
     // within a sweep): segment cf and key offset co inside it, wave-uniform.
@@ -1082,27 +1084,22 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
     int cf = 0, co = 0;
     SegPtrs sp{};
     auto reset_cursor = [&](int tile) __attribute__((always_inline)) {
-        if constexpr (FAST) {
-            const int j0 = tile * BN;
-            cf = __builtin_amdgcn_readfirstlane(seg_of(j0, a));
-            co = j0 - cf * a.seg_len;
-        }
+        const int j = tile * BN;
+        cf = min(j / a.seg_len, a.nseg - 1);
+        co = j - cf * a.seg_len;
     };
-    auto load_ptrs = [&]() __attribute__((always_inline)) {
+    auto load_ptrs = [&]() {
         if constexpr (FAST) sp = load_seg_ptrs(cf);
     };
-    auto issue = [&](int tile, auto S) __attribute__((always_inline)) {
-        constexpr int st = decltype(S)::value & 3;
+    auto issue = [&](int tile, auto S) {
+        constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int row = co + 8 * wave + 4 * i;
-                const bool nxt = row >= a.seg_len;
-                const long rr = nxt ? row - a.seg_len : row;
-                const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-                dma16_sbase((nxt ? sp.k1 : sp.k0) + off, kvo[i], m0k(st, i));
-                dma16_sbase((nxt ? sp.v1 : sp.v0) + off, vvo[i], m0k(st, i) + TILE * 2);
-            }
+            const int row = co + 4 * wave;
+            const bool nxt = row >= a.seg_len;
+            const long rr = nxt ? row - a.seg_len : row;
+            const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
+            dma16x2_sbase((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
+                          m0v(st, 0));
             co += BN;
             if (co >= a.seg_len) {
                 co -= a.seg_len;
@@ -1111,8 +1108,8 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
         } else {
             const int j0 = tile * BN;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int j = j0 + 8 * wave + 4 * i + lr;
+            for (int i = 0; i < 1; ++i) {
+                const int j = j0 + 4 * wave + 4 * i + lr;
                 const uint16_t *kp = kZeroRow + kch[i] * 8;
                 const uint16_t *vp = kZeroRow + vch[i] * 8;
                 if (j < a.Tk) {
@@ -1122,136 +1119,135 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
                     vp = sSegV[f] + o + vch[i] * 8;
                 }
                 dma16_vaddr(kp, m0k(st, i));
-                dma16_vaddr(vp, m0k(st, i) + TILE * 2);
+                dma16_vaddr(vp, m0v(st, i));
             }
         }
     };
 
     // Per-lane LDS pointers of the fragment reads in stage 0; the stage, the
     // upper half of d and the key steps are immediate offsets.
-    const lds_u16 *kfp[4];
+    const lds_u16 *kfp[NS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kfp[s] = sbase + n * D + (((2 * s + g) ^ (n & 7)) << 3);
+    for (int s = 0; s < NS; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 15)) << 3);
     const int G = lane >> 4, sl = lane & 15;
     const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
     const lds_u16 *vfp[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-        vfp[t] = sbase + TILE + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+        vfp[t] = vbase + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
 
     // Softmax with a fixed per-row exponent reference (log2 units): P =
-    // exp2(s * c - mref).  mref is the row max of the row's first key tile (of
-    // the piece), so P <= 1 there; later tiles may exceed it, which is harmless
-    // while the running sum stays far from the fp32 range.  A row whose sum
-    // ends above 2^64 (or overflows) is recomputed in a second pass with its
-    // exact row max as reference.  The accumulators are therefore touched only
-    // by MFMAs inside the key loop.  Each row's result depends on its own
-    // scores only.  The row sum adds the bf16-rounded P that the PV product uses.
-    f32x16 acc[2][NT];
-    float mref[2] = {0.f, 0.f}, l[2] = {0.f, 0.f}, mmax[2] = {-INFINITY, -INFINITY};
+    // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
+    // P <= 1 there; later tiles may exceed it, which is harmless while the
+    // running sum stays far from the fp32 range.  A row whose sum ends above
+    // 2^64 (or overflows) is recomputed in a second pass with its exact row max
+    // as reference.  The accumulators are therefore touched only by MFMAs inside
+    // the key loop.  Each row's result depends on its own scores only.  The row
+    // sum adds the bf16-rounded P that the PV product uses.
+    f32x16 acc[NB][NT];
+    float mref[NB] = {0.f}, l[NB] = {0.f}, mmax[NB] = {-INFINITY};
     const float c = a.c;
 
     // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
     // transposed 8-byte reads each).
-    // The K reads are issued in the order the QK MFMA chain consumes them
-    // (the fences keep the scheduler from regrouping them by base register,
-    // which would make the first MFMAs wait for nearly all eight).
-    auto read_k = [&](auto S, bf16x8 *kf) __attribute__((always_inline)) {
-        constexpr int st = decltype(S)::value & 3;
+    auto read_k = [&](auto S, bf16x8 *kf) {
+        constexpr int st = decltype(S)::value;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s & 3] + st * STAGE + (s >> 2) * 64));
-            compiler_fence();
-        }
+        for (int s = 0; s < NS; ++s)
+            kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s] + st * TILE));
     };
-    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) __attribute__((always_inline)) {
-        constexpr int st = decltype(S)::value & 3;
+    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
+        constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s) * D);
-                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * STAGE + (t >> 1) * 64 + (16 * s + 8) * D);
+                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s + 8) * D);
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
-    auto qk = [&](const bf16x8 *kf, f32x16 *s) __attribute__((always_inline)) {
+    auto qk = [&](const bf16x8 *kf, f32x16 *s) {
         s[0] = f32x16{};
-        s[1] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[1][st], s[1], 0, 0, 0);
-        }
+        for (int st = 0; st < NS; ++st) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
     };
-    auto apply_mask = [&](f32x16 *s, int tile) __attribute__((always_inline)) {
+    auto apply_mask = [&](f32x16 *s, int tile) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (tile * BN + 8 * (r >> 2) + 4 * g + (r & 3) >= lim[b]) s[b][r] = -INFINITY;
     };
-    auto rowmax = [&](const f32x16 &s) __attribute__((always_inline)) {
+    auto rowmax = [&](const f32x16 &s) {
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         return pair_max(mx);
     };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    // P for keys 8 h .. 8 h + 7 of the lane's 16 (block b), and its row sum.
-    auto softmax_part = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr, int b, int h)
-                            __attribute__((always_inline)) {
+    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            pf[b][h][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b][8 * h + j], c, -mr[b]));
-        const bf16x8 &p8 = pf[b][h];
-        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), ones, l[b], false);
-        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, l[b], false);
-        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, l[b], false);
-        l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, l[b], false);
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pf[b][h][j] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[b][8 * h + j], c, -mr[b]));
+                const bf16x8 &p8 = pf[b][h];
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 0, 1), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 2, 3), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 4, 5), ones, l[b], false);
+                l[b] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p8, p8, 6, 7), ones, l[b], false);
+            }
     };
-    // O^T += V^T P^T for block b.
-    auto pv_block = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2], int b) __attribute__((always_inline)) {
+    // O^T += V^T P^T.
+    auto pv = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2]) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)  // consecutive MFMAs write different accumulators
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
+            for (int st = 0; st < 2; ++st) {
                 const bf16x8 v = __builtin_bit_cast(
                     bf16x8, (v8i16)__builtin_shufflevector(vf[t][st][0], vf[t][st][1], 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[b][st], acc[b][t], 0, 0, 0);
+                acc[0][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, pf[0][st], acc[0][t], 0, 0, 0);
             }
     };
 
-    // Software pipeline over key tiles.  Step t (stage t mod 4 relative to the
-    // piece's first tile): wait until this wave's DMA of tile t+1 has landed
-    // (tile t+2 may still be in flight), barrier (every wave's DMA of t+1 has
-    // landed; every wave is done with tile t-1, whose stage takes tile t+3),
-    // then in one basic block: S(t+1) on the matrix cores while the VALU turns
-    // S(t) into P, followed by O += V(t) P and the prefetch of tile t+3.  The
-    // loop leaves after the piece's last tile (its S(t+1) is never used); the
-    // look-ahead tiles past it read valid rows (the key cursor wraps inside the
-    // last segment) and are drained before the stages are reused.
+    // Software pipeline over key tiles, PV one tile behind the softmax.  Step
+    // t (stage s(t) = t mod 5): wait until this wave's DMA of tile t+1 has
+    // landed (t+2 may still be in flight), barrier (every wave's DMA of t+1 has
+    // landed; every wave is done with step t-1, so the stage of tile t-2 is
+    // free), then in one basic block: the K(t+1) fragment reads; O += V(t-1)
+    // P(t-1) from registers, each MFMA followed by the transposed reads of the
+    // V(t) fragments that take over its A operand's registers (they feed the
+    // PV of step t+1); then S(t+1) = K(t+1) Q^T; the VALU turns S(t) into P(t)
+    // under both; last the prefetch of tile t+3 into the stage of tile t-2.
+    // The step after the last tile only adds the last PV (its tile is past
+    // every row's limit, so its P is 0).
     //
     // Masked steps: a row whose limit lies at or below the tile start takes an
     // infinite exponent reference (P = 0); the element-wise mask runs only when
     // some row's limit falls inside the tile, at most a few tiles per block.
-    f32x16 scur[2];
-    auto step = [&](int t, auto S, auto masked, auto maxonly) __attribute__((always_inline)) {
+    f32x16 scur[NB];
+    bf16x8 pprev[NB][2];
+    v4i16 vcur[NT][2][2];  // V^T fragments of the tile whose PV runs next
+    auto step = [&](int t, auto S, auto masked, auto maxonly) {
+        constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
         load_ptrs();  // segment pointers of tile t + 3
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile t+2 may stay in flight
+        __builtin_amdgcn_s_waitcnt(kWaitVm2);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
-        float mr[2] = {mref[0], mref[1]};
+        float mr[NB] = {mref[0]};
         if (MASK) {
             const int t0 = t * BN;
             bool part = false;
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 part = part || (lim[b] > t0 && lim[b] < t0 + BN);
                 mr[b] = lim[b] <= t0 ? INFINITY : mref[b];
             }
@@ -1260,60 +1256,41 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
                 apply_mask(scur, t);
             }
         }
-        // All fragment reads first (K of tile t+1, V of tile t), so their LDS
-        // latency hides behind the MFMAs and VALU work that follows.
         bf16x8 kf[NS];
-        v4i16 vf[NT][2][2];
-        read_k(std::integral_constant<int, (decltype(S)::value + 1) & 3>{}, kf);
+        read_k(std::integral_constant<int, (s0 + 1) % NSTG>{}, kf);
         __builtin_amdgcn_sched_barrier(0);  // the K reads go first
-        f32x16 snext[2];
+        f32x16 snext[NB];
         if (MAXONLY) {
             qk(kf, snext);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+            for (int b = 0; b < NB; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
+            issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
         } else {
-            // Three scheduling regions, so that no PV MFMA waits in the QK
-            // stream for a V fragment read just before it:
-            //   QK(t+1) MFMAs | V reads, softmax of block 0 and half of block 1;
-            //   PV(t) of block 0 | the other half of block 1's softmax;
-            //   PV(t) of block 1 | the prefetch.
-            bf16x8 pf[2][2];
-            read_v(S, vf);
+            bf16x8 pf[NB][2];
+            pv(vcur, pprev);
+            read_v(std::integral_constant<int, s0>{}, vcur);
+            softmax(scur, pf, mr);
             qk(kf, snext);
-            softmax_part(scur, pf, mr, 0, 0);
-            softmax_part(scur, pf, mr, 0, 1);
-            softmax_part(scur, pf, mr, 1, 0);
+            issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 0; k < 8; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
             }
-            pin(snext[0]);
-            pin(snext[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            pv_block(vf, pf, 0);
-            softmax_part(scur, pf, mr, 1, 1);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
 #pragma unroll
-            for (int t = 0; t < NT; ++t) pin(acc[0][t]);
-            __builtin_amdgcn_sched_barrier(0);
-            pv_block(vf, pf, 1);
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) pin(acc[1][t]);
+                for (int h = 0; h < 2; ++h) pprev[b][h] = pf[b][h];
         }
-        // Prefetch tile t+3 into the stage of tile t-1 (every wave finished
-        // with it before this step's barrier), while the PV MFMAs drain.
-        issue(t + 3, std::integral_constant<int, (decltype(S)::value + 3) & 3>{});
         scur[0] = snext[0];
-        scur[1] = snext[1];
     };
-    // One pass over the tiles [tb, te) of the current piece.
-    auto sweep = [&](bool first_sweep, int tb, int te, auto maxonly) __attribute__((always_inline)) {
+    auto sweep = [&](bool first_sweep, int tb, auto maxonly) __attribute__((always_inline)) {
         reset_cursor(tb);
         load_ptrs();
         issue(tb, I0{});
@@ -1321,10 +1298,7 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
         issue(tb + 1, I1{});
         load_ptrs();
         issue(tb + 2, I2{});
-        // Tile tb landed, and so did every older vector-memory operation (the
-        // previous piece's stores may still be in flight, and stores and loads
-        // need not complete in order).
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -1336,30 +1310,42 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
         if (first_sweep) {
             if (tb >= nfull) apply_mask(scur, tb);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int b = 0; b < NB; ++b) {
                 const float m = rowmax(scur[b]);
                 mref[b] = m == -INFINITY ? 0.f : m * c;  // no key of the piece: P = 0 throughout
             }
         }
-        // Groups of four steps (static stages): unmasked while the whole group
-        // is visible to every row, masked from there on.
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pprev[b][h] = bf16x8{};
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int ss = 0; ss < 2; ++ss) vcur[tt][ss][0] = vcur[tt][ss][1] = v4i16{0, 0, 0, 0};
+        // Groups of five steps (static stages): unmasked while the whole group
+        // is visible to every row, masked from there on, up to the step after
+        // the last tile (which only adds the last PV).
         int base = tb;
 #pragma unroll 1
-        for (; base + 4 <= nfull; base += 4) {
+        for (; base + 5 <= nfull; base += 5) {
             step(base, I0{}, std::false_type{}, maxonly);
             step(base + 1, I1{}, std::false_type{}, maxonly);
             step(base + 2, I2{}, std::false_type{}, maxonly);
             step(base + 3, I3{}, std::false_type{}, maxonly);
+            step(base + 4, I4{}, std::false_type{}, maxonly);
         }
 #pragma unroll 1
-        for (; base < te; base += 4) {
+        for (; base <= ntiles; base += 5) {
             step(base, I0{}, std::true_type{}, maxonly);
-            if (base + 1 >= te) break;
+            if (base + 1 > ntiles) break;
             step(base + 1, I1{}, std::true_type{}, maxonly);
-            if (base + 2 >= te) break;
+            if (base + 2 > ntiles) break;
             step(base + 2, I2{}, std::true_type{}, maxonly);
-            if (base + 3 >= te) break;
+            if (base + 3 > ntiles) break;
             step(base + 3, I3{}, std::true_type{}, maxonly);
+            if (base + 4 > ntiles) break;
+            step(base + 4, I4{}, std::true_type{}, maxonly);
         }
         // drain the look-ahead tiles before the stages are reused
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -1367,23 +1353,24 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
     };
 
     // Tiles [tb, te) of unit (head, qb).  slot < 0: the whole unit, write O
-    // (and LSE); else write the partial result to workspace slot `slot`.
+    // (and LSE); else write the partial result (unnormalised O, reference,
+    // sum) to workspace slot `slot`.
     auto do_piece = [&](int head, int qb, int tb, int te, int slot) __attribute__((always_inline)) {
         const int q0 = qb * BM;
         hoff = (long)head * D;
         const int lim_end = te * BN;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            qi[b] = q0 + 64 * wave + 32 * b + n;
+        for (int b = 0; b < NB; ++b) {
+            qi[b] = q0 + 32 * NB * wave + 32 * b + n;
             qv[b] = qi[b] < a.Tq;
             lim[b] = min(key_limit(qv[b] ? qi[b] : a.Tq - 1, a), lim_end);
         }
+        ntiles = te;
         nfull = min(te, min(key_limit(q0, a), lim_end) / BN);  // tiles visible to every row
         if (tid == 0) sRedo = 0;
-
-        // Q^T B operands of both blocks: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
+        // Q^T B operands: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             const uint16_t *qrow = (const uint16_t *)a.q + (long)(qv[b] ? qi[b] : a.Tq - 1) * a.ld + hoff;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -1392,45 +1379,48 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
             }
         }
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < NB; ++b) {
             l[b] = 0.f;
             mmax[b] = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
         }
-        sweep(true, tb, te, std::false_type{});
+        __syncthreads();
+    #pragma unroll
+        for (int b = 0; b < NB; ++b)
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
+        sweep(true, tb, std::false_type{});
 
         // Rare second pass for rows whose sum left the safe range.
         const float kSafeSum = 18446744073709551616.f;  // 2^64
-        bool redo[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
-        if (__builtin_amdgcn_ballot_w64(redo[0] || redo[1]) && lane == 0) sRedo = 1;
+        bool redo[NB];
+    #pragma unroll
+        for (int b = 0; b < NB; ++b) redo[b] = qv[b] && !(pair_sum(l[b]) <= kSafeSum);
+        if (__builtin_amdgcn_ballot_w64(redo[0]) && lane == 0) sRedo = 1;
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(sRedo)) {
             asm volatile("");
-            sweep(false, tb, te, std::true_type{});  // exact row maxima
+            sweep(false, tb, std::true_type{});  // exact row maxima
             __syncthreads();
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
+    #pragma unroll
+            for (int b = 0; b < NB; ++b) {
                 if (redo[b]) mref[b] = mmax[b] * c;
                 l[b] = 0.f;
-#pragma unroll
+    #pragma unroll
                 for (int t = 0; t < NT; ++t) acc[b][t] = f32x16{};
             }
-            sweep(false, tb, te, std::false_type{});
+            sweep(false, tb, std::false_type{});
         }
 
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
+    #pragma unroll
+        for (int b = 0; b < NB; ++b) {
             const float lt = pair_sum(l[b]);
             if (!qv[b]) continue;
             if (slot >= 0) {
-                const int row = 64 * wave + 32 * b + n;
+                const int row = 32 * NB * wave + 32 * b + n;
                 float *ps = a.ws + (long)slot * kSlotFloats;
-#pragma unroll
+    #pragma unroll
                 for (int t = 0; t < NT; ++t)
-#pragma unroll
+    #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         *(f32x4 *)(ps + row * D + 32 * t + 8 * i + 4 * g) =
                             f32x4{acc[b][t][4 * i], acc[b][t][4 * i + 1], acc[b][t][4 * i + 2], acc[b][t][4 * i + 3]};
@@ -1442,9 +1432,9 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
             }
             const float inv = 1.f / lt;
             const long obase = (long)qi[b] * a.ld + hoff;
-#pragma unroll
+    #pragma unroll
             for (int t = 0; t < NT; ++t)
-#pragma unroll
+    #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int dcol = 32 * t + 8 * i + 4 * g;
                     const float o0 = acc[b][t][4 * i + 0] * inv, o1 = acc[b][t][4 * i + 1] * inv;
@@ -1461,115 +1451,90 @@ __global__ __launch_bounds__(256) void attn_fwd_bf16_d128_split(const KArgs a) {
                 }
             if (g == 0 && a.lse) a.lse[(long)head * a.Tq + qi[b]] = mref[b] / kLog2e + logf(lt);
         }
-        // Every wave is done with the stages and sRedo; the stores above may
-        // stay in flight (the next piece waits for them before its first read).
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        compiler_fence();
-        __builtin_amdgcn_s_barrier();
-        compiler_fence();
+        // Every wave is done with the stages and sRedo before the next piece.
+        __syncthreads();
+
     };
 
+    // Pieces of this workgroup: a main runs [0, min(n, T)) of its unit, a
+    // spare its share of the tail pieces.
     int unit, spare;
     split_role(blockIdx.x, a, unit, spare);
-    if (unit >= 0) {  // main: tiles [0, min(n, T)) of its unit
+    auto run_tail = [&](int k) __attribute__((always_inline)) {
+        const int u = __builtin_amdgcn_readfirstlane(find_tail_unit(sPre, a.units, k));
+        const int i = k - __builtin_amdgcn_readfirstlane(sPre[u]);
+        const int head = u / a.nqb, qb = u - head * a.nqb;
+        const int tb = a.cut + i * a.piece;
+        const int te = min(block_tiles(qb, a), tb + a.piece);
+        do_piece(head, qb, tb, te, a.units + k);
+    };
+    if (unit >= 0) {
         const int head = unit / a.nqb, qb = unit - head * a.nqb;
-        const int n = block_tiles(qb, a);
-        __syncthreads();
-        do_piece(head, qb, 0, min(n, a.cut), n > a.cut ? unit : -1);
+        const int nt = block_tiles(qb, a);
+        do_piece(head, qb, 0, min(nt, a.cut), nt > a.cut ? unit : -1);
         return;
     }
-    // spare: tail positions [spare_start(s), spare_start(s + 1))
-    build_tail_prefix(a, sTail, sTmp);
-    const int p1 = spare_start(spare + 1, a);
-    int p = spare_start(spare, a);
+    const int k0 = (int)((long)spare * a.tail_total / a.nspare);
+    const int k1 = (int)((long)(spare + 1) * a.tail_total / a.nspare);
 #pragma unroll 1
-    while (p < p1) {
-        const int u = __builtin_amdgcn_readfirstlane(find_tail_unit(sTail, a.units, p));
-        const int t0 = __builtin_amdgcn_readfirstlane(sTail[u]);
-        const int tn = __builtin_amdgcn_readfirstlane(sTail[u + 1]) - t0;
-        const int off = p - t0, end = min(tn, p1 - t0);
-        if (off < 0 || end <= off) break;  // cannot happen with a consistent prefix table
-        const int head = u / a.nqb, qb = u - head * a.nqb;
-        const int slot = off == 0 ? a.units + u : 2 * a.units + spare;
-        do_piece(head, qb, a.cut + off, a.cut + end, slot);
-        p = t0 + end;
-    }
+    for (int k = k0; k < k1; ++k) run_tail(k);
 }
 
 // Merges the pieces of every split unit of a split launch: with piece s holding
 // acc_s (unnormalised O), reference m_s and sum l_s per row, M = max m_s over
 // the pieces that saw keys, L = sum 2^(m_s - M) l_s, O = sum 2^(m_s - M) acc_s / L
-// and LSE = M ln 2 + ln L.  Pieces are taken in a fixed order (main, tail
-// start, continuations), so the result does not depend on timing.  One
-// workgroup per unit; units that were not split return at once.
+// and LSE = M ln 2 + ln L.  Pieces are taken in a fixed order (main, then the
+// tail pieces in order), so the result does not depend on timing.  Eight
+// workgroups per unit, 32 rows each (thread: row tid / 8, 16 columns); units
+// that were not split return at once.
+constexpr int kCombineParts = 8;
 __global__ __launch_bounds__(256) void attn_combine_d128(const KArgs a) {
-    constexpr int D = 128, BM = kD128BM, C4 = D / 4, ITEMS = BM * C4 / 256;
-    __shared__ int sTail[kMaxSplitUnits + 1];
-    __shared__ int sTmp[256];
-    __shared__ float sM[BM], sW[BM], sInv[BM];
+    constexpr int D = 128, BM = kD128BM, RP = BM / kCombineParts;  // rows per workgroup
     const int tid = threadIdx.x;
-    const int u = blockIdx.x;
+    const int u = blockIdx.x / kCombineParts, part = blockIdx.x % kCombineParts;
     const int head = u / a.nqb, qb = u - head * a.nqb;
-    if (block_tiles(qb, a) <= a.cut) return;
-    build_tail_prefix(a, sTail, sTmp);
-    const int t0 = sTail[u], tn = sTail[u + 1] - t0;
-    const int sa = spare_of(t0, a), sb = spare_of(t0 + tn - 1, a);
-    const int npieces = 2 + sb - sa;
-    auto slot_of = [&](int k) {
-        return k == 0 ? u : k == 1 ? a.units + u : 2 * a.units + sa + k - 1;
-    };
-
-    // Per row: largest reference among pieces that saw keys, and 1 / L.
-    {
-        float M = -INFINITY;
-        for (int k = 0; k < npieces; ++k) {
-            const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
-            if (ps[BM * D + BM + tid] > 0.f) M = fmaxf(M, ps[BM * D + tid]);
-        }
-        float L = 0.f;
-        for (int k = 0; k < npieces; ++k) {
-            const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
-            const float ls = ps[BM * D + BM + tid];
-            if (ls > 0.f) L += exp2f(ps[BM * D + tid] - M) * ls;
-        }
-        sM[tid] = M;
-        sInv[tid] = 1.f / L;
-        const int row = qb * BM + tid;
-        if (a.lse && row < a.Tq) a.lse[(long)head * a.Tq + row] = M / kLog2e + logf(L);
+    const int q = unit_pieces(u, a);
+    if (q == 0) return;
+    int k0 = 0;  // tail pieces of the units before u (pieces depend on the query block only)
+    for (int b = 0; b < a.nqb; ++b) {
+        const int qb_pieces = unit_pieces(b, a);
+        k0 += qb_pieces * head + (b < qb ? qb_pieces : 0);
     }
-    // Thread tid owns column chunk tid % 32 of rows tid / 32 + 8 k.
-    const int c4 = tid % C4, r0 = tid / C4;
-    f32x4 o[ITEMS];
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int npieces = 1 + q;
+    auto slot_of = [&](int k) { return k == 0 ? u : a.units + k0 + k - 1; };
+    const int row = part * RP + tid / 8, c0 = 16 * (tid % 8);
+    const int qrow = qb * BM + row;
+
+    float M = -INFINITY;
     for (int k = 0; k < npieces; ++k) {
         const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
-        __syncthreads();
-        const float ls = ps[BM * D + BM + tid];
-        sW[tid] = ls > 0.f ? exp2f(ps[BM * D + tid] - sM[tid]) : 0.f;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const int row = r0 + 8 * j;
-            const f32x4 v = *(const f32x4 *)(ps + row * D + 4 * c4);
-            o[j] += sW[row] * v;
-        }
+        if (ps[BM * D + BM + row] > 0.f) M = fmaxf(M, ps[BM * D + row]);
     }
+    float L = 0.f;
+    f32x4 o[4] = {};
+    for (int k = 0; k < npieces; ++k) {
+        const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
+        const float ls = ps[BM * D + BM + row];
+        const float w = ls > 0.f ? exp2f(ps[BM * D + row] - M) : 0.f;
+        L += w * ls;
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const int row = r0 + 8 * j;
-        const int qrow = qb * BM + row;
-        if (qrow >= a.Tq) continue;
-        const f32x4 v = o[j] * sInv[row];
-        const long off = (long)qrow * a.ld + (long)head * D + 4 * c4;
+        for (int i = 0; i < 4; ++i) o[i] += w * *(const f32x4 *)(ps + row * D + c0 + 4 * i);
+    }
+    if (qrow >= a.Tq) return;
+    const float inv = 1.f / L;
+    if (a.lse && tid % 8 == 0) a.lse[(long)head * a.Tq + qrow] = M / kLog2e + logf(L);
+    const long off = (long)qrow * a.ld + (long)head * D + c0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f32x4 v = o[i] * inv;
         if (a.out_f32) {
-            *(f32x4 *)((float *)a.o + off) = v;
+            *(f32x4 *)((float *)a.o + off + 4 * i) = v;
         } else {
             const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)v[0]);
             const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)v[1]);
             const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)v[2]);
             const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)v[3]);
-            *(u32x2 *)((uint16_t *)a.o + off) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
+            *(u32x2 *)((uint16_t *)a.o + off + 4 * i) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
         }
     }
 }
@@ -1661,9 +1626,93 @@ int64_t host_block_tiles(int64_t qb, const KArgs &k) {
     return (lim + kD128BN - 1) / kD128BN;
 }
 
-// Smallest share of key tiles a split range gets (fewer ranges than compute
-// units for small problems).
-constexpr int64_t kMinRangeTiles = 8;
+// Schedule of a split launch: the common cut T of the mains, tiles per tail
+// piece, tail pieces in all and first-phase pieces per spare.
+struct SplitPlan {
+    int32_t cut, piece, pieces;
+};
+
+// Costs of the split schedule in units of one key-tile step of a main,
+// measured on the Wan-1.3B step shape: a tail piece pays ~13 us beyond its
+// tiles (Q load, pipeline fill, look-ahead drain, partial write), spares run
+// their tiles ~1.35x slower than the mains (their K/V rows are rarely in L2),
+// and merging a partial result costs ~0.01 step.  A split is taken only if it
+// is predicted to be at least 10 % shorter than the plain launch.
+constexpr double kPieceOverheadTiles = 16.0;
+constexpr double kSpareTileCost = 1.35;
+constexpr double kMergeTilesPerSlot = 0.01;
+constexpr double kSplitMargin = 0.9;
+
+// Chooses T, P and m by simulating the split schedule (see the work
+// decomposition comment) on the problem's unit lengths; false when the split
+// would not beat the plain launch by a margin.  Plans are cached per shape.
+bool plan_split(const KArgs &k, int64_t H, int G, SplitPlan *out) {
+    struct Entry {
+        int64_t key[6];
+        bool ok;
+        SplitPlan plan;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> cache;
+    const int64_t key[6] = {k.Tq, k.Tk, k.kpf, k.prefix, H, G};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : cache)
+            if (std::equal(key, key + 6, e.key)) {
+                *out = e.plan;
+                return e.ok;
+            }
+    }
+    const int64_t nqb = k.nqb, U = nqb * H, S = G - U;
+    std::vector<int64_t> nq(nqb);
+    int64_t nmax = 0, total = 0;
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+        nq[qb] = host_block_tiles(qb, k);
+        nmax = std::max(nmax, nq[qb]);
+        total += nq[qb] * H;
+    }
+    const double ov = kPieceOverheadTiles;
+    double best = (double)nmax * kSplitMargin;  // the plain launch's makespan, less a margin
+    bool ok = false;
+    SplitPlan bp{};
+    std::vector<int32_t> len;
+    const int64_t tlo = std::max<int64_t>(1, (int64_t)(0.7 * (double)total / (double)G));
+    for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128}) {
+        for (int64_t T = tlo; T < nmax; ++T) {
+            len.clear();
+            int64_t split_units = 0;
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t qb = 0; qb < nqb; ++qb) {
+                    const int64_t r = nq[qb] - T;
+                    if (r > 0) ++split_units;
+                    for (int64_t o = 0; o < r; o += P) len.push_back((int32_t)std::min<int64_t>(P, r - o));
+                }
+            const int64_t K = (int64_t)len.size();
+            if (K == 0 || U + K > 2 * (int64_t)G) continue;
+            double mk = (double)std::min(nmax, T) + ov;  // the mains
+            for (int64_t s = 0; s < S; ++s) {             // the spares
+                double f = 0.0;
+                for (int64_t kk = s * K / S; kk < (s + 1) * K / S; ++kk) f += kSpareTileCost * len[kk] + ov;
+                mk = std::max(mk, f);
+            }
+            mk += kMergeTilesPerSlot * (double)(split_units + K);
+            if (mk < best) {
+                best = mk;
+                ok = true;
+                bp = SplitPlan{(int32_t)T, P, (int32_t)K};
+            }
+        }
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() >= 64) cache.erase(cache.begin());
+    Entry e;
+    std::copy(key, key + 6, e.key);
+    e.ok = ok;
+    e.plan = bp;
+    cache.push_back(e);
+    *out = bp;
+    return ok;
+}
 
 // Compute units of the current device, cached per device.
 hipError_t cu_count(int *out) {
@@ -1693,40 +1742,18 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         if (p.ws && U < kMaxSplitUnits) {
             int cu = 0;
             if (const hipError_t e = cu_count(&cu)) return e;
-            std::vector<int64_t> nq(k.nqb);
-            int64_t total = 0, nmax = 0;
-            for (int64_t qb = 0; qb < k.nqb; ++qb) {
-                nq[qb] = host_block_tiles(qb, k);
-                total += nq[qb] * p.H;
-                nmax = std::max(nmax, nq[qb]);
-            }
-            const int64_t G = std::min<int64_t>(std::min<int64_t>(cu, kMaxSplitUnits),
-                                                std::max<int64_t>(U + 1, total / kMinRangeTiles));
-            if (G > U) {
-                const int64_t S = G - U;
-                auto tails = [&](int64_t T) {
-                    int64_t t = 0;
-                    for (int64_t n : nq) t += std::max<int64_t>(0, n - T) * p.H;
-                    return t;
-                };
-                int64_t lo = 1, hi = nmax;  // smallest cut T with tails(T) <= S * T
-                while (lo < hi) {
-                    const int64_t mid = (lo + hi) / 2;
-                    if (tails(mid) <= S * mid) hi = mid;
-                    else lo = mid + 1;
-                }
-                const int64_t tt = tails(lo);
-                bool fit = true;  // every XCD has a workgroup for each of its mains
-                for (int64_t x = 0; x < 8; ++x)
-                    fit = fit && (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
-                if (tt > 0 && fit && tt < INT32_MAX) {
-                    k.ws = (float *)p.ws;
-                    k.nprog = (int32_t)G;
-                    k.units = (int32_t)U;
-                    k.cut = (int32_t)lo;
-                    k.nspare = (int32_t)S;
-                    k.tail_total = (int32_t)tt;
-                }
+            const int64_t G = std::min<int64_t>(cu, kMaxSplitUnits);
+            bool fit = G > U;  // every XCD has a workgroup for each of its mains
+            for (int64_t x = 0; fit && x < 8; ++x) fit = (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
+            SplitPlan plan{};
+            if (fit && plan_split(k, p.H, (int)G, &plan)) {
+                k.ws = (float *)p.ws;
+                k.nprog = (int32_t)G;
+                k.units = (int32_t)U;
+                k.cut = plan.cut;
+                k.nspare = (int32_t)(G - U);
+                k.tail_total = plan.pieces;
+                k.piece = plan.piece;
             }
         }
         const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;
@@ -1737,10 +1764,10 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
                 hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(512), 0, stream, k);
         } else {
             if (fast)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(256), 0, stream, k);
+                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(512), 0, stream, k);
             else
-                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaLane>), dim3(k.nprog), dim3(256), 0, stream, k);
-            hipLaunchKernelGGL(attn_combine_d128, dim3(k.units), dim3(256), 0, stream, k);
+                hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaLane>), dim3(k.nprog), dim3(512), 0, stream, k);
+            hipLaunchKernelGGL(attn_combine_d128, dim3(k.units * kCombineParts), dim3(256), 0, stream, k);
         }
     } else if (p.in_dtype == RTR_BF16) {
         k.nqb = (int)((p.Tq + 127) / 128);

@@ -379,6 +379,36 @@ def test_split_matches_plain_at_full_size():
     assert float((l1 - l2).abs().max()) < 1e-3   # row sums of bf16-rounded weights
 
 
+def test_split_runs_and_matches_plain_one_frame_chunk():
+    # A one-frame chunk on the Wan-1.3B layer (84 units of 256 rows for 256
+    # compute units): the schedule splits, so the workspace must be written,
+    # and the result must match the plain launch within the bars above.
+    kpf, H, d, W, R = 1560, 12, 128, 6, 1
+    x = gen.stream_inputs(kpf, H, d, 1, W, R, "bf16", base_seed=5, wid=2)
+    kv, kr, vr, kf, vf = _make_cache(W, R, kpf, H, d, "bf16")
+    rtr.rtr_kv_reset_ref(kv, REF_REPLACE, dev(x["ref_k"]), dev(x["ref_v"]), R, -1)
+    rtr.rtr_kv_append_evict(kv, dev(x["ring_k"]), dev(x["ring_v"]), W)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    o1, l1 = rtr.rtr_attn_stream_step(kv, q, k, v, 1, want_lse=True, out_dtype=torch.float32)
+    ws = rtr.new_workspace(d)
+    ws.fill_(0xFF)
+    o2, l2 = rtr.rtr_attn_stream_step(kv, q, k, v, 1, want_lse=True, out_dtype=torch.float32,
+                                      workspace=ws)
+    torch.cuda.synchronize()
+    assert int((ws != 0xFF).sum()) > 0, "the split path did not run"
+    d_o = (o1 - o2).abs()
+    assert float(d_o.max()) < 2e-3 and float(d_o.mean()) < 1e-4
+    assert float((l1 - l2).abs().max()) < 1e-3
+    pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
+    pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
+    rows = _sample_rows(kpf, kpf, 16, seed=6)
+    heads = [0, H - 1]
+    ro, rl = oracle.attn_stream_rows(pk, pv, x["q"].values, x["k"].values, x["v"].values, kpf,
+                                     rows, heads)
+    assert_bf16_close(host(o2)[rows][:, heads], ro, "o")
+    assert_bf16_close(host(l2)[heads][:, rows], rl, "lse")
+
+
 def test_split_workspace_too_small_is_rejected():
     q = torch.zeros((512, 1, 128), dtype=torch.bfloat16, device="cuda")
     need = rtr.rtr_attn_workspace_size(128)
