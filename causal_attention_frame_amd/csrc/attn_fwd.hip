@@ -77,19 +77,31 @@ struct KArgs {
     int32_t piece;
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.
-// Give every XCD one contiguous range of work items so the query blocks of one
-// head (which read the same K/V) share an L2; inside a head, the latest (most
-// keys) query block goes first.
-__device__ inline int xcd_order(int b, int nwg) {
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2,
+// and an XCD starts its workgroups in index order as compute units free up.
+// Every XCD gets one contiguous head-major range of work items (head, query
+// block) so the query blocks of one head (which read the same K/V) share an
+// L2, and runs that range by query block, latest (most keys) first, across
+// its heads: longest work first, so no long block starts late.
+__device__ inline void map_block(int b, int nwg, int nqb, int &head, int &qb) {
     const int x = b & 7, i = b >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
-    return x * q8 + (x < r8 ? x : r8) + i;
-}
-__device__ inline void map_block(int b, int nwg, int nqb, int &head, int &qb) {
-    const int w = xcd_order(b, nwg);
-    head = w / nqb;
-    qb = nqb - 1 - (w - head * nqb);
+    const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
+    int rem = i;
+    head = lo / nqb;
+    qb = lo - head * nqb;  // not reached for a valid b
+    for (int q = nqb - 1; q >= 0; --q) {
+        if (hi - 1 - q < 0) continue;
+        const int hmin = lo - q > 0 ? (lo - q + nqb - 1) / nqb : 0;  // first head with unit (h, q) >= lo
+        const int hmax = (hi - 1 - q) / nqb;                          // last head with unit (h, q) < hi
+        const int cnt = hmax >= hmin ? hmax - hmin + 1 : 0;
+        if (rem < cnt) {
+            head = hmin + rem;
+            qb = q;
+            return;
+        }
+        rem -= cnt;
+    }
 }
 
 __device__ inline int key_limit(int i, const KArgs &a) {
