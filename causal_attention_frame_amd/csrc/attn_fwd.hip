@@ -470,19 +470,12 @@ __device__ inline v4i16 lds_tr16(const lds_u16 *p) {
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber is still honoured
-// 16 bytes per lane from global memory to LDS byte address m0 + 16 * lane.
-// Source: a wave-uniform 64-bit base in SGPRs plus a per-lane 32-bit offset.
-// The s_nop covers the wait states after an m0 write and after a VALU write of
-// an SGPR that a vector memory instruction reads.
-__device__ inline void dma16_sbase(uint64_t sbase, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(sbase), "s"(m0)
-                 : "memory", "m0");
-}
-// Two such loads in one statement (the K and the V row group of a tile); every
-// SGPR operand is written before the statement, so one 5-wait-state guard
-// covers both, and the second m0 write needs one wait state.
+// Two DMA loads (the K and the V row group of a tile), each 16 bytes per lane
+// from global memory to LDS byte address m0 + 16 * lane; source: a wave-uniform
+// 64-bit base in SGPRs plus a per-lane 32-bit offset.  The s_nop 4 covers the
+// wait states after an m0 write and after a VALU write of an SGPR that a vector
+// memory instruction reads (every SGPR operand is written before the
+// statement, so one guard covers both loads); the second m0 write needs one.
 __device__ inline void dma16x2_sbase(uint64_t kb, uint64_t vb, uint32_t ko, uint32_t vo, uint32_t mk, uint32_t mv) {
     asm volatile(
         "s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
@@ -491,7 +484,7 @@ __device__ inline void dma16x2_sbase(uint64_t kb, uint64_t vb, uint32_t ko, uint
         : "v"(ko), "v"(vo), "s"(mk), "s"(mv), "s"(kb), "s"(vb)
         : "memory", "m0");
 }
-// Same, from a per-lane 64-bit address.
+// One DMA load from a per-lane 64-bit address.
 __device__ inline void dma16_vaddr(const void *src, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
                  :
@@ -524,11 +517,6 @@ constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
 __device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// An empty volatile statement that reads an MFMA accumulator: the MFMAs that
-// produce it stay in front of it in program order (MFMAs have no side
-// effects, so without a use they may be sunk past later barriers).
-__device__ inline void pin(const f32x16 &x) { asm volatile("" ::"a"(x)); }
 
 // DMA addressing of the head_dim-128 kernel.
 enum DmaMode : int {
