@@ -122,7 +122,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan13b_stream_step",
-                    choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal"])
+                    choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal",
+                             "rollout"],
+                    help="rollout: one step is a whole 240-chunk rollout (stream step, commit, "
+                         "and a reference swap every 60 chunks)")
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -144,6 +147,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = gen.WORKLOADS[args.workload]
+    if args.workload == "rollout":
+        return rollout(args, w, dev)
 
     def to_dev(t):
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -264,6 +269,116 @@ def main():
                             "algorithmic_bytes": append_bytes}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, x, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def rollout(args, w, dev):
+    """A long streaming rollout: `chunks` successive C-frame chunks through the
+    W-frame window with an anchored reference that is replaced before chunks
+    0, swap_every, 2*swap_every, ... (RTR-DiT notes, Key Designs 4).  At each
+    swap the window keeps its newest frame (at chunk 0 it starts empty), so the
+    prefix refills from 1 frame.  One timed step is one whole rollout: every
+    reset, stream step and commit, all on device-resident inputs drawn from a
+    pool of P seeded chunk inputs and P reference frames."""
+    import torch
+    from causal_attention_frame_amd import inputs as gen
+    from causal_attention_frame_amd import rtr
+
+    kpf, H, d, C, W, R = w["k"], w["H"], w["d"], w["C"], w["W"], w["R"]
+    chunks, every, P = w["chunks"], w["swap_every"], 4
+
+    def dev_bf16(shape, step, tag):
+        t = gen.normal(shape, "bf16", 0, w["wid"], step, tag)
+        return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    pool = [tuple(dev_bf16((C * kpf, H, d), s, t) for t in (gen.TAG_Q, gen.TAG_K, gen.TAG_V))
+            for s in range(P)]
+    refs = [tuple(dev_bf16((R, kpf, H, d), s, t) for t in (gen.TAG_REFK, gen.TAG_REFV))
+            for s in range(P)]
+    kr = torch.empty((W, kpf, H, d), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty_like(kr)
+    kf = torch.empty((R, kpf, H, d), dtype=torch.bfloat16, device=dev)
+    vf = torch.empty_like(kf)
+    kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+    o = torch.empty_like(pool[0][0])
+    stream = torch.cuda.current_stream(dev)
+    ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
+
+    # window occupancy before each chunk, known on the host from the schedule
+    flops, count = [], 0
+    for i in range(chunks):
+        if i % every == 0:
+            count = 0 if i == 0 else min(count, 1)
+        flops.append(4 * d * H * stream_pairs_per_head(kpf, C, R + count))
+        count = min(W, count + C)
+    flops_total = sum(flops)
+
+    def one_rollout(ev=None):
+        for i in range(chunks):
+            if i % every == 0:
+                rk, rv = refs[(i // every) % P]
+                rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, rk, rv, R, 0 if i == 0 else 1)
+            q, k, v = pool[i % P]
+            if ev is not None:
+                ev[i][0].record(stream)
+            rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o, workspace=ws)
+            if ev is not None:
+                ev[i][1].record(stream)
+            rtr.rtr_kv_append_evict(kv, k, v, C)
+
+    for _ in range(args.warmup):
+        one_rollout()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_rollout()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    # one more rollout with events around each stream step, for the kernel time
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(chunks)]
+    one_rollout(ev)
+    torch.cuda.synchronize(dev)
+    attn_s = sum(a.elapsed_time(b) for a, b in ev) * 1e-3
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    frames = C * chunks
+    achieved = flops_total / attn_s / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(flops_total / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "rollout", "heads": H, "head_dim": d, "tokens_per_frame": kpf,
+                   "chunk_frames": C, "window_frames": W, "ref_frames": R, "chunks": chunks,
+                   "ref_swap_every": every, "keep_recent": 1},
+        "latent_frames_per_s_per_layer": round(frames / (ms_per_step * 1e-3), 1),
+        "ms_per_chunk": round(ms_per_step / chunks, 5),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_bf16_d128" + ("" if ws is None else " (+ split-K when planned)"),
+            "kernel_avg_us": round(attn_s / chunks * 1e6, 2),
+            "algorithmic_flop_per_launch": round(flops_total / chunks),
+        },
+    }
+    rtr.rtr_kv_destroy(kv)
+    if not args.no_cpu_baseline:
+        x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"])
+        out["cpu_baseline"] = cpu_baseline("rollout_stream_step", x, w, args.cpu_heads)
+        out["cpu_baseline"]["sample"] += " (one steady-state chunk of the rollout)"
     print(json.dumps(out), flush=True)
 
 
