@@ -1,0 +1,122 @@
+"""Pins of the float64 attention gradients against things other than themselves.
+
+The gradients are the derivative of the Attn equation (RTR-DiT notes, "DiT as
+Real-Time Rerenderer ...", Key Designs 2).  They are pinned to central finite
+differences of the (separately pinned) forward oracle, to torch.autograd on a
+literal float64 forward written here, and to invariants that follow from the
+softmax: rows of dS sum to zero, so dK sums to zero over keys and dQ ignores a
+common shift of all keys; rows of P sum to one, so dV sums to the summed dO.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention_bwd import attn_block_causal_bwd, attn_bwd_cols, attn_bwd_rows
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _inputs(T, H, d, seed):
+    return [_rand((T, H, d), seed + t) for t in range(4)]
+
+
+@pytest.mark.parametrize("T,H,d,kpf", [(7, 2, 4, 3), (6, 1, 3, 1), (5, 1, 4, 8)])
+def test_gradients_match_central_differences(T, H, d, kpf):
+    """Pin: central differences of L = sum(O * G), O from the forward oracle.
+    Covers a ragged last frame (7 = 3+3+1), token causality (k = 1) and the
+    unmasked case (k > T)."""
+    q, k, v, g = _inputs(T, H, d, 10)
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf)
+    eps = 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_block_causal(qq, kk, vv, kpf)
+        return float(np.sum(o * g))
+
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            args_p = [q.copy(), k.copy(), v.copy()]
+            args_m = [q.copy(), k.copy(), v.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("T,kpf", [(40, 6), (33, 33), (24, 1)])
+def test_gradients_match_autograd(T, kpf):
+    """Pin: torch.autograd (float64, CPU) through softmax(Q K^T / sqrt(d) + M) V
+    written out here."""
+    H, d = 2, 16
+    q, k, v, g = _inputs(T, H, d, 20)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    mask = torch.where(j // kpf <= i // kpf, 0.0, float("-inf")).double()
+    s = torch.einsum("thd,shd->hts", tq, tk) / d ** 0.5 + mask
+    o = torch.einsum("hts,shd->thd", torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(g))
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_gradient_invariants():
+    """Pin: closed-form consequences of the softmax, per head."""
+    T, H, d, kpf = 50, 3, 8, 7
+    q, k, v, g = _inputs(T, H, d, 30)
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf)
+    # rows of dS sum to zero -> sum over keys of dK is zero
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-11)
+    # rows of P sum to one -> sum over keys of dV equals sum over queries of dO
+    np.testing.assert_allclose(dv.sum(axis=0), g.sum(axis=0), atol=1e-11)
+    # a common shift of every key leaves P, hence dQ and dV, unchanged
+    shift = _rand((1, H, d), 31)
+    dq2, _, dv2 = attn_block_causal_bwd(q, k + shift, v, g, kpf)
+    np.testing.assert_allclose(dq2, dq, atol=1e-10)
+    np.testing.assert_allclose(dv2, dv, atol=1e-10)
+    # token 0 of frame 0 with k = 1 sees only itself: P = 1 there, dS = 0, dQ = 0
+    dq1, _, _ = attn_block_causal_bwd(q, k, v, g, 1)
+    assert np.all(dq1[0] == 0.0)
+    # keys of the last frame are seen only by rows of the last frame
+    last = (T - 1) // kpf * kpf
+    g2 = g.copy()
+    g2[last:] = 0.0
+    _, dk2, dv2 = attn_block_causal_bwd(q, k, v, g2, kpf)
+    assert np.all(dk2[last:] == 0.0) and np.all(dv2[last:] == 0.0)
+
+
+def test_gradients_scale_argument():
+    """An explicit scale equal to 1/sqrt(d) gives the same gradients; another
+    scale equals the default applied to Q pre-multiplied accordingly (dK and dV
+    exactly, dQ times the factor by the chain rule)."""
+    T, H, d, kpf = 20, 1, 8, 5
+    q, k, v, g = _inputs(T, H, d, 40)
+    a = attn_block_causal_bwd(q, k, v, g, kpf)
+    b = attn_block_causal_bwd(q, k, v, g, kpf, scale=1 / np.sqrt(d))
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-14, atol=1e-15)
+    f = 0.37 * np.sqrt(d)                  # scale 0.37 == default scale on f * q
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf, scale=0.37)
+    dq2, dk2, dv2 = attn_block_causal_bwd(f * q, k, v, g, kpf)
+    np.testing.assert_allclose(dk, dk2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, dv2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dq, f * dq2, rtol=1e-12, atol=1e-13)
+
+
+def test_rows_and_cols_variants_equal_dense():
+    T, H, d, kpf = 61, 2, 8, 9
+    q, k, v, g = _inputs(T, H, d, 50)
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf)
+    rows = [0, 5, 8, 9, 30, 53, 54, 60]
+    np.testing.assert_allclose(attn_bwd_rows(q, k, v, g, kpf, rows, [1, 0]),
+                               dq[rows][:, [1, 0]], rtol=1e-12, atol=1e-13)
+    cols = [0, 8, 9, 17, 40, 54, 60]
+    ck, cv = attn_bwd_cols(q, k, v, g, kpf, cols, [1], group=7)
+    np.testing.assert_allclose(ck, dk[cols][:, [1]], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(cv, dv[cols][:, [1]], rtol=1e-12, atol=1e-13)
