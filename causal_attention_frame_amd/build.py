@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "librtr_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = ["rtr_api.hip", "attn_fwd.hip", "kv_copy.hip"]
+SOURCES = ["rtr_api.hip", "attn_fwd.hip", "attn_bwd.hip", "kv_copy.hip"]
 ARCH = "gfx950"
 
 

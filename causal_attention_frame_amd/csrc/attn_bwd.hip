@@ -1,0 +1,551 @@
+// Gradients of frame-block-causal attention for gfx950 (MI355X / CDNA4).
+//
+// dQ, dK, dV of Attn(Q,K,V) = softmax(Q K^T * scale + M) V, the equation of
+// the RTR-DiT notes ("DiT as Real-Time Rerenderer ...", Key Designs 2), whose
+// generator post-training (Key Designs 3) back-propagates through it.  From the
+// forward's natural-log LSE, its output O and the upstream gradient dO, with
+// P = exp(S - LSE) recomputed tile by tile and D_i = sum_c dO_ic O_ic:
+//   dV = P^T dO,   dS = P * (dO V^T - D),   dK = scale dS^T Q,   dQ = scale dS K.
+// The frame mask enters as in the forward: key j is seen by query i iff
+// floor(j/k) <= floor(i/k), so a key is seen by every row from the first row
+// of its own frame on, and a row by every key below the end of its frame.
+//
+// Kernels (head_dim 128, bf16 in and out, fp32 accumulation):
+//   attn_bwd_prep       one 32-row tile per workgroup: LSE in log2 units and D
+//                       per row, and the tile's Q and dO transposed into the
+//                       layout the dK/dV kernel reads as MFMA A operands;
+//   attn_bwd_dkdv_d128  one workgroup per 256 keys of a head (8 waves x 32):
+//                       K and V stay in registers as MFMA B operands and the
+//                       workgroup walks the 32-row query tiles that see its
+//                       keys, staged into an LDS ring by DMA; dK^T and dV^T
+//                       accumulate in registers;
+//   attn_bwd_dq_d128    one workgroup per 256 query rows (8 waves x 32): Q and
+//                       dO stay in registers, the workgroup walks the 32-key
+//                       tiles its rows see; dQ^T accumulates in registers.
+// dQ is produced apart from dK/dV, recomputing S and dP, so that no partial
+// sum leaves a workgroup: no atomics, and the result is deterministic.
+//
+// MFMA is v_mfma_f32_32x32x16_bf16.  Lane l of a wave is (n = l mod 32,
+// g = l / 32).  An A operand lane holds row n and k = 8g..8g+7 of a 16-step;
+// a B operand lane column n and the same k; accumulator element r of a lane is
+// row 8 (r/4) + 4 g + (r mod 4), column n.  A 32x32 accumulator can therefore
+// serve directly as the B operand of a product that contracts over its rows:
+// k-step h takes elements 8h..8h+7, i.e. rows 16h + 8 (e/4) + 4g + (e mod 4)
+// for e = 0..7, and the A operand reads its k positions in that same order.
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <type_traits>
+
+#include "device_util.h"
+#include "rtr_internal.h"
+
+namespace rtr {
+namespace {
+
+using namespace dev;
+
+struct BArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float *lse;
+    uint16_t *dq, *dk, *dv;
+    float *rows;   // [H][nqt][64]: log2-domain LSE of the tile's 32 rows, then their D
+    uint16_t *qt;  // [H][nqt][4096]: transposed Q tiles
+    uint16_t *dot; // [H][nqt][4096]: transposed dO tiles
+    int32_t T, kpf, nqt;
+    int32_t nkb, nqb;  // 256-key blocks, 256-row blocks per head
+    int32_t nwg;       // workgroups of the current launch
+    int64_t ld;        // row stride in elements (H * 128)
+    float c;           // scale * log2(e)
+    float scale;
+};
+
+constexpr int kD = 128;
+constexpr int kTile = 32 * kD;  // elements of one 32-row tile
+
+// Position p (0..31) of a transposed tile row holds query row swap23(p) of the
+// tile: within each 16-row step the middle two groups of four trade places, so
+// that an A operand lane's eight k positions 8g..8g+7 of step h are the rows
+// 16h + 8 (e/4) + 4g + (e mod 4) that the accumulator layout assigns to it.
+__device__ inline int swap23(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// Transposed tile: row d (0..127) of 32 positions = four 16-byte chunks; chunk
+// c of row d is stored at chunk c ^ ((d / 4) mod 4), so that the 16 lanes of
+// one LDS pass (rows d..d+15, one logical chunk) touch 16 distinct bank groups.
+
+// Row-major 32x128 tile staged for plain reads only: chunk c (8 columns) of
+// row r at chunk c ^ (r mod 16).
+__device__ inline int swz_plain(int r) { return r & 15; }
+// Row-major tile read both plainly (16-byte reads of 16 rows) and transposed
+// (ds_read_b64_tr_b16 over 4 rows x 32 bytes): chunk c of row r at chunk
+// c ^ s(r), s(r) = 2 (r mod 8) + (r / 8 mod 2) -- a permutation of 0..15 over
+// any 16 consecutive rows, whose values shifted right by one also differ
+// over any 4 consecutive rows starting at a multiple of 4.
+__device__ inline int swz_dual(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// Row statistics and transposed tiles.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_bwd_prep(const BArgs a) {
+    __shared__ uint16_t sT[2][kD][33];  // [Q, dO][d][row], padded against bank conflicts
+    const int tile = blockIdx.x, head = blockIdx.y;
+    const int tid = threadIdx.x, r = tid >> 3, c8 = tid & 7;  // row, 16-column group
+    const int qrow = tile * 32 + r;
+    const bool valid = qrow < a.T;
+    const long off = (long)qrow * a.ld + (long)head * kD + 16 * c8;
+    u32x4 qv[2] = {}, dv[2] = {}, ov[2] = {};
+    if (valid) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            qv[h] = gload16(a.q + off + 8 * h);
+            dv[h] = gload16(a.dout + off + 8 * h);
+            ov[h] = gload16(a.o + off + 8 * h);
+        }
+    }
+    float dsum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            dsum = fmaf(bf_lo(dv[h][w]), bf_lo(ov[h][w]), dsum);
+            dsum = fmaf(bf_hi(dv[h][w]), bf_hi(ov[h][w]), dsum);
+        }
+    dsum += __shfl_xor(dsum, 1);
+    dsum += __shfl_xor(dsum, 2);
+    dsum += __shfl_xor(dsum, 4);
+    float *rows = a.rows + ((long)head * a.nqt + tile) * 64;
+    if (c8 == 0) {
+        rows[r] = valid ? a.lse[(long)head * a.T + qrow] * kLog2e : INFINITY;
+        rows[32 + r] = valid ? dsum : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int d = 16 * c8 + 8 * h + 2 * w;
+            sT[0][d][r] = (uint16_t)qv[h][w];
+            sT[0][d + 1][r] = (uint16_t)(qv[h][w] >> 16);
+            sT[1][d][r] = (uint16_t)dv[h][w];
+            sT[1][d + 1][r] = (uint16_t)(dv[h][w] >> 16);
+        }
+    __syncthreads();
+    const long tbase = ((long)head * a.nqt + tile) * kTile;
+#pragma unroll
+    for (int zz = 0; zz < 2; ++zz) {
+        const int z = tid + 256 * zz;  // output chunk: row d, stored chunk pc
+        const int d = z >> 2, pc = z & 3, lc = pc ^ ((d >> 2) & 3);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = 8 * lc + 2 * e;
+                w[e] = (uint32_t)sT[t][d][swap23(p)] | ((uint32_t)sT[t][d][swap23(p + 1)] << 16);
+            }
+            *(u32x4 *)((t ? a.dot : a.qt) + tbase + 8 * z) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK and dV: one workgroup per 256 keys.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void attn_bwd_dkdv_d128(const BArgs a) {
+    constexpr int NS = 8, NT = 4, NSTG = 4;
+    // One LDS array: regions of NSTG stages each -- row-major Q, row-major dO,
+    // transposed Q, transposed dO (8 KB per stage), then the row statistics
+    // (256 B per stage).  Every fragment read is one of a few per-lane bases
+    // plus an immediate offset (region, stage, column block) below 64 KB.
+    constexpr int RQ = 0, RDO = NSTG * kTile, RQT = 2 * NSTG * kTile, RDOT = 3 * NSTG * kTile;
+    constexpr int RROW = 4 * NSTG * kTile;  // in uint16 units
+    __shared__ __attribute__((aligned(256))) uint16_t smem[4 * NSTG * kTile + NSTG * 128];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+
+    int head, blk;
+    xcd_order(blockIdx.x, a.nwg, a.nkb, head, blk);
+    const int kb = a.nkb - 1 - blk;  // highest order index = lowest keys = most rows
+    const int k0 = kb * 256;
+    const long hoff = (long)head * kD;
+
+    // This lane's key (column n of the wave's S tiles) and the first row that sees it.
+    const int kj = k0 + 32 * wave + n;
+    const bool kvalid = kj < a.T;
+    const int qmin = (kj / a.kpf) * a.kpf;
+    const int t0 = ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
+    const int nt = a.nqt - t0;
+    // Tiles that start below the first row of the block's last key frame may
+    // hold rows that miss some of its keys: they take the element-wise mask.
+    const int last_key = min(k0 + 255, a.T - 1);
+    const int nmask = min(nt, max(0, ((last_key / a.kpf) * a.kpf - t0 * 32 + 31) / 32));
+
+    // K and V as B operands: lane (n, g) holds row kj, columns 16 s + 8 g .. + 7.
+    bf16x8 kf[NS], vf[NS];
+    {
+        const long ro = (long)(kvalid ? kj : a.T - 1) * a.ld + hoff;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kf[s] = __builtin_bit_cast(bf16x8, gload16(a.k + ro + 16 * s + 8 * g));
+            vf[s] = __builtin_bit_cast(bf16x8, gload16(a.v + ro + 16 * s + 8 * g));
+        }
+    }
+
+    // DMA of one query tile, 5 loads per wave: row-major Q and dO (wave w
+    // fills rows 4w + lr, lane (lr, pch) the stored chunk pch), the two
+    // transposed tiles (contiguous 8 KB, wave w its 1 KB) and the row
+    // statistics (32 bytes per wave, lanes 0 and 1).
+    const int lr = lane >> 4, pch = lane & 15;
+    const int prow = 4 * wave + lr;
+    const uint32_t plain_col = (uint32_t)(16 * (pch ^ swz_plain(prow)));
+    const uint32_t l0 = lds_addr((lds_u16 *)smem) + 1024 * wave;
+    auto issue = [&](int i, auto S) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value;
+        const int tq = min(t0 + i, a.nqt - 1);
+        const int row = min(tq * 32 + prow, a.T - 1);
+        const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + plain_col;
+        dma16x2((uint64_t)a.q, (uint64_t)a.dout, off, off, l0 + 2 * (RQ + st * kTile), l0 + 2 * (RDO + st * kTile));
+        const long tb = ((long)head * a.nqt + tq) * kTile * 2 + 1024 * wave;
+        dma16x2((uint64_t)a.qt + tb, (uint64_t)a.dot + tb, 16u * lane, 16u * lane, l0 + 2 * (RQT + st * kTile),
+                l0 + 2 * (RDOT + st * kTile));
+        const uint64_t rb = (uint64_t)(a.rows + ((long)head * a.nqt + tq) * 64 + 8 * wave);
+        if (lane < 2) dma16(rb, 16u * lane, lds_addr((lds_u16 *)smem) + 2 * (RROW + st * 128) + 32 * wave);
+    };
+
+    auto issue_rt = [&](int i) __attribute__((always_inline)) {
+        switch (i & 3) {
+            case 0: issue(i, std::integral_constant<int, 0>{}); break;
+            case 1: issue(i, std::integral_constant<int, 1>{}); break;
+            case 2: issue(i, std::integral_constant<int, 2>{}); break;
+            default: issue(i, std::integral_constant<int, 3>{}); break;
+        }
+    };
+    // Fragment addresses (LDS byte addresses, stage 0 of the Q regions; the
+    // region and stage are immediate offsets).  Plain read of k-step s (row n,
+    // logical chunk 2s + g, stored at chunk (2s + g) ^ (n mod 16)) is at
+    // aq ^ 32 s; transposed read of row d = 32 t + n, k-step h (logical chunk
+    // 2h + g, stored at (2h + g) ^ (n/4 mod 4)) at at ^ 32 h, + 2048 t.  The
+    // XOR is issued at each use, so the eight addresses never occupy registers.
+    const uint32_t lbase = lds_addr((lds_u16 *)smem);
+    const uint32_t aq = lbase + 2 * (n * kD + 8 * (g ^ swz_plain(n)));
+    const uint32_t at = lbase + 2 * (RQT + n * 32 + 8 * (g ^ ((n >> 2) & 3)));
+    const uint32_t ar = lbase + 2 * (RROW + 8 * g);
+    auto xaddr = [](uint32_t base, auto X) __attribute__((always_inline)) {
+        uint32_t r;
+        asm volatile("v_xor_b32 %0, %2, %1" : "=v"(r) : "v"(base), "i"(decltype(X)::value));
+        return (const lds_u16 *)(uintptr_t)r;
+    };
+    using Z = std::integral_constant<int, 0>;
+    uint32_t aqs = aq, ats = at;
+    auto rd_plain = [&](auto K, int off) __attribute__((always_inline)) {
+        return lds_b128(xaddr(aqs, std::integral_constant<int, 32 * decltype(K)::value>{}) + off);
+    };
+    auto rd_tr = [&](auto H, int off) __attribute__((always_inline)) {
+        return lds_b128(xaddr(ats, std::integral_constant<int, 32 * decltype(H)::value>{}) + off);
+    };
+    const lds_u16 *pr = (const lds_u16 *)(uintptr_t)ar;
+
+    f32x16 dkt[NT], dvt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dkt[t] = dvt[t] = f32x16{};
+    const float c = a.c;
+
+    // One query tile: S = Q K^T, P (bf16) from S, dP = dO V^T, dS = P (dP - D)
+    // with the bf16 P, then dV^T += dO^T P and dK^T += Q^T dS.
+    // The ring stage is a runtime value: unrolling the loop over static stages
+    // makes the register allocator copy the accumulators between the unrolled
+    // copies, which does not fit in 256 registers.
+    auto step = [&](int i) __attribute__((always_inline)) {
+        constexpr int st = 0;  // stage offsets live in the per-step bases
+        const int rst = i & 3;
+        aqs = aq + rst * kTile * 2;
+        ats = at + rst * kTile * 2;
+        pr = (const lds_u16 *)(uintptr_t)(ar + rst * 256);
+        __builtin_amdgcn_s_waitcnt(wait_vm(10));  // this wave's loads of tile i landed
+        lds_barrier();                             // everyone's have; stage of tile i - 1 is free
+        f32x16 sc = {};
+        auto qk = [&](auto K) __attribute__((always_inline)) {
+            constexpr int k = decltype(K)::value;
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_plain(K, RQ + st * kTile), kf[k], sc, 0, 0, 0);
+        };
+        qk(std::integral_constant<int, 0>{}); qk(std::integral_constant<int, 1>{});
+        qk(std::integral_constant<int, 2>{}); qk(std::integral_constant<int, 3>{});
+        qk(std::integral_constant<int, 4>{}); qk(std::integral_constant<int, 5>{});
+        qk(std::integral_constant<int, 6>{}); qk(std::integral_constant<int, 7>{});
+        // Row e of group j is 8 j + 4 g + e of the tile; it sees this lane's
+        // key iff 8 j + e >= thr (always, past the first nmask tiles).
+        const int thr = i < nmask ? qmin - (t0 + i) * 32 - 4 * g : INT_MIN;
+        uint32_t pw[8];  // P as bf16 pairs, rows 2m, 2m + 1 of the lane's 16
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 l2 = *(const lds_f32x4 *)(pr + st * 128 + 16 * j);
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(fmaf(sc[4 * j + e], c, -l2[e]));
+                p[e] = (8 * j + e >= thr) ? p[e] : 0.f;
+            }
+            pw[2 * j] = pack_bf16x2(p[0], p[1]);
+            pw[2 * j + 1] = pack_bf16x2(p[2], p[3]);
+        }
+        const bf16x8 pb[2] = {__builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]}),
+                              __builtin_bit_cast(bf16x8, u32x4{pw[4], pw[5], pw[6], pw[7]})};
+        f32x16 dp = {};
+        auto dov = [&](auto K) __attribute__((always_inline)) {
+            constexpr int k = decltype(K)::value;
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_plain(K, RDO + st * kTile), vf[k], dp, 0, 0, 0);
+        };
+        dov(std::integral_constant<int, 0>{}); dov(std::integral_constant<int, 1>{});
+        dov(std::integral_constant<int, 2>{}); dov(std::integral_constant<int, 3>{});
+        dov(std::integral_constant<int, 4>{}); dov(std::integral_constant<int, 5>{});
+        dov(std::integral_constant<int, 6>{}); dov(std::integral_constant<int, 7>{});
+        uint32_t sw[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const f32x4 dd = *(const lds_f32x4 *)(pr + st * 128 + 64 + 16 * j);
+            const uint32_t w0 = pw[2 * j], w1 = pw[2 * j + 1];
+            sw[2 * j] = pack_bf16x2(bf_lo(w0) * (dp[4 * j] - dd[0]), bf_hi(w0) * (dp[4 * j + 1] - dd[1]));
+            sw[2 * j + 1] = pack_bf16x2(bf_lo(w1) * (dp[4 * j + 2] - dd[2]), bf_hi(w1) * (dp[4 * j + 3] - dd[3]));
+        }
+        const bf16x8 sb[2] = {__builtin_bit_cast(bf16x8, u32x4{sw[0], sw[1], sw[2], sw[3]}),
+                              __builtin_bit_cast(bf16x8, u32x4{sw[4], sw[5], sw[6], sw[7]})};
+        auto grads = [&](auto H) __attribute__((always_inline)) {
+            constexpr int h = decltype(H)::value;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                dvt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(H, (RDOT - RQT) + st * kTile + 1024 * t), pb[h],
+                                                                 dvt[t], 0, 0, 0);
+                dkt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_tr(H, st * kTile + 1024 * t), sb[h], dkt[t], 0, 0, 0);
+            }
+        };
+        grads(std::integral_constant<int, 0>{});
+        grads(std::integral_constant<int, 1>{});
+        issue_rt(i + NSTG - 1);
+    };
+
+    issue(0, std::integral_constant<int, 0>{});
+    issue(1, std::integral_constant<int, 1>{});
+    issue(2, std::integral_constant<int, 2>{});
+#pragma unroll 1
+    for (int i = 0; i < nt; ++i) {
+        step(i);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no DMA outlives the workgroup's LDS
+    compiler_fence();
+
+    if (!kvalid) return;
+    const long ob = (long)kj * a.ld + hoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * t + 8 * j + 4 * g;
+            *(u32x2 *)(a.dk + ob + d0) = u32x2{pack_bf16x2(dkt[t][4 * j] * a.scale, dkt[t][4 * j + 1] * a.scale),
+                                               pack_bf16x2(dkt[t][4 * j + 2] * a.scale, dkt[t][4 * j + 3] * a.scale)};
+            *(u32x2 *)(a.dv + ob + d0) = u32x2{pack_bf16x2(dvt[t][4 * j], dvt[t][4 * j + 1]),
+                                               pack_bf16x2(dvt[t][4 * j + 2], dvt[t][4 * j + 3])};
+        }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per 256 query rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
+    constexpr int NS = 8, NT = 4, NSTG = 4;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[NSTG * kTile];
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+
+    int head, qb;
+    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
+    const int q0 = qb * 256;
+    const long hoff = (long)head * kD;
+    const int qi = q0 + 32 * wave + n;
+    const bool qv = qi < a.T;
+    auto key_limit = [&](int i) __attribute__((always_inline)) { return (int)min((long)(i / a.kpf + 1) * a.kpf, (long)a.T); };
+    const int lim = key_limit(qv ? qi : a.T - 1);
+    const int lim_lo = key_limit(q0);
+    const int lim_hi = key_limit(min(q0 + 255, a.T - 1));
+    const int ntiles = (lim_hi + 31) / 32;
+    const int nfull = min(ntiles, lim_lo / 32);  // tiles every row of the block sees whole
+
+    // Q and dO as B operands: lane (n, g) holds row qi, columns 16 s + 8 g .. + 7.
+    bf16x8 qf[NS], df[NS];
+    {
+        const long ro = (long)(qv ? qi : a.T - 1) * a.ld + hoff;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            qf[s] = __builtin_bit_cast(bf16x8, gload16(a.q + ro + 16 * s + 8 * g));
+            df[s] = __builtin_bit_cast(bf16x8, gload16(a.dout + ro + 16 * s + 8 * g));
+        }
+    }
+    float l2 = INFINITY, dd = 0.f;
+    if (qv) {
+        const float *rs = a.rows + ((long)head * a.nqt + qi / 32) * 64;
+        l2 = rs[qi & 31];
+        dd = rs[32 + (qi & 31)];
+    }
+
+    // DMA of one key tile: K and V rows 4w + lr, lane (lr, pch) the stored chunk pch.
+    const int lr = lane >> 4, pch = lane & 15;
+    const int prow = 4 * wave + lr;
+    const uint32_t col2 = (uint32_t)(16 * (pch ^ swz_dual(prow)));
+    const uint32_t lk = lds_addr((lds_u16 *)sK), lv = lds_addr((lds_u16 *)sV);
+    auto issue = [&](int j, auto S) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value;
+        const int row = min(j * 32 + prow, a.T - 1);
+        const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + col2;
+        dma16x2((uint64_t)a.k, (uint64_t)a.v, off, off, lk + st * kTile * 2 + 1024 * wave, lv + st * kTile * 2 + 1024 * wave);
+    };
+
+    // Plain reads (A operand of S^T = K Q^T and dP^T = V dO^T: key row n,
+    // k = 16 s + 8 g ..).
+    const lds_u16 *pk[NS], *pv[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const int o = n * kD + 8 * ((2 * s + g) ^ swz_dual(n));
+        pk[s] = (lds_u16 *)sK + o;
+        pv[s] = (lds_u16 *)sV + o;
+    }
+    // Transposed reads (A operand of dQ^T = K^T dS^T: row d = 32 t + n, k-step h
+    // at keys 16 h + 4 g + 0..3 and 16 h + 8 + 4 g + 0..3).  ds_read_b64_tr_b16:
+    // the 16 lanes of group G read a 4-row x 16-column block, lane sl giving the
+    // address of row sl/4, columns 4 (sl mod 4) .. + 3, and receive column sl.
+    const int G = lane >> 4, sl = lane & 15;
+    const lds_u16 *ptr[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int r = 4 * (G >> 1) + (sl >> 2) + 8 * e;
+            const int ch = 4 * t + 2 * (G & 1) + ((sl & 3) >> 1);
+            ptr[t][e] = (lds_u16 *)sK + r * kD + 8 * (ch ^ swz_dual(r)) + 4 * (sl & 1);
+        }
+
+    f32x16 dqt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dqt[t] = f32x16{};
+    const float c = a.c;
+
+    auto step = [&](int j, auto S, auto masked) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value;
+        constexpr bool MASK = decltype(masked)::value;
+        __builtin_amdgcn_s_waitcnt(wait_vm(4));
+        lds_barrier();
+        f32x16 s = {}, dp = {};
+#pragma unroll
+        for (int k = 0; k < NS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(pk[k] + st * kTile), qf[k], s, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(pv[k] + st * kTile), df[k], dp, 0, 0, 0);
+        bf16x8 sb[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
+            if (MASK) p = (j * 32 + 8 * (r >> 2) + 4 * g + (r & 3) < lim) ? p : 0.f;
+            sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dd));
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x8 kt = cat_tr(lds_tr16(ptr[t][0] + st * kTile + 16 * h * kD),
+                                         lds_tr16(ptr[t][1] + st * kTile + 16 * h * kD));
+                dqt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, sb[h], dqt[t], 0, 0, 0);
+            }
+        issue(j + NSTG - 1, std::integral_constant<int, (st + NSTG - 1) % NSTG>{});
+    };
+
+    issue(0, I0{});
+    issue(1, I1{});
+    issue(2, I2{});
+    int j = 0;
+#pragma unroll 1
+    for (; j + 4 <= nfull; j += 4) {
+        step(j, I0{}, std::false_type{});
+        step(j + 1, I1{}, std::false_type{});
+        step(j + 2, I2{}, std::false_type{});
+        step(j + 3, I3{}, std::false_type{});
+    }
+#pragma unroll 1
+    for (; j < ntiles; j += 4) {
+        step(j, I0{}, std::true_type{});
+        if (j + 1 >= ntiles) break;
+        step(j + 1, I1{}, std::true_type{});
+        if (j + 2 >= ntiles) break;
+        step(j + 2, I2{}, std::true_type{});
+        if (j + 3 >= ntiles) break;
+        step(j + 3, I3{}, std::true_type{});
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    compiler_fence();
+
+    if (!qv) return;
+    const long ob = (long)qi * a.ld + hoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * t + 8 * i + 4 * g;
+            *(u32x2 *)(a.dq + ob + d0) = u32x2{pack_bf16x2(dqt[t][4 * i] * a.scale, dqt[t][4 * i + 1] * a.scale),
+                                               pack_bf16x2(dqt[t][4 * i + 2] * a.scale, dqt[t][4 * i + 3] * a.scale)};
+        }
+}
+
+}  // namespace
+
+hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes) {
+    const int64_t nqt = (T + 31) / 32;
+    *bytes = (size_t)(H * nqt) * (64 * sizeof(float) + 2 * kTile * sizeof(uint16_t));
+    return hipSuccess;
+}
+
+hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
+    if (p.T == 0) return hipSuccess;
+    BArgs a{};
+    a.q = (const uint16_t *)p.q;
+    a.k = (const uint16_t *)p.k;
+    a.v = (const uint16_t *)p.v;
+    a.o = (const uint16_t *)p.o;
+    a.dout = (const uint16_t *)p.dout;
+    a.lse = p.lse;
+    a.dq = (uint16_t *)p.dq;
+    a.dk = (uint16_t *)p.dk;
+    a.dv = (uint16_t *)p.dv;
+    a.T = (int32_t)p.T;
+    a.kpf = (int32_t)std::min<int64_t>(p.tokens_per_frame, p.T);
+    a.nqt = (int32_t)((p.T + 31) / 32);
+    a.nkb = (int32_t)((p.T + 255) / 256);
+    a.nqb = a.nkb;
+    a.ld = (int64_t)p.H * kD;
+    a.scale = p.scale;
+    a.c = p.scale * kLog2e;
+    const int64_t ntile = (int64_t)p.H * a.nqt;
+    a.rows = (float *)p.ws;
+    a.qt = (uint16_t *)(a.rows + ntile * 64);
+    a.dot = a.qt + ntile * kTile;
+
+    hipLaunchKernelGGL(attn_bwd_prep, dim3(a.nqt, p.H), dim3(256), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+    a.nwg = p.H * a.nkb;
+    hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+    a.nwg = p.H * a.nqb;
+    hipLaunchKernelGGL(attn_bwd_dq_d128, dim3(a.nwg), dim3(512), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace rtr

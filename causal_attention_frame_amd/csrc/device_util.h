@@ -1,0 +1,114 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// the XCD-aware work order, LDS access and global-to-LDS DMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace rtr {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2,
+// and an XCD starts its workgroups in index order as compute units free up.
+// Every XCD gets one contiguous head-major range of work items (head, block)
+// so the blocks of one head (which read the same tensors) share an L2, and
+// runs that range by block index, highest first, across its heads.  Callers
+// number blocks so that the highest index carries the most work.
+__device__ inline void xcd_order(int b, int nwg, int nblk, int &head, int &blk) {
+    const int x = b & 7, i = b >> 3;
+    const int q8 = nwg >> 3, r8 = nwg & 7;
+    const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
+    int rem = i;
+    head = lo / nblk;
+    blk = lo - head * nblk;  // not reached for a valid b
+    for (int q = nblk - 1; q >= 0; --q) {
+        if (hi - 1 - q < 0) continue;
+        const int hmin = lo - q > 0 ? (lo - q + nblk - 1) / nblk : 0;
+        const int hmax = (hi - 1 - q) / nblk;
+        const int cnt = hmax >= hmin ? hmax - hmin + 1 : 0;
+        if (rem < cnt) {
+            head = hmin + rem;
+            blk = q;
+            return;
+        }
+        rem -= cnt;
+    }
+}
+
+__device__ inline uint32_t lds_addr(const lds_u16 *p) { return (uint32_t)(uintptr_t)p; }
+
+__device__ inline v4i16 lds_tr16(const lds_u16 *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+}
+
+__device__ inline bf16x8 lds_b128(const lds_u16 *p) { return __builtin_bit_cast(bf16x8, *(lds_u32x4 *)p); }
+
+__device__ inline bf16x8 cat_tr(v4i16 lo, v4i16 hi) {
+    return __builtin_bit_cast(bf16x8, (v8i16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ inline u32x4 gload16(const uint16_t *p) { return *(const global_u32x4 *)p; }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber is still honoured
+// Two DMA loads, each 16 bytes per lane from global memory to LDS byte address
+// m0 + 16 * lane; source: a wave-uniform 64-bit base in SGPRs plus a per-lane
+// 32-bit byte offset.  The s_nop 4 covers the wait states after an m0 write
+// and after a VALU write of an SGPR that a vector memory instruction reads
+// (every SGPR operand is written before the statement, so one guard covers
+// both loads); the second m0 write needs one.
+__device__ inline void dma16x2(uint64_t b0, uint64_t b1, uint32_t o0, uint32_t o1, uint32_t m0a, uint32_t m0b) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5"
+        :
+        : "v"(o0), "v"(o1), "s"(m0a), "s"(m0b), "s"(b0), "s"(b1)
+        : "memory", "m0");
+}
+// One DMA load of the same form.
+__device__ inline void dma16(uint64_t b0, uint32_t o0, uint32_t m0a) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %2"
+                 :
+                 : "v"(o0), "s"(m0a), "s"(b0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Barrier after this wave's LDS reads have completed.
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+}
+
+// Two floats to a bf16 pair (round to nearest even), lo in the low half.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo, (__bf16)hi});
+}
+
+}  // namespace dev
+}  // namespace rtr

@@ -218,6 +218,78 @@ int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, 
     return ok();
 }
 
+int rtr_attn_bwd_workspace_size(int64_t T, int32_t H, int32_t d, size_t *bytes) {
+    if (!bytes) return fail(RTR_EINVAL, "bytes is NULL");
+    *bytes = 0;
+    if (T < 0 || T > kMaxTokens) return fail(RTR_EINVAL, "T=%lld out of range [0, 2^30]", (long long)T);
+    if (H < 1) return fail(RTR_EINVAL, "H=%d must be >= 1", H);
+    if (d != 128) return fail(RTR_EUNSUPPORTED, "backward head dim %d not supported (128)", d);
+    if (const hipError_t e = rtr::attention_bwd_workspace_bytes(T, H, bytes)) return hip_fail(e, "workspace size");
+    return ok();
+}
+
+int rtr_attn_block_causal_bwd(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, const void *d_o, void *dq, void *dk, void *dv,
+                              int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
+                              rtr_dtype dtype, float scale, void *workspace,
+                              size_t workspace_bytes, rtr_stream stream) {
+    if (T < 0 || T > kMaxTokens) return fail(RTR_EINVAL, "T=%lld out of range [0, 2^30]", (long long)T);
+    if (H < 1) return fail(RTR_EINVAL, "H=%d must be >= 1", H);
+    if (tokens_per_frame < 1) return fail(RTR_EINVAL, "tokens_per_frame must be >= 1");
+    if (!valid_dtype(dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (dtype != RTR_BF16) return fail(RTR_EUNSUPPORTED, "backward supports bf16 only");
+    if (d != 128) return fail(RTR_EUNSUPPORTED, "backward head dim %d not supported (128)", d);
+    if (T * H * d >= ((int64_t)1 << 31)) return fail(RTR_EUNSUPPORTED, "T * H * d must be below 2^31");
+    if (int rc = check_scale(scale)) return rc;
+    if (T == 0) return ok();
+    const void *in[6] = {q, k, v, o, lse, d_o};
+    void *out[3] = {dq, dk, dv};
+    for (const void *x : in)
+        if (!x) return fail(RTR_EINVAL, "q, k, v, o, lse and d_o must be non-NULL");
+    for (const void *x : out)
+        if (!x) return fail(RTR_EINVAL, "dq, dk and dv must be non-NULL");
+    for (const void *x : {q, k, v, o, d_o, (const void *)dq, (const void *)dk, (const void *)dv})
+        if (!aligned16(x)) return fail(RTR_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) != 0) return fail(RTR_EINVAL, "lse must be 4-byte aligned");
+    const int64_t tb = T * H * d * 2, lb = T * H * 4;
+    const int64_t in_sz[6] = {tb, tb, tb, tb, lb, tb};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(out[i], tb, in[j], in_sz[j])) return fail(RTR_EINVAL, "an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], tb, out[j], tb)) return fail(RTR_EINVAL, "outputs overlap");
+    }
+    size_t need = 0;
+    if (const hipError_t e = rtr::attention_bwd_workspace_bytes(T, H, &need)) return hip_fail(e, "workspace size");
+    if (!workspace) return fail(RTR_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(RTR_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(workspace, (int64_t)need, in[j], in_sz[j])) return fail(RTR_EINVAL, "workspace overlaps an input");
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, (int64_t)need, out[i], tb)) return fail(RTR_EINVAL, "workspace overlaps an output");
+
+    rtr::BwdProblem p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = d_o;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.T = T;
+    p.tokens_per_frame = tokens_per_frame;
+    p.H = H;
+    p.scale = resolve_scale(scale, d);
+    p.ws = workspace;
+    const hipError_t e = rtr::launch_attention_bwd(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return ok();
+}
+
 int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
                   int32_t window_frames, int32_t ref_capacity_frames, int64_t tokens_per_frame,
                   int32_t H, int32_t d, rtr_dtype dtype) {

@@ -50,6 +50,22 @@ hipError_t launch_attention(const AttnProblem &p, hipStream_t stream);
 // head dim and input type (0: the launch never splits).
 hipError_t attention_workspace_bytes(int32_t d, rtr_dtype in_dtype, size_t *bytes);
 
+// Gradients of the full-sequence form (bf16, head_dim 128).  ws holds
+// attention_bwd_workspace_bytes(T, H) bytes: per 32-row tile the log2-domain
+// LSE and D of its rows and its transposed Q and dO.
+struct BwdProblem {
+    const void *q = nullptr, *k = nullptr, *v = nullptr, *o = nullptr, *dout = nullptr;
+    const float *lse = nullptr;
+    void *dq = nullptr, *dk = nullptr, *dv = nullptr;
+    int64_t T = 0, tokens_per_frame = 1;
+    int32_t H = 0;
+    float scale = 0.f;
+    void *ws = nullptr;
+};
+
+hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes);
+hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream);
+
 // Copies of whole [k, H, d] frames (16-byte multiples, 16-byte aligned).
 struct CopyJobs {
     const void *src[kMaxCopies] = {};

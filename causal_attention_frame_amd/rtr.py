@@ -47,6 +47,10 @@ _SIGNATURES = {
                                              _c_i64, ctypes.c_int, ctypes.c_int, _c_f32, _vp,
                                              ctypes.c_size_t, _vp]),
     "rtr_attn_workspace_size": (ctypes.c_int, [_c_i32, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "rtr_attn_block_causal_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64,
+                                                 _c_i32, _c_i32, _c_i64, ctypes.c_int, _c_f32, _vp,
+                                                 ctypes.c_size_t, _vp]),
+    "rtr_attn_bwd_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)]),
     "rtr_kv_create": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _c_i32, _c_i32,
                                      _c_i64, _c_i32, _c_i32, ctypes.c_int]),
     "rtr_kv_destroy": (ctypes.c_int, [_vp]),
@@ -163,6 +167,36 @@ def rtr_attn_block_causal(q, k, v, tokens_per_frame, o=None, lse=None, scale=0.0
                                        float(scale), ws, ws_bytes, _stream(stream, q.device)),
            "rtr_attn_block_causal")
     return o, lse
+
+
+def rtr_attn_bwd_workspace_size(T, H, d=128):
+    """Bytes of device workspace rtr_attn_block_causal_bwd needs."""
+    n = ctypes.c_size_t(0)
+    _check(lib().rtr_attn_bwd_workspace_size(int(T), int(H), int(d), ctypes.byref(n)),
+           "rtr_attn_bwd_workspace_size")
+    return n.value
+
+
+def rtr_attn_block_causal_bwd(q, k, v, o, lse, d_o, tokens_per_frame, dq=None, dk=None, dv=None,
+                              scale=0.0, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of rtr_attn_block_causal for the upstream
+    gradient d_o, from the forward's o and lse.  The workspace (a device byte
+    tensor of rtr_attn_bwd_workspace_size bytes) is allocated when not given."""
+    import torch
+    T, H, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(max(1, rtr_attn_bwd_workspace_size(T, H, d)), dtype=torch.uint8,
+                                device=q.device)
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().rtr_attn_block_causal_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), T, H, d,
+                                           int(tokens_per_frame), _dtype_code(q), float(scale), ws,
+                                           ws_bytes, _stream(stream, q.device)),
+           "rtr_attn_block_causal_bwd")
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------- the cache

@@ -125,6 +125,40 @@ int rtr_attn_block_causal(const void *q, const void *k, const void *v, void *o, 
 int rtr_attn_workspace_size(int32_t d, rtr_dtype in_dtype, size_t *bytes);
 
 /* ------------------------------------------------------------------------
+ * Gradients of the full-sequence form: dQ, dK, dV of Attn(Q,K,V) (Key
+ * Designs 2 equation) for an upstream gradient dO -- the pass through which
+ * the generator post-training of Key Designs 3 (Self Forcing + DMD) sends its
+ * gradient.  With P = softmax(Q K^T * scale + M) recomputed from lse:
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),  dK = scale dS^T Q,
+ *   dQ = scale dS K.
+ *
+ *   q, k, v : [T, H, d] device bf16, the forward's inputs
+ *   o, lse  : the forward's output ([T, H, d] bf16) and natural-log LSE
+ *             ([H, T] float32) for the same inputs, mask and scale, as
+ *             written by rtr_attn_block_causal
+ *   d_o     : [T, H, d] device bf16, gradient of the loss with respect to o
+ *   dq, dk, dv : [T, H, d] device bf16 outputs (overwritten, not accumulated)
+ *   tokens_per_frame, scale : as in the forward call
+ *   d       : 128
+ *   dtype   : RTR_BF16
+ *   workspace, workspace_bytes : caller-owned device scratch of at least
+ *             rtr_attn_bwd_workspace_size(T, H, d) bytes, 256-byte aligned,
+ *             clobbered; it must not overlap any argument buffer, and calls
+ *             that may run concurrently need separate workspaces
+ * Limits: T * H * d < 2^31.  T == 0 is a no-op.  Returns RTR_OK or a negative
+ * rtr_status (RTR_EUNSUPPORTED for another dtype or head dim).
+ * ---------------------------------------------------------------------- */
+int rtr_attn_block_causal_bwd(const void *q, const void *k, const void *v, const void *o,
+                              const float *lse, const void *d_o, void *dq, void *dk, void *dv,
+                              int64_t T, int32_t H, int32_t d, int64_t tokens_per_frame,
+                              rtr_dtype dtype, float scale, void *workspace,
+                              size_t workspace_bytes, rtr_stream stream);
+
+/* Workspace bytes rtr_attn_block_causal_bwd needs: per head and 32-row tile,
+ * 256 bytes of row statistics and 16 KiB of transposed Q and dO. */
+int rtr_attn_bwd_workspace_size(int64_t T, int32_t H, int32_t d, size_t *bytes);
+
+/* ------------------------------------------------------------------------
  * KV cache of one attention layer over caller-owned device buffers
  * (Key Designs 4).  k_ring, v_ring: [W, k, H, d]; k_ref, v_ref: [R_cap, k, H, d]
  * (may be NULL when R_cap == 0).  Starts empty: count 0, no reference,

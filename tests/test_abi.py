@@ -244,3 +244,49 @@ def test_state_roundtrip_resume():
         rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_CLEAR, None, None, 1, 1)
         rtr.rtr_kv_commit_inplace(kv, 2)
     assert _state(a) == _state(b)
+
+
+def _bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + MB, v=FAKE + 2 * MB, o=FAKE + 3 * MB, lse=FAKE + 4 * MB,
+             do=FAKE + 5 * MB, dq=FAKE + 6 * MB, dk=FAKE + 7 * MB, dv=FAKE + 8 * MB, T=64, H=2,
+             d=128, kpf=16, dt=rtr.RTR_BF16, scale=0.0, ws=FAKE + 16 * MB, ws_bytes=16 * MB,
+             stream=None)
+    a.update(kw)
+    return rtr.lib().rtr_attn_block_causal_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                                               a["dq"], a["dk"], a["dv"], a["T"], a["H"], a["d"],
+                                               a["kpf"], a["dt"], a["scale"], a["ws"],
+                                               a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), rtr.RTR_EINVAL),
+    (dict(H=0), rtr.RTR_EINVAL),
+    (dict(kpf=0), rtr.RTR_EINVAL),
+    (dict(d=64), rtr.RTR_EUNSUPPORTED),
+    (dict(dt=rtr.RTR_F32), rtr.RTR_EUNSUPPORTED),
+    (dict(dt=9), rtr.RTR_EINVAL),
+    (dict(T=1 << 20, H=16), rtr.RTR_EUNSUPPORTED),     # T * H * d >= 2^31
+    (dict(do=None), rtr.RTR_EINVAL),
+    (dict(lse=None), rtr.RTR_EINVAL),
+    (dict(dv=None), rtr.RTR_EINVAL),
+    (dict(q=FAKE + 8), rtr.RTR_EINVAL),                 # misaligned
+    (dict(lse=FAKE + 4 * MB + 2), rtr.RTR_EINVAL),      # misaligned lse
+    (dict(dk=FAKE + 64), rtr.RTR_EINVAL),               # dk overlaps q
+    (dict(dk=FAKE + 6 * MB + 64), rtr.RTR_EINVAL),      # dk overlaps dq
+    (dict(ws=None), rtr.RTR_EINVAL),
+    (dict(ws=FAKE + 16 * MB + 16), rtr.RTR_EINVAL),     # workspace not 256-byte aligned
+    (dict(ws_bytes=100), rtr.RTR_EINVAL),               # workspace too small
+    (dict(ws=FAKE + 5 * MB), rtr.RTR_EINVAL),           # workspace overlaps d_o
+    (dict(scale=float("inf")), rtr.RTR_EINVAL),
+])
+def test_block_causal_bwd_rejects_before_launch(kw, code):
+    assert _bwd(**kw) == code
+    assert rtr.lib().rtr_last_error()
+
+
+def test_bwd_workspace_size():
+    n = rtr.rtr_attn_bwd_workspace_size(100, 3, 128)
+    assert n == 3 * 4 * (256 + 2 * 8192)        # 4 tiles of 32 rows per head
+    assert rtr.rtr_attn_bwd_workspace_size(0, 3, 128) == 0
+    with pytest.raises(rtr.RtrError):
+        rtr.rtr_attn_bwd_workspace_size(100, 3, 64)
