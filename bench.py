@@ -31,7 +31,12 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 METRIC = "block-causal attn TFLOP/s + latent frames/s per layer (frac of MFMA peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
-KERNEL_SRC = os.path.join(ROOT, "causal_attention_frame_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "causal_attention_frame_amd", "csrc")
+# Sources whose code the counter runs of a workload depend on.
+KERNEL_SRCS = {
+    "forward": [os.path.join(CSRC, "attn_fwd.hip")],
+    "backward": [os.path.join(CSRC, "attn_bwd.hip"), os.path.join(CSRC, "device_util.h")],
+}
 
 
 def stream_pairs_per_head(kpf, C, prefix_frames):
@@ -48,16 +53,17 @@ def full_pairs_per_head(T, kpf):
     return pairs
 
 
-def kernel_hash():
-    """Hash of the kernel source's code: // comments, trailing blanks and
+def kernel_hash(which="forward"):
+    """Hash of the kernel sources' code: // comments, trailing blanks and
     blank lines are dropped, so editing a comment does not orphan the
-    committed counter runs (the source has no block comments)."""
+    committed counter runs (the sources have no block comments)."""
     lines = []
-    with open(KERNEL_SRC) as f:
-        for line in f:
-            code = line.split("//", 1)[0].rstrip()
-            if code:
-                lines.append(code)
+    for path in KERNEL_SRCS[which]:
+        with open(path) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
@@ -73,7 +79,8 @@ def read_traffic(workload):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_hash():
+    which = "backward" if workload.endswith("_bwd") else "forward"
+    if vals.get("kernel_source_sha256_16") != kernel_hash(which):
         return None
     try:
         return float(vals["attn_hbm_bytes_per_launch_calibrated"])
@@ -123,7 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan13b_stream_step",
                     choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal",
-                             "rollout"],
+                             "full_block_causal_bwd", "rollout"],
                     help="rollout: one step is a whole 240-chunk rollout (stream step, commit, "
                          "and a reference swap every 60 chunks)")
     ap.add_argument("--cpu-heads", type=int, default=12,
@@ -149,6 +156,8 @@ def main():
     w = gen.WORKLOADS[args.workload]
     if args.workload == "rollout":
         return rollout(args, w, dev)
+    if args.workload == "full_block_causal_bwd":
+        return backward(args, w, dev)
 
     def to_dev(t):
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -269,6 +278,94 @@ def main():
                             "algorithmic_bytes": append_bytes}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, x, w, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+def backward(args, w, dev):
+    """Gradients of the full-sequence form (the training step's attention
+    backward): one step is one rtr_attn_block_causal_bwd call -- the prep, dK/dV
+    and dQ kernels -- on resident q, k, v, o, lse and dO (o and lse from the
+    library's forward).  Algorithmic work: the five products of the standard
+    count (S recomputed, dP, dV, dK, dQ), 2.5x the forward's."""
+    import torch
+    from causal_attention_frame_amd import inputs as gen
+    from causal_attention_frame_amd import rtr
+
+    kpf, H, d, F = w["k"], w["H"], w["d"], w["frames"]
+    T = kpf * F
+    x = gen.bwd_inputs(T, H, d, "bf16", base_seed=0, wid=w["wid"])
+    q, k, v, do = (torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16) for t in x)
+    o, lse = rtr.rtr_attn_block_causal(q, k, v, kpf, want_lse=True)
+    ws = torch.empty(rtr.rtr_attn_bwd_workspace_size(T, H, d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    pairs = full_pairs_per_head(T, kpf)
+    flops = 10 * d * H * pairs
+
+    def step():
+        rtr.rtr_attn_block_causal_bwd(q, k, v, o, lse, do, kpf, dq, dk, dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = elapsed * 1e3 / args.steps
+    call_s = float(call_ms.mean()) * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "full_block_causal_bwd", "heads": H, "head_dim": d,
+                   "tokens_per_frame": kpf, "frames": F, "tokens": T},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(flops / call_s / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic("full_block_causal_bwd"),
+            "kernel": "attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128 (one call)",
+            "kernel_avg_us": round(call_s * 1e6, 2),
+            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count()
+        heads = list(range(min(H, args.cpu_heads)))
+        rows = list(range(0, T, max(1, T // 64)))
+        t1 = time.perf_counter()
+        oracle.attn_bwd_rows(x[0].values, x[1].values, x[2].values, x[3].values, kpf, rows, heads)
+        dt = time.perf_counter() - t1
+        seen = sum(min((r // kpf + 1) * kpf, T) for r in rows)
+        # per (row, key) pair the row variant forms S, dP and dQ: 6 d flops
+        out["cpu_baseline"] = {"value": 6 * d * len(heads) * seen / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": int(cores), "kind": "oracle",
+                               "sample": f"oracle.attn_bwd_rows (dQ) on {len(rows)} rows x "
+                                         f"{len(heads)} heads", "seconds": round(dt, 3)}
     print(json.dumps(out), flush=True)
 
 

@@ -8,6 +8,7 @@ failed build never leaves a half-written library behind.
 import os
 import subprocess
 import sys
+import shutil
 import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -24,7 +25,7 @@ def hipcc():
 
 def flags():
     return [
-        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # Packed fp32 VALU ops are kept out of every kernel.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
@@ -33,23 +34,37 @@ def flags():
     ]
 
 
-def build(verbose=False, extra_flags=(), out_path=LIB_PATH):
-    srcs = [os.path.join(HERE, "csrc", s) for s in SOURCES]
-    fd, tmp = tempfile.mkstemp(prefix=".librtr_attn.", suffix=".so.tmp", dir=os.path.dirname(out_path))
-    os.close(fd)
-    cmd = [hipcc()] + flags() + list(extra_flags) + srcs + ["-o", tmp]
+# Extra flags per source.  attn_bwd.hip: builtin MFMAs in VGPR form (their
+# results feed VALU code); its long-lived accumulators use AGPRs explicitly.
+SOURCE_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
+    if verbose and res.stderr.strip():
+        print(res.stderr, file=sys.stderr)
+
+
+def build(verbose=False, extra_flags=(), out_path=LIB_PATH):
+    """Compile every source to an object (with its own extra flags), link them
+    into one shared library, and move it into place."""
+    tmpdir = tempfile.mkdtemp(prefix=".librtr_build.", dir=os.path.dirname(out_path))
+    tmp = os.path.join(tmpdir, LIB_NAME)
     try:
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-        if verbose and res.stderr.strip():
-            print(res.stderr, file=sys.stderr)
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src + ".o")
+            _run([hipcc()] + flags() + list(SOURCE_FLAGS.get(src, [])) + list(extra_flags)
+                 + ["-c", os.path.join(HERE, "csrc", src), "-o", obj], verbose)
+            objs.append(obj)
+        _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
         os.replace(tmp, out_path)
     finally:
-        if os.path.exists(tmp):
-            os.unlink(tmp)
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return out_path
 
 
