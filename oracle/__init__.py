@@ -9,16 +9,18 @@ the pages' definitions.
 Sources (the pages are web notes on "DiT as Real-Time Rerenderer: Streaming
 Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
   * attention.py  -- Key Designs 2 ("Causal 3D attention for streaming
-    autoregression"), the Attn(Q,K,V) equation with the frame mask M.
+    autoregression"), the Attn(Q,K,V) equation with the frame mask M; and
+    attn_cross, the text cross-attention of Key Designs 1 (text encoded by
+    T5 and injected through cross attention), which has no mask.
   * attention_bwd.py -- gradients (dQ, dK, dV) of the Key Designs 2 equation,
     the pass that Key Designs 3's post-training back-propagates through.
   * listkv.py     -- Key Designs 4 ("Reference-preserving KV cache update and
     live style switching"), and Key Designs 1 for the reference as one extra
-    latent frame placed before the first frame.
+    latent frame placed before the first frame; its TextKV is the
+    cross-attention cache of the same section.
 
-Every function here is pinned by tests/test_oracle.py, tests/test_oracle_bwd.py and
-tests/test_listkv.py
-against things other than itself (brute-force loops, textbook special cases,
+Every function here is pinned by tests/test_oracle.py, tests/test_oracle_bwd.py,
+tests/test_oracle_cross.py and tests/test_listkv.py against things other than itself (brute-force loops, textbook special cases,
 closed forms and invariants).
 """
 
@@ -29,10 +31,11 @@ from .attention import (  # noqa: F401
     attn_rows,
     attn_stream_step,
     attn_stream_rows,
+    attn_cross,
 )
 from .attention_bwd import (  # noqa: F401
     attn_block_causal_bwd,
     attn_bwd_rows,
     attn_bwd_cols,
 )
-from .listkv import ListKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401
+from .listkv import ListKV, TextKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401

@@ -190,3 +190,22 @@ def attn_stream_rows(prefix_k, prefix_v, q, k, v, tokens_per_frame, rows, heads=
             o[b, a] = out[0]
             lse[a, b] = l[0]
     return o, lse
+
+
+def attn_cross(q, k_text, v_text, scale=None):
+    """Cross-attention of video tokens to text tokens (RTR-DiT notes, Key
+    Designs 1: text is encoded by T5 and injected through cross attention),
+    dense and literal:
+    softmax(Q K^T * scale) V with no mask -- every query sees every text token.
+
+    q: [Tq, H, d]; k_text, v_text: [Lt, H, d], Lt >= 1.
+    Returns (o [Tq, H, d], lse [H, Tq]).
+    """
+    q, kk, vv = _f64(q), _f64(k_text), _f64(v_text)
+    Tq, H, d = q.shape
+    sc = _default_scale(d, scale)
+    o = np.empty((Tq, H, d))
+    lse = np.empty((H, Tq))
+    for h in range(H):
+        o[:, h, :], lse[h] = _softmax_attend((q[:, h, :] @ kk[:, h, :].T) * sc, vv[:, h, :])
+    return o, lse

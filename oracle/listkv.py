@@ -96,3 +96,36 @@ class ListKV:
             return z, z.copy()
         return (np.concatenate([np.asarray(x).reshape(tokens_per_frame, H, d) for x in ks]),
                 np.concatenate([np.asarray(x).reshape(tokens_per_frame, H, d) for x in vs]))
+
+
+class TextKV:
+    """One layer's cross-attention cache (RTR-DiT notes, Key Designs 4): a
+    fixed-capacity cache initialised with the K/V of the current text
+    condition, reused by every chunk, and re-initialised (the old condition
+    discarded) when a new text prompt arrives.  Readings: the cache holds
+    exactly the current condition's tokens (no rolling: text does not grow
+    with the video); `set` replaces the whole content and counts a new
+    generation; `clear` leaves no condition, after which cross-attention has
+    nothing to attend to."""
+
+    def __init__(self, capacity_tokens):
+        if capacity_tokens < 1:
+            raise ValueError("capacity_tokens must be >= 1")
+        self.capacity = int(capacity_tokens)
+        self.k = None
+        self.v = None
+        self.generation = 0
+
+    def set(self, k_text, v_text):
+        """k_text, v_text: [n, H, d] with 1 <= n <= capacity."""
+        if len(k_text) != len(v_text) or not (1 <= len(k_text) <= self.capacity):
+            raise ValueError("text K/V must have the same length in [1, capacity]")
+        self.k = np.array(k_text, copy=True)
+        self.v = np.array(v_text, copy=True)
+        self.generation += 1
+
+    def clear(self):
+        self.k = self.v = None
+
+    def tokens(self):
+        return 0 if self.k is None else len(self.k)
