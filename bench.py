@@ -130,7 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan13b_stream_step",
                     choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal",
-                             "full_block_causal_bwd", "rollout"],
+                             "full_block_causal_bwd", "wan13b_cross_step", "rollout"],
                     help="rollout: one step is a whole 240-chunk rollout (stream step, commit, "
                          "and a reference swap every 60 chunks)")
     ap.add_argument("--cpu-heads", type=int, default=12,
@@ -158,6 +158,8 @@ def main():
         return rollout(args, w, dev)
     if args.workload == "full_block_causal_bwd":
         return backward(args, w, dev)
+    if args.workload == "wan13b_cross_step":
+        return cross(args, w, dev)
 
     def to_dev(t):
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -366,6 +368,104 @@ def backward(args, w, dev):
                                "cores": int(cores), "kind": "oracle",
                                "sample": f"oracle.attn_bwd_rows (dQ) on {len(rows)} rows x "
                                          f"{len(heads)} heads", "seconds": round(dt, 3)}
+    print(json.dumps(out), flush=True)
+
+
+def cross(args, w, dev):
+    """Text cross-attention of one chunk: one step is one rtr_attn_cross call of
+    the chunk's C*k query rows against the text cache's tokens (no mask).  The
+    cache reset of a text switch (copy of the new condition's K and V) is timed
+    separately and reported as `text_reset`."""
+    import torch
+    from causal_attention_frame_amd import inputs as gen
+    from causal_attention_frame_amd import rtr
+
+    H, d, Lt = w["H"], w["d"], w["text_tokens"]
+    Tq = w["C"] * w["k"]
+    x = gen.cross_inputs(Tq, Lt, H, d, "bf16", base_seed=0, wid=w["wid"])
+    q, kt, vt = (torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16) for t in x)
+    kb, vb = torch.empty_like(kt), torch.empty_like(vt)
+    tc = rtr.rtr_text_cache_create(kb, vb, Lt, H, d)
+    rtr.rtr_text_cache_reset(tc, kt, vt, Lt)
+    o = torch.empty_like(q)
+    ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
+    stream = torch.cuda.current_stream(dev)
+    flops = 4 * d * H * Tq * Lt
+
+    def step():
+        rtr.rtr_attn_cross(tc, q, o=o, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # text switch: re-initialise the cache with a condition of the same length
+    er = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in er:
+        a.record(stream)
+        rtr.rtr_text_cache_reset(tc, vt, kt, Lt)
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    reset_s = float(np.median([a.elapsed_time(b) for a, b in er])) * 1e-3
+    reset_bytes = 2 * 2 * Lt * H * d * 2
+    ms_per_step = elapsed * 1e3 / args.steps
+    call_s = float(call_ms.mean()) * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "wan13b_cross_step", "heads": H, "head_dim": d, "query_tokens": Tq,
+                   "text_tokens": Lt},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(flops / call_s / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_bf16_d128" + ("" if ws is None else " (+ split-K when planned)"),
+            "kernel_avg_us": round(call_s * 1e6, 2),
+            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
+        },
+        "text_reset": {"bound": "hbm", "median_us": round(reset_s * 1e6, 2),
+                       "achieved": round(reset_bytes / reset_s / 1e9, 1), "unit": "GB/s",
+                       "peak": PEAK_HBM_GBS, "algorithmic_bytes": reset_bytes},
+    }
+    tc.close()
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count()
+        heads = min(H, args.cpu_heads)
+        t1 = time.perf_counter()
+        oracle.attn_cross(x[0].values[:, :heads], x[1].values[:, :heads], x[2].values[:, :heads])
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": 4 * d * heads * Tq * Lt / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": int(cores), "kind": "oracle",
+                               "sample": f"oracle.attn_cross (dense float64) on heads 0..{heads - 1} of {H}",
+                               "seconds": round(dt, 3)}
     print(json.dumps(out), flush=True)
 
 

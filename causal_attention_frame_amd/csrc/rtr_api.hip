@@ -36,6 +36,15 @@ struct rtr_kv_cache {
     int64_t slot_frame_id[RTR_MAX_WINDOW];  // indexed by physical slot
 };
 
+// One layer's text cross-attention cache (host-side metadata over caller buffers).
+struct rtr_text_cache {
+    void *k_buf, *v_buf;
+    int32_t capacity, H, d;
+    rtr_dtype dt;
+    int32_t n;        // tokens of the current condition (0: none)
+    int64_t gen;      // conditions set so far
+};
+
 namespace {
 
 thread_local std::string g_err;
@@ -536,6 +545,132 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
     p.d = kv->d;
     p.scale = resolve_scale(scale, kv->d);
     p.in_dtype = kv->dt;
+    p.out_dtype = out_dtype;
+    const hipError_t e = rtr::launch_attention(p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int rtr_text_cache_create(rtr_text_cache **out, void *k_buf, void *v_buf, int32_t capacity_tokens,
+                          int32_t H, int32_t d, rtr_dtype dtype) {
+    if (!out) return fail(RTR_EINVAL, "out is NULL");
+    if (capacity_tokens < 1 || capacity_tokens > kMaxTokens)
+        return fail(RTR_EINVAL, "capacity_tokens=%d must be >= 1", capacity_tokens);
+    if (H < 1) return fail(RTR_EINVAL, "H must be >= 1");
+    if (!valid_dtype(dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (d != 64 && d != 128) return fail(RTR_EUNSUPPORTED, "head dim %d not supported (64, 128)", d);
+    if (!k_buf || !v_buf) return fail(RTR_EINVAL, "cache buffers must be non-NULL");
+    if (!aligned16(k_buf) || !aligned16(v_buf)) return fail(RTR_EINVAL, "cache buffers must be 16-byte aligned");
+    const int64_t nb = (int64_t)capacity_tokens * H * d * esize(dtype);
+    if (overlaps(k_buf, nb, v_buf, nb)) return fail(RTR_EINVAL, "cache buffers overlap");
+    rtr_text_cache *tc = new (std::nothrow) rtr_text_cache();
+    if (!tc) return fail(RTR_EINVAL, "out of host memory");
+    tc->k_buf = k_buf;
+    tc->v_buf = v_buf;
+    tc->capacity = capacity_tokens;
+    tc->H = H;
+    tc->d = d;
+    tc->dt = dtype;
+    tc->n = 0;
+    tc->gen = 0;
+    *out = tc;
+    return ok();
+}
+
+int rtr_text_cache_destroy(rtr_text_cache *tc) {
+    delete tc;
+    return ok();
+}
+
+int rtr_text_cache_reset(rtr_text_cache *tc, const void *k_text, const void *v_text, int32_t n_tokens,
+                         rtr_stream stream) {
+    if (!tc) return fail(RTR_EINVAL, "cache handle is NULL");
+    if (n_tokens < 0 || n_tokens > tc->capacity)
+        return fail(RTR_EINVAL, "n_tokens=%d outside [0, %d]", n_tokens, tc->capacity);
+    if ((k_text == nullptr) != (v_text == nullptr))
+        return fail(RTR_EINVAL, "k_text and v_text must both be NULL or both non-NULL");
+    if (n_tokens == 0) {
+        tc->n = 0;
+        return ok();
+    }
+    const int64_t tok_b = (int64_t)tc->H * tc->d * esize(tc->dt);
+    if (k_text && !(k_text == tc->k_buf && v_text == tc->v_buf)) {
+        if (!aligned16(k_text) || !aligned16(v_text)) return fail(RTR_EINVAL, "text pointers must be 16-byte aligned");
+        const int64_t nb = tok_b * n_tokens, cap_b = tok_b * tc->capacity;
+        for (const void *src : {k_text, v_text})
+            for (const void *dst : {tc->k_buf, tc->v_buf})
+                if (overlaps(src, nb, dst, cap_b)) return fail(RTR_EINVAL, "new text K/V overlaps the cache buffers");
+        rtr::CopyJobs jobs;
+        jobs.src[0] = k_text;
+        jobs.dst[0] = tc->k_buf;
+        jobs.src[1] = v_text;
+        jobs.dst[1] = tc->v_buf;
+        jobs.n = 2;
+        jobs.bytes = nb;
+        const hipError_t e = rtr::launch_frame_copies(jobs, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "text copy launch");
+    }
+    tc->n = n_tokens;
+    ++tc->gen;
+    return ok();
+}
+
+int rtr_text_cache_state(const rtr_text_cache *tc, int32_t *n_tokens, int64_t *generation) {
+    if (!tc) return fail(RTR_EINVAL, "cache handle is NULL");
+    if (n_tokens) *n_tokens = tc->n;
+    if (generation) *generation = tc->gen;
+    return ok();
+}
+
+int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse, int64_t Tq,
+                   rtr_dtype out_dtype, float scale, void *workspace, size_t workspace_bytes,
+                   rtr_stream stream) {
+    if (!tc) return fail(RTR_EINVAL, "cache handle is NULL");
+    if (Tq < 0 || Tq > kMaxTokens) return fail(RTR_EINVAL, "Tq=%lld out of range [0, 2^30]", (long long)Tq);
+    if (!valid_dtype(out_dtype)) return fail(RTR_EINVAL, "unknown dtype");
+    if (tc->dt == RTR_F32 && out_dtype != RTR_F32)
+        return fail(RTR_EUNSUPPORTED, "float32 cache needs float32 output");
+    if (int rc = check_scale(scale)) return rc;
+    if (tc->n == 0) return fail(RTR_ESTATE, "the text cache holds no condition");
+    if (Tq == 0) return ok();
+    if (!q || !o) return fail(RTR_EINVAL, "q and o must be non-NULL");
+    if (!aligned16(q) || !aligned16(o) || !aligned16(lse))
+        return fail(RTR_EINVAL, "device pointers must be 16-byte aligned");
+    const int64_t tok_in = (int64_t)tc->H * tc->d * esize(tc->dt);
+    const int64_t in_b = Tq * tok_in, cap_b = tok_in * tc->capacity;
+    const int64_t out_b = Tq * tc->H * tc->d * esize(out_dtype), lse_b = Tq * tc->H * 4;
+    const void *ins[3] = {q, tc->k_buf, tc->v_buf};
+    const int64_t in_sz[3] = {in_b, cap_b, cap_b};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(o, out_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "o overlaps q or the cache");
+        if (overlaps(lse, lse_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "lse overlaps q or the cache");
+    }
+    if (overlaps(lse, lse_b, o, out_b)) return fail(RTR_EINVAL, "lse overlaps o");
+    void *ws = nullptr;
+    {
+        const void *bufs[5] = {q, tc->k_buf, tc->v_buf, o, lse};
+        const int64_t sizes[5] = {in_b, cap_b, cap_b, out_b, lse ? lse_b : 0};
+        if (int rc = check_workspace(workspace, workspace_bytes, tc->d, tc->dt, bufs, sizes, 5, &ws)) return rc;
+    }
+    // Every query sees every text token: one key segment, all of it a prefix
+    // that no frame limit cuts.
+    rtr::AttnProblem p;
+    p.ws = ws;
+    p.q = q;
+    p.o = o;
+    p.lse = lse;
+    p.kseg[0] = tc->k_buf;
+    p.vseg[0] = tc->v_buf;
+    p.nseg = 1;
+    p.seg_len = tc->n;
+    p.Tq = Tq;
+    p.Tk = tc->n;
+    p.prefix = tc->n;
+    p.tokens_per_frame = Tq;
+    p.H = tc->H;
+    p.d = tc->d;
+    p.scale = resolve_scale(scale, tc->d);
+    p.in_dtype = tc->dt;
     p.out_dtype = out_dtype;
     const hipError_t e = rtr::launch_attention(p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");

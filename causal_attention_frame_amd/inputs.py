@@ -8,14 +8,14 @@ Recipe: every tensor is drawn in float32 from
 numpy.random.Generator(PCG64(SeedSequence([base_seed, workload_id, step, tag])))
 as N(0, 1) and, for bf16 workloads, rounded once to bfloat16 with
 round-to-nearest-even.  Tags: Q=0, K=1, V=2, reference K=3, reference V=4,
-outlier row pick=5, upstream gradient dO=6.  The optional outlier treatment multiplies exactly
+outlier row pick=5, upstream gradient dO=6, text K=7, text V=8.  The optional outlier treatment multiplies exactly
 round(frac * rows) distinct (token, head) rows of a K tensor by a power of two
 (exact in bfloat16, so it commutes with the rounding).
 """
 
 import numpy as np
 
-TAG_Q, TAG_K, TAG_V, TAG_REFK, TAG_REFV, TAG_OUTLIER, TAG_DO = 0, 1, 2, 3, 4, 5, 6
+TAG_Q, TAG_K, TAG_V, TAG_REFK, TAG_REFV, TAG_OUTLIER, TAG_DO, TAG_TEXTK, TAG_TEXTV = range(9)
 
 # Shapes of the synthetic workloads (Wan-DiT-shaped attention layers).
 WORKLOADS = {
@@ -25,6 +25,7 @@ WORKLOADS = {
     "full_block_causal": dict(wid=3, H=12, d=128, k=1560, frames=22, dtype="bf16"),
     "rollout": dict(wid=4, H=12, d=128, k=1560, C=3, W=6, R=1, chunks=240,
                     swap_every=60, dtype="bf16"),
+    "wan13b_cross_step": dict(wid=7, H=12, d=128, k=1560, C=3, text_tokens=512, dtype="bf16"),
     "full_block_causal_bwd": dict(wid=6, H=12, d=128, k=1560, frames=22, dtype="bf16"),
     "wan14b_stream_step": dict(wid=5, H=40, d=128, k=1560, C=3, W=9, R=1, dtype="bf16",
                                outlier_frac=0.01, outlier_scale=8.0),
@@ -109,6 +110,13 @@ def bwd_inputs(T, H, d, dtype, base_seed=0, wid=0, step=0):
     """Q, K, V of a full sequence plus an upstream gradient dO, all [T, H, d]."""
     return (full_sequence_inputs(T, H, d, dtype, base_seed, wid, step)
             + (normal((T, H, d), dtype, base_seed, wid, step, TAG_DO),))
+
+
+def cross_inputs(Tq, Lt, H, d, dtype, base_seed=0, wid=0, step=0):
+    """Queries [Tq, H, d] and one text condition's K, V [Lt, H, d]."""
+    return (normal((Tq, H, d), dtype, base_seed, wid, step, TAG_Q),
+            normal((Lt, H, d), dtype, base_seed, wid, step, TAG_TEXTK),
+            normal((Lt, H, d), dtype, base_seed, wid, step, TAG_TEXTV))
 
 
 def stream_inputs(k, H, d, C, W, R, dtype, base_seed=0, wid=0, step=0, outlier_frac=0.0,

@@ -62,6 +62,13 @@ _SIGNATURES = {
     "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
     "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
     "rtr_kv_set_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
+    "rtr_text_cache_create": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                             ctypes.c_int]),
+    "rtr_text_cache_destroy": (ctypes.c_int, [_vp]),
+    "rtr_text_cache_reset": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp]),
+    "rtr_text_cache_state": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64)]),
+    "rtr_attn_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, ctypes.c_int, _c_f32, _vp,
+                                      ctypes.c_size_t, _vp]),
     "rtr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rtr_last_error": (ctypes.c_char_p, []),
     "rtr_version": (ctypes.c_int, []),
@@ -295,6 +302,66 @@ def rtr_kv_get_state(kv):
 
 def rtr_kv_set_state(kv, st):
     _check(lib().rtr_kv_set_state(kv.handle, ctypes.byref(st)), "rtr_kv_set_state")
+
+
+# ---------------------------------------------------------------- text cross-attention
+class TextCache:
+    """One layer's text cross-attention cache (handle + buffers [capacity, H, d])."""
+
+    def __init__(self, k_buf, v_buf, capacity_tokens, H, d, dtype):
+        self._bufs = (k_buf, v_buf)
+        self.capacity, self.H, self.d, self.dtype = capacity_tokens, H, d, dtype
+        h = _vp()
+        _check(lib().rtr_text_cache_create(ctypes.byref(h), _ptr(k_buf), _ptr(v_buf), capacity_tokens,
+                                           H, d, dtype), "rtr_text_cache_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().rtr_text_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rtr_text_cache_create(k_buf, v_buf, capacity_tokens, H, d, dtype=RTR_BF16):
+    return TextCache(k_buf, v_buf, capacity_tokens, H, d, dtype)
+
+
+def rtr_text_cache_reset(tc, k_text, v_text, n_tokens, stream=None):
+    dev = k_text.device if k_text is not None else tc._bufs[0].device
+    _check(lib().rtr_text_cache_reset(tc.handle, _ptr(k_text), _ptr(v_text), int(n_tokens),
+                                      _stream(stream, dev)), "rtr_text_cache_reset")
+
+
+def rtr_text_cache_state(tc):
+    n, g = _c_i32(0), _c_i64(0)
+    _check(lib().rtr_text_cache_state(tc.handle, ctypes.byref(n), ctypes.byref(g)), "rtr_text_cache_state")
+    return n.value, g.value
+
+
+def rtr_attn_cross(tc, q, o=None, lse=None, scale=0.0, out_dtype=None, want_lse=False, workspace=None,
+                   stream=None):
+    """Cross-attention of q [Tq, H, d] to the cache's text tokens.  Returns (o, lse or None)."""
+    import torch
+    Tq, H, d = q.shape
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((Tq, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().rtr_attn_cross(tc.handle, _ptr(q), _ptr(o), _ptr(lse), Tq, _dtype_code(o), float(scale), ws,
+                                ws_bytes, _stream(stream, q.device)), "rtr_attn_cross")
+    return o, lse
 
 
 def rtr_version():

@@ -214,6 +214,43 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
 int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, const void *v_ref,
                      int32_t ref_frames, int32_t keep_recent, rtr_stream stream);
 
+/* ------------------------------------------------------------------------
+ * Text cross-attention and its cache (Key Designs 1: text is encoded by T5 and
+ * injected through cross attention; Key Designs 4: a fixed-length
+ * cross-attention cache is initialised and, when a new text prompt arrives,
+ * re-initialised so that the old condition is discarded).  The cache holds
+ * the K/V of the current text condition for one layer, [n, H, d] with
+ * 1 <= n <= capacity, in caller-owned device buffers k_buf, v_buf of
+ * [capacity, H, d]; every chunk's queries attend to all n tokens (no mask):
+ *   O = softmax(Q K_text^T * scale) V_text.
+ * A reference-only switch leaves this cache untouched; a text switch resets
+ * it (and, on the 3D cache, calls rtr_kv_reset_ref with RTR_REF_KEEP).
+ * ---------------------------------------------------------------------- */
+typedef struct rtr_text_cache rtr_text_cache; /* opaque, host-side metadata */
+
+int rtr_text_cache_create(rtr_text_cache **out, void *k_buf, void *v_buf, int32_t capacity_tokens,
+                          int32_t H, int32_t d, rtr_dtype dtype);
+int rtr_text_cache_destroy(rtr_text_cache *tc);
+
+/* Re-initialise with a new condition of n_tokens (1..capacity) tokens:
+ * k_text, v_text are [n_tokens, H, d] device buffers copied into the cache on
+ * `stream` (both NULL: the caller already wrote them into k_buf/v_buf).
+ * n_tokens == 0 clears the cache (no condition).  Increments the generation
+ * whenever a condition is set. */
+int rtr_text_cache_reset(rtr_text_cache *tc, const void *k_text, const void *v_text,
+                         int32_t n_tokens, rtr_stream stream);
+
+/* Current token count and generation. */
+int rtr_text_cache_state(const rtr_text_cache *tc, int32_t *n_tokens, int64_t *generation);
+
+/* Cross-attention of Tq query rows ([Tq, H, d], the cache's dtype) to the
+ * cache's tokens: o [Tq, H, d] out_dtype, lse [H, Tq] float32 or NULL,
+ * scale <= 0 selects 1/sqrt(d), workspace as for rtr_attn_block_causal.
+ * An empty cache is RTR_ESTATE. */
+int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse, int64_t Tq,
+                   rtr_dtype out_dtype, float scale, void *workspace, size_t workspace_bytes,
+                   rtr_stream stream);
+
 /* Metadata snapshot / restore (checkpoint-resume).  set_state validates the
  * snapshot against the cache's W and R_cap and changes nothing on error. */
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out);

@@ -290,3 +290,42 @@ def test_bwd_workspace_size():
     assert rtr.rtr_attn_bwd_workspace_size(0, 3, 128) == 0
     with pytest.raises(rtr.RtrError):
         rtr.rtr_attn_bwd_workspace_size(100, 3, 64)
+
+
+def test_text_cache_metadata_and_rejections():
+    """Host-side text cache: state changes without touching the device (the
+    caller-wrote-it form of reset, and clear) and argument checks."""
+    L = rtr.lib()
+    h = ctypes.c_void_p()
+    assert L.rtr_text_cache_create(ctypes.byref(h), FAKE, FAKE + MB, 0, 2, 128, rtr.RTR_BF16) == rtr.RTR_EINVAL
+    assert L.rtr_text_cache_create(ctypes.byref(h), FAKE, FAKE + 64, 16, 2, 128, rtr.RTR_BF16) == rtr.RTR_EINVAL
+    assert L.rtr_text_cache_create(ctypes.byref(h), FAKE, FAKE + MB, 16, 2, 96, rtr.RTR_BF16) == rtr.RTR_EUNSUPPORTED
+    assert L.rtr_text_cache_create(ctypes.byref(h), FAKE, FAKE + MB, 16, 2, 128, rtr.RTR_BF16) == rtr.RTR_OK
+    n, g = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    assert L.rtr_text_cache_state(h, ctypes.byref(n), ctypes.byref(g)) == 0 and (n.value, g.value) == (0, 0)
+    # an empty cache has nothing to attend to
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 3 * MB, None, 8, rtr.RTR_BF16, 0.0, None, 0,
+                            None) == rtr.RTR_ESTATE
+    # the caller wrote the condition into the cache buffers itself: no copy
+    assert L.rtr_text_cache_reset(h, None, None, 12, None) == rtr.RTR_OK
+    assert L.rtr_text_cache_reset(h, FAKE, FAKE + MB, 12, None) == rtr.RTR_OK   # same buffers: no copy
+    assert L.rtr_text_cache_state(h, ctypes.byref(n), ctypes.byref(g)) == 0 and (n.value, g.value) == (12, 2)
+    assert L.rtr_text_cache_reset(h, None, None, 17, None) == rtr.RTR_EINVAL    # over capacity
+    assert L.rtr_text_cache_reset(h, FAKE + 2 * MB, None, 4, None) == rtr.RTR_EINVAL
+    assert L.rtr_text_cache_reset(h, FAKE + 8, FAKE + 2 * MB, 4, None) == rtr.RTR_EINVAL  # overlaps the cache
+    assert L.rtr_text_cache_state(h, ctypes.byref(n), ctypes.byref(g)) == 0 and (n.value, g.value) == (12, 2)
+    # cross-attention argument checks
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 2 * MB + 64, None, 8, rtr.RTR_BF16, 0.0, None, 0,
+                            None) == rtr.RTR_EINVAL       # o overlaps q
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 8, None, 8, rtr.RTR_BF16, 0.0, None, 0,
+                            None) == rtr.RTR_EINVAL       # o overlaps the cache (and misaligned)
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 3 * MB, None, -1, rtr.RTR_BF16, 0.0, None, 0,
+                            None) == rtr.RTR_EINVAL
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 3 * MB, None, 8, rtr.RTR_BF16, float("inf"), None, 0,
+                            None) == rtr.RTR_EINVAL
+    assert L.rtr_attn_cross(h, FAKE + 2 * MB, FAKE + 3 * MB, None, 0, rtr.RTR_BF16, 0.0, None, 0,
+                            None) == rtr.RTR_OK           # no rows: no-op
+    # clear
+    assert L.rtr_text_cache_reset(h, None, None, 0, None) == rtr.RTR_OK
+    assert L.rtr_text_cache_state(h, ctypes.byref(n), ctypes.byref(g)) == 0 and (n.value, g.value) == (0, 2)
+    assert L.rtr_text_cache_destroy(h) == rtr.RTR_OK
