@@ -34,15 +34,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_{workload}.txt")
 CSRC = os.path.join(ROOT, "causal_attention_frame_amd", "csrc")
 # Sources whose code the counter runs of a workload depend on.
 KERNEL_SRCS = {
-    "forward": [os.path.join(CSRC, "attn_fwd.hip")],
+    "forward": [os.path.join(CSRC, "attn_fwd.hip"), os.path.join(CSRC, "device_util.h")],
     "backward": [os.path.join(CSRC, "attn_bwd.hip"), os.path.join(CSRC, "device_util.h")],
 }
 
 
-def stream_pairs_per_head(kpf, C, prefix_frames):
+def stream_pairs_per_head(kpf, C, prefix_frames, block_frames=1):
     """Visible (query, key) pairs of one head in a streaming step: chunk frame c
-    sees the prefix frames and chunk frames 0..c."""
-    return sum(kpf * (prefix_frames * kpf + (c + 1) * kpf) for c in range(C))
+    sees the prefix frames and the chunk frames of its mask block and earlier
+    blocks (blocks of block_frames frames; 1 = the per-frame mask)."""
+    B = max(1, min(block_frames, C))
+    return sum(kpf * (prefix_frames * kpf + min((c // B + 1) * B, C) * kpf) for c in range(C))
 
 
 def full_pairs_per_head(T, kpf):
@@ -107,7 +109,7 @@ def cpu_baseline(workload, x, w, heads):
         t0 = time.perf_counter()
         oracle.attn_stream_step(*args)
         dt = time.perf_counter() - t0
-        flops = 4 * d * heads * stream_pairs_per_head(kpf, w["C"], w["R"] + w["W"])
+        flops = 4 * d * heads * stream_pairs_per_head(kpf, w["C"], x["ref_k"].shape[0] + w["W"])
         sample = (f"oracle.attn_stream_step (dense float64) on heads 0..{heads - 1} of {H}, "
                   f"all {w['C'] * kpf} query rows")
     else:
@@ -136,6 +138,11 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ref-frames", type=int, default=0,
+                    help="streaming workloads: anchored reference frames (default: the workload's)")
+    ap.add_argument("--block-frames", type=int, default=1,
+                    help="streaming workloads: frames per in-chunk mask block (chunk-level causality "
+                         "with the chunk length; default 1, the per-frame mask)")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -168,7 +175,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
     if args.workload.endswith("stream_step"):
-        C, W, R = w["C"], w["W"], w["R"]
+        C, W, R = w["C"], w["W"], (args.ref_frames or w["R"])
         x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"],
                               outlier_frac=w.get("outlier_frac", 0.0),
                               outlier_scale=w.get("outlier_scale", 1.0))
@@ -182,14 +189,19 @@ def main():
         q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
         o = torch.empty_like(q)
         frames = C
-        flops = 4 * d * H * stream_pairs_per_head(kpf, C, R + W)
+        flops = 4 * d * H * stream_pairs_per_head(kpf, C, R + W, args.block_frames)
         append_bytes = 2 * 2 * C * kpf * H * d * 2     # K and V, read + write
         config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
                   "chunk_frames": C, "window_frames": W, "ref_frames": R,
                   "query_tokens": C * kpf, "key_tokens": (R + W + C) * kpf}
+        if args.block_frames != 1:
+            config["mask_block_frames"] = args.block_frames
 
         def attention():
-            rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o, workspace=ws)
+            if args.block_frames == 1:
+                rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o, workspace=ws)
+            else:
+                rtr.rtr_attn_stream_step_blocked(kv, q, k, v, C, args.block_frames, o=o, workspace=ws)
 
         def commit():
             rtr.rtr_kv_append_evict(kv, k, v, C)

@@ -34,18 +34,13 @@
 #include <cstddef>
 #include <type_traits>
 
+#include "device_util.h"
 #include "rtr_internal.h"
 
 namespace rtr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
+using namespace dev;
 
 struct KArgs {
     const void *q;
@@ -76,33 +71,6 @@ struct KArgs {
     int32_t tail_total;
     int32_t piece;
 };
-
-// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2,
-// and an XCD starts its workgroups in index order as compute units free up.
-// Every XCD gets one contiguous head-major range of work items (head, query
-// block) so the query blocks of one head (which read the same K/V) share an
-// L2, and runs that range by query block, latest (most keys) first, across
-// its heads: longest work first, so no long block starts late.
-__device__ inline void map_block(int b, int nwg, int nqb, int &head, int &qb) {
-    const int x = b & 7, i = b >> 3;
-    const int q8 = nwg >> 3, r8 = nwg & 7;
-    const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
-    int rem = i;
-    head = lo / nqb;
-    qb = lo - head * nqb;  // not reached for a valid b
-    for (int q = nqb - 1; q >= 0; --q) {
-        if (hi - 1 - q < 0) continue;
-        const int hmin = lo - q > 0 ? (lo - q + nqb - 1) / nqb : 0;  // first head with unit (h, q) >= lo
-        const int hmax = (hi - 1 - q) / nqb;                          // last head with unit (h, q) < hi
-        const int cnt = hmax >= hmin ? hmax - hmin + 1 : 0;
-        if (rem < cnt) {
-            head = hmin + rem;
-            qb = q;
-            return;
-        }
-        rem -= cnt;
-    }
-}
 
 __device__ inline int key_limit(int i, const KArgs &a) {
     const int f = i / a.kpf;
@@ -139,11 +107,6 @@ __device__ inline float pair_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
-
-// 16-byte load through a global (not flat) address.
-__device__ inline u32x4 gload16(const uint16_t *p) { return *(const global_u32x4 *)p; }
 
 // Key addressing modes of the bf16 kernel.
 enum SegMode : int {
@@ -192,7 +155,7 @@ void attn_fwd_bf16(const KArgs a) {
     const int n = lane & 31, g = lane >> 5;
 
     int head, qb;
-    map_block(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
 
@@ -451,39 +414,13 @@ void attn_fwd_bf16(const KArgs a) {
 // this way it is invisible to that model, the fragment reads get exact
 // lgkmcnt waits, and the kernel waits for the DMA itself (vmcnt, in order).
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint16_t lds_u16;
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // A zero key/value row: keys past the end of a ragged key range are loaded from it.
 __device__ __attribute__((aligned(16))) const uint16_t kZeroRow[128] = {};
 
-__device__ inline uint32_t lds_addr(const lds_u16 *p) { return (uint32_t)(uintptr_t)p; }
-
-__device__ inline v4i16 lds_tr16(const lds_u16 *p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
-}
-
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber is still honoured
-// Two DMA loads (the K and the V row group of a tile), each 16 bytes per lane
-// from global memory to LDS byte address m0 + 16 * lane; source: a wave-uniform
-// 64-bit base in SGPRs plus a per-lane 32-bit offset.  The s_nop 4 covers the
-// wait states after an m0 write and after a VALU write of an SGPR that a vector
-// memory instruction reads (every SGPR operand is written before the
-// statement, so one guard covers both loads); the second m0 write needs one.
-__device__ inline void dma16x2_sbase(uint64_t kb, uint64_t vb, uint32_t ko, uint32_t vo, uint32_t mk, uint32_t mv) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %4\n\t"
-        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %5"
-        :
-        : "v"(ko), "v"(vo), "s"(mk), "s"(mv), "s"(kb), "s"(vb)
-        : "memory", "m0");
-}
 // One DMA load from a per-lane 64-bit address.
 __device__ inline void dma16_vaddr(const void *src, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
@@ -510,13 +447,7 @@ __device__ inline SegPtrs load_seg_ptrs(int f) {
     return {k[0], k[1], v[0], v[1]};
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
-constexpr int kWaitVm2 = 0x0F72;    // vmcnt(2): all but this wave's 2 newest loads done
-constexpr int kWaitVm4 = 0x0F74;    // vmcnt(4)
-constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 
-__device__ inline void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // DMA addressing of the head_dim-128 kernel.
 enum DmaMode : int {
@@ -555,7 +486,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     const int n = lane & 31, g = lane >> 5;
 
     int head, qb;
-    map_block(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
 
@@ -628,7 +559,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             const bool nxt = row >= a.seg_len;
             const long rr = nxt ? row - a.seg_len : row;
             const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-            dma16x2_sbase((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
+            dma16x2((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
                           m0v(st, 0));
             co += BN;
             if (co >= a.seg_len) {
@@ -770,7 +701,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
         load_ptrs();  // segment pointers of tile t + 3
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        __builtin_amdgcn_s_waitcnt(wait_vm(2));
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
@@ -831,7 +762,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         issue(1, I1{});
         load_ptrs();
         issue(2, I2{});
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile 0 landed
+        __builtin_amdgcn_s_waitcnt(wait_vm(4));  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -878,7 +809,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             step(base + 4, I4{}, std::true_type{}, maxonly);
         }
         // drain the look-ahead tiles before the stages are reused
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
         compiler_fence();
     };
 
@@ -1098,7 +1029,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
             const bool nxt = row >= a.seg_len;
             const long rr = nxt ? row - a.seg_len : row;
             const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-            dma16x2_sbase((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
+            dma16x2((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
                           m0v(st, 0));
             co += BN;
             if (co >= a.seg_len) {
@@ -1237,7 +1168,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
         load_ptrs();  // segment pointers of tile t + 3
-        __builtin_amdgcn_s_waitcnt(kWaitVm2);
+        __builtin_amdgcn_s_waitcnt(wait_vm(2));
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
@@ -1298,7 +1229,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         issue(tb + 1, I1{});
         load_ptrs();
         issue(tb + 2, I2{});
-        __builtin_amdgcn_s_waitcnt(kWaitVm4);  // tile 0 landed
+        __builtin_amdgcn_s_waitcnt(wait_vm(4));  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -1348,7 +1279,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
             step(base + 4, I4{}, std::true_type{}, maxonly);
         }
         // drain the look-ahead tiles before the stages are reused
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
         compiler_fence();
     };
 
@@ -1550,7 +1481,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(const KArgs a) {
 
     const int tid = threadIdx.x;
     int head, qb;
-    map_block(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
     const int qi = q0 + tid;

@@ -486,9 +486,19 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
                          float scale, void *workspace, size_t workspace_bytes,
                          rtr_stream stream) {
+    return rtr_attn_stream_step_blocked(kv, q, k, v, o, lse, chunk_frames, 1, out_dtype, scale, workspace,
+                                        workspace_bytes, stream);
+}
+
+int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                                 void *o, float *lse, int32_t chunk_frames, int32_t block_frames,
+                                 rtr_dtype out_dtype, float scale, void *workspace,
+                                 size_t workspace_bytes, rtr_stream stream) {
     if (int rc = check_cache(kv)) return rc;
     if (chunk_frames < 1 || chunk_frames > RTR_MAX_CHUNK)
         return fail(RTR_EUNSUPPORTED, "chunk_frames=%d outside [1, %d]", chunk_frames, RTR_MAX_CHUNK);
+    if (block_frames < 1) return fail(RTR_EINVAL, "block_frames=%d must be >= 1", block_frames);
+    const int32_t mask_frames = block_frames < chunk_frames ? block_frames : chunk_frames;
     if (!valid_dtype(out_dtype)) return fail(RTR_EINVAL, "unknown dtype");
     if (kv->dt == RTR_F32 && out_dtype != RTR_F32)
         return fail(RTR_EUNSUPPORTED, "float32 cache needs float32 output");
@@ -540,7 +550,7 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
     p.Tq = Tq;
     p.prefix = (int64_t)(kv->ref_frames + kv->count) * kv->kpf;
     p.Tk = p.prefix + Tq;
-    p.tokens_per_frame = kv->kpf;
+    p.tokens_per_frame = (int64_t)mask_frames * kv->kpf;  // mask unit; segments stay one frame
     p.H = kv->H;
     p.d = kv->d;
     p.scale = resolve_scale(scale, kv->d);

@@ -16,7 +16,7 @@ from .build import LIB_PATH
 RTR_OK, RTR_EINVAL, RTR_EUNSUPPORTED, RTR_EHIP, RTR_ESTATE = 0, -1, -2, -3, -4
 RTR_BF16, RTR_F32 = 0, 1
 RTR_REF_KEEP, RTR_REF_REPLACE, RTR_REF_CLEAR = 0, 1, 2
-RTR_MAX_WINDOW, RTR_MAX_REF, RTR_MAX_CHUNK = 64, 1, 16
+RTR_MAX_WINDOW, RTR_MAX_REF, RTR_MAX_CHUNK = 64, 4, 16
 
 _c_i32, _c_i64, _c_f32, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 
@@ -59,6 +59,8 @@ _SIGNATURES = {
     "rtr_kv_commit_inplace": (ctypes.c_int, [_vp, _c_i32]),
     "rtr_attn_stream_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, ctypes.c_int,
                                             _c_f32, _vp, ctypes.c_size_t, _vp]),
+    "rtr_attn_stream_step_blocked": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                                    ctypes.c_int, _c_f32, _vp, ctypes.c_size_t, _vp]),
     "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
     "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
     "rtr_kv_set_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
@@ -284,6 +286,25 @@ def rtr_attn_stream_step(kv, q, k, v, chunk_frames, o=None, lse=None, scale=0.0,
                                       int(chunk_frames), _dtype_code(o), float(scale), ws, ws_bytes,
                                       _stream(stream, q.device)),
            "rtr_attn_stream_step")
+    return o, lse
+
+
+def rtr_attn_stream_step_blocked(kv, q, k, v, chunk_frames, block_frames, o=None, lse=None, scale=0.0,
+                                 out_dtype=None, want_lse=False, workspace=None, stream=None):
+    """A streaming step whose in-chunk mask works in blocks of `block_frames`
+    frames (chunk-level causality).  Returns (o, lse or None)."""
+    import torch
+    Tq, H, d = q.shape
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((Tq, H, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().rtr_attn_stream_step_blocked(kv.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                              int(chunk_frames), int(block_frames), _dtype_code(o),
+                                              float(scale), ws, ws_bytes, _stream(stream, q.device)),
+           "rtr_attn_stream_step_blocked")
     return o, lse
 
 

@@ -62,7 +62,7 @@ typedef enum {
 typedef void *rtr_stream; /* hipStream_t */
 
 #define RTR_MAX_WINDOW 64 /* window frames W */
-#define RTR_MAX_REF 1     /* reference frames R */
+#define RTR_MAX_REF 4     /* reference frames R (several anchored style references) */
 #define RTR_MAX_CHUNK 16  /* frames per streaming chunk C */
 
 typedef struct rtr_kv_cache rtr_kv_cache; /* opaque, host-side ring metadata */
@@ -203,6 +203,18 @@ int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, c
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
                          float scale, void *workspace, size_t workspace_bytes,
                          rtr_stream stream);
+
+/* The same step with a coarser mask inside the chunk (chunk-level causality:
+ * fixed-size chunks whose tokens see each other and every earlier token).  The
+ * chunk's frames form blocks of block_frames frames; query row r sees every
+ * cached key and the chunk keys of blocks <= its own, i.e. the frame mask with
+ * block_frames * k tokens as its unit.  block_frames == 1 is
+ * rtr_attn_stream_step; block_frames >= chunk_frames makes the whole chunk
+ * mutually visible.  Other arguments and errors as rtr_attn_stream_step. */
+int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                                 void *o, float *lse, int32_t chunk_frames, int32_t block_frames,
+                                 rtr_dtype out_dtype, float scale, void *workspace,
+                                 size_t workspace_bytes, rtr_stream stream);
 
 /* Condition switch (Key Designs 4).  First the reference: KEEP leaves it,
  * REPLACE anchors ref_frames (1..R_cap) new frames k_ref, v_ref

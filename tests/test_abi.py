@@ -104,7 +104,7 @@ def _cache(W=4, R=1, kpf=8, H=2, d=64, dtype=rtr.RTR_BF16):
 @pytest.mark.parametrize("args,code", [
     (dict(W=-1), rtr.RTR_EUNSUPPORTED),
     (dict(W=rtr.RTR_MAX_WINDOW + 1), rtr.RTR_EUNSUPPORTED),
-    (dict(R=2), rtr.RTR_EUNSUPPORTED),
+    (dict(R=rtr.RTR_MAX_REF + 1), rtr.RTR_EUNSUPPORTED),
     (dict(kpf=0), rtr.RTR_EINVAL),
     (dict(d=80), rtr.RTR_EUNSUPPORTED),
 ])
@@ -146,6 +146,9 @@ def test_failed_calls_change_nothing():
     assert L.rtr_attn_stream_step(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
                                   FAKE + 903 * MB, None, 1, 0, 0.0, FAKE + 1024, MB,
                                   None) == rtr.RTR_EINVAL  # workspace over the ring
+    assert L.rtr_attn_stream_step_blocked(h, FAKE + 900 * MB, FAKE + 901 * MB, FAKE + 902 * MB,
+                                          FAKE + 903 * MB, None, 1, 0, 0, 0.0, None, 0,
+                                          None) == rtr.RTR_EINVAL  # block_frames 0
     assert L.rtr_attn_stream_step(h, None, FAKE + 901 * MB, FAKE + 902 * MB,
                                   FAKE + 903 * MB, None, 1, 0, 0.0, None, 0, None) == rtr.RTR_EINVAL
     assert L.rtr_attn_stream_step(None, FAKE, FAKE, FAKE, FAKE, None, 1, 0, 0.0,
