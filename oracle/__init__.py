@@ -12,6 +12,8 @@ Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
     autoregression"), the Attn(Q,K,V) equation with the frame mask M; and
     attn_cross, the text cross-attention of Key Designs 1 (text encoded by
     T5 and injected through cross attention), which has no mask.
+  * rope.py       -- temporal rotary encoding and the position of the anchored
+    reference in front of the rolling window (position-aware cache).
   * attention_bwd.py -- gradients (dQ, dK, dV) of the Key Designs 2 equation,
     the pass that Key Designs 3's post-training back-propagates through.
   * listkv.py     -- Key Designs 4 ("Reference-preserving KV cache update and
@@ -20,7 +22,8 @@ Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
     cross-attention cache of the same section.
 
 Every function here is pinned by tests/test_oracle.py, tests/test_oracle_bwd.py,
-tests/test_oracle_cross.py and tests/test_listkv.py against things other than itself (brute-force loops, textbook special cases,
+tests/test_oracle_cross.py, tests/test_oracle_blocks.py,
+tests/test_oracle_rope.py and tests/test_listkv.py against things other than itself (brute-force loops, textbook special cases,
 closed forms and invariants).
 """
 
@@ -38,4 +41,5 @@ from .attention_bwd import (  # noqa: F401
     attn_bwd_rows,
     attn_bwd_cols,
 )
+from .rope import rope_rotate, reference_shift  # noqa: F401
 from .listkv import ListKV, TextKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401
