@@ -143,6 +143,9 @@ def main():
     ap.add_argument("--block-frames", type=int, default=1,
                     help="streaming workloads: frames per in-chunk mask block (chunk-level causality "
                          "with the chunk length; default 1, the per-frame mask)")
+    ap.add_argument("--ref-rope", action="store_true",
+                    help="streaming workloads: position-aware reference (re-encoded in front of the "
+                         "window every step; 22 temporal rotary pairs, as Wan's 44 temporal dims)")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -184,6 +187,8 @@ def main():
         kf = torch.empty((R, kpf, H, d), dtype=torch.bfloat16, device=dev)
         vf = torch.empty_like(kf)
         kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+        if args.ref_rope:
+            rtr.rtr_kv_set_ref_rope(kv, torch.empty_like(kf), 22, 10000.0, R)
         rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, to_dev(x["ref_k"]), to_dev(x["ref_v"]), R, -1)
         rtr.rtr_kv_append_evict(kv, to_dev(x["ring_k"]), to_dev(x["ring_v"]), W)
         q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
@@ -196,6 +201,8 @@ def main():
                   "query_tokens": C * kpf, "key_tokens": (R + W + C) * kpf}
         if args.block_frames != 1:
             config["mask_block_frames"] = args.block_frames
+        if args.ref_rope:
+            config["position_aware_reference"] = True
 
         def attention():
             if args.block_frames == 1:

@@ -6,6 +6,8 @@
 // that are contiguous across the workgroup, and each thread keeps four loads in
 // flight before its stores.
 
+#include <cmath>
+
 #include "rtr_internal.h"
 
 namespace rtr {
@@ -40,7 +42,85 @@ __global__ __launch_bounds__(kThreads) void frame_copy(const CopyArgs a) {
     }
 }
 
+// Temporal rotary re-encoding of the anchored reference's K (position-aware
+// cache): element pairs (2i, 2i+1), i < pairs, of every head row rotated by
+// the angle whose cosine and sine the host computed for this shift; the other
+// elements are copied.  One thread per 8 elements (16 bytes of bf16).
+struct RotateArgs {
+    const uint16_t *src;
+    uint16_t *dst;
+    int64_t n8;      // 8-element groups in all
+    int32_t d8;      // 8-element groups per head row
+    int32_t pairs;
+    float cs[64], sn[64];
+};
+
+__global__ __launch_bounds__(kThreads) void ref_rotate_bf16(const RotateArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= a.n8) return;
+    const u32x4 v = ((const u32x4 *)a.src)[i];
+    const int p0 = (int)(i % a.d8) * 4;  // first pair of this group
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int p = p0 + w;
+        if (p < a.pairs) {
+            const float x0 = __uint_as_float(v[w] << 16), x1 = __uint_as_float(v[w] & 0xFFFF0000u);
+            const float y0 = x0 * a.cs[p] - x1 * a.sn[p], y1 = x0 * a.sn[p] + x1 * a.cs[p];
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            o[w] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)y0, (__bf16)y1});
+        } else {
+            o[w] = v[w];
+        }
+    }
+    ((u32x4 *)a.dst)[i] = o;
+}
+
+__global__ __launch_bounds__(kThreads) void ref_rotate_f32(const RotateArgs a) {
+    // float32 cache: one thread per 4 elements (two pairs), n8 counts them.
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= a.n8) return;
+    const u32x4 v = ((const u32x4 *)a.src)[i];
+    const int p0 = (int)(i % a.d8) * 2;
+    u32x4 o = v;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const int p = p0 + w;
+        if (p < a.pairs) {
+            const float x0 = __uint_as_float(v[2 * w]), x1 = __uint_as_float(v[2 * w + 1]);
+            o[2 * w] = __float_as_uint(x0 * a.cs[p] - x1 * a.sn[p]);
+            o[2 * w + 1] = __float_as_uint(x0 * a.sn[p] + x1 * a.cs[p]);
+        }
+    }
+    ((u32x4 *)a.dst)[i] = o;
+}
+
 }  // namespace
+
+hipError_t launch_ref_rotate(const RotateJob &j, hipStream_t stream) {
+    if (j.rows <= 0) return hipSuccess;
+    RotateArgs a{};
+    a.src = (const uint16_t *)j.src;
+    a.dst = (uint16_t *)j.dst;
+    a.pairs = j.pairs;
+    const double two_pi = 6.283185307179586;
+    for (int p = 0; p < j.pairs && p < 64; ++p) {
+        // angle = shift * base^(-p / pairs), reduced in double before the float cast
+        double ang = (double)j.shift * std::pow((double)j.base, -(double)p / j.pairs);
+        ang = std::fmod(ang, two_pi);
+        a.cs[p] = (float)std::cos(ang);
+        a.sn[p] = (float)std::sin(ang);
+    }
+    const int per16 = j.dt == RTR_BF16 ? 8 : 4;  // elements per 16-byte group
+    a.d8 = j.d / per16;
+    a.n8 = j.rows * a.d8;
+    const dim3 grid((unsigned)((a.n8 + kThreads - 1) / kThreads));
+    if (j.dt == RTR_BF16)
+        hipLaunchKernelGGL(ref_rotate_bf16, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(ref_rotate_f32, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_frame_copies(const CopyJobs &jobs, hipStream_t stream) {
     if (jobs.n <= 0 || jobs.bytes <= 0) return hipSuccess;

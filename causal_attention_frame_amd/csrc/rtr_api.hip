@@ -34,6 +34,17 @@ struct rtr_kv_cache {
     int32_t count, head, ref_frames;
     int64_t ref_gen, next_id;
     int64_t slot_frame_id[RTR_MAX_WINDOW];  // indexed by physical slot
+    // Position-aware reference (rtr_kv_set_ref_rope): the reference K rotated
+    // into k_ref_view for the last shift applied, valid while (shift, ref_gen,
+    // ref_frames) are unchanged.
+    void *k_ref_view = nullptr;
+    int32_t rope_pairs = 0;
+    double rope_base = 10000.0;
+    int64_t pos_offset = 0;
+    // (memo of work already enqueued; a const call may update it)
+    mutable bool view_valid = false;
+    mutable int64_t view_shift = 0, view_gen = -1;
+    mutable int32_t view_frames = 0;
 };
 
 // One layer's text cross-attention cache (host-side metadata over caller buffers).
@@ -511,9 +522,10 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
     const int64_t in_b = fb * chunk_frames;
     const int64_t out_b = Tq * kv->H * kv->d * esize(out_dtype);
     const int64_t lse_b = Tq * kv->H * 4;
-    const void *ins[7] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
-    const int64_t in_sz[7] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
-    for (int i = 0; i < 7; ++i) {
+    const void *ins[8] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, kv->k_ref_view};
+    const int64_t in_sz[8] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap,
+                              kv->k_ref_view ? fb * kv->R_cap : 0};
+    for (int i = 0; i < 8; ++i) {
         if (overlaps(o, out_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "o overlaps an input or the cache");
         if (overlaps(lse, lse_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "lse overlaps an input or the cache");
     }
@@ -526,11 +538,38 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
         if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws)) return rc;
     }
 
+    // Position-aware reference: rotate the reference K so that it sits right
+    // in front of the oldest frame this call sees (re-rotated only when that
+    // position or the reference changes).
+    const void *kref = kv->k_ref;
+    if (kv->k_ref_view && kv->ref_frames > 0) {
+        const int64_t oldest = (kv->count > 0 ? kv->slot_frame_id[kv->head] : kv->next_id) + kv->pos_offset;
+        const int64_t shift = oldest - kv->ref_frames;
+        if (!(kv->view_valid && kv->view_shift == shift && kv->view_gen == kv->ref_gen &&
+              kv->view_frames == kv->ref_frames)) {
+            rtr::RotateJob j;
+            j.src = kv->k_ref;
+            j.dst = kv->k_ref_view;
+            j.rows = (int64_t)kv->ref_frames * kv->kpf * kv->H;
+            j.d = kv->d;
+            j.dt = kv->dt;
+            j.pairs = kv->rope_pairs;
+            j.base = kv->rope_base;
+            j.shift = shift;
+            if (const hipError_t e = rtr::launch_ref_rotate(j, (hipStream_t)stream)) return hip_fail(e, "reference rotation launch");
+            kv->view_valid = true;
+            kv->view_shift = shift;
+            kv->view_gen = kv->ref_gen;
+            kv->view_frames = kv->ref_frames;
+        }
+        kref = kv->k_ref_view;
+    }
+
     rtr::AttnProblem p;
     p.ws = ws;
     int nseg = 0;
     for (int r = 0; r < kv->ref_frames; ++r) {
-        p.kseg[nseg] = (const char *)kv->k_ref + r * fb;
+        p.kseg[nseg] = (const char *)kref + r * fb;
         p.vseg[nseg++] = (const char *)kv->v_ref + r * fb;
     }
     for (int i = 0; i < kv->count; ++i) {
@@ -687,6 +726,34 @@ int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse,
     return ok();
 }
 
+int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, float rope_base,
+                        int64_t position_offset) {
+    if (int rc = check_cache(kv)) return rc;
+    if (!k_ref_view) {
+        kv->k_ref_view = nullptr;
+        kv->view_valid = false;
+        return ok();
+    }
+    if (kv->R_cap < 1) return fail(RTR_ESTATE, "cache was created without reference capacity");
+    if (rope_pairs < 1 || rope_pairs > kv->d / 2)
+        return fail(RTR_EINVAL, "rope_pairs=%d outside [1, %d]", rope_pairs, kv->d / 2);
+    if (!(rope_base > 1.0f) || std::isinf(rope_base)) return fail(RTR_EINVAL, "rope_base must be finite and > 1");
+    if (position_offset < 0 || position_offset > kMaxTokens) return fail(RTR_EINVAL, "position_offset out of range");
+    if (!aligned16(k_ref_view)) return fail(RTR_EINVAL, "k_ref_view must be 16-byte aligned");
+    const int64_t fb = frame_bytes(kv);
+    const void *bufs[4] = {kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
+    const int64_t sizes[4] = {fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(k_ref_view, fb * kv->R_cap, bufs[i], sizes[i]))
+            return fail(RTR_EINVAL, "k_ref_view overlaps a cache buffer");
+    kv->k_ref_view = k_ref_view;
+    kv->rope_pairs = rope_pairs;
+    kv->rope_base = rope_base;
+    kv->pos_offset = position_offset;
+    kv->view_valid = false;
+    return ok();
+}
+
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out) {
     if (int rc = check_cache(kv)) return rc;
     if (!out) return fail(RTR_EINVAL, "out is NULL");
@@ -731,6 +798,7 @@ int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in) {
     kv->next_id = in->next_frame_id;
     for (auto &x : kv->slot_frame_id) x = -1;
     for (int p = 0; p < in->count; ++p) kv->slot_frame_id[in->slot[p]] = in->frame_id[p];
+    kv->view_valid = false;  // the restored reference may differ: rotate it again
     return ok();
 }
 

@@ -76,4 +76,20 @@ struct CopyJobs {
 
 hipError_t launch_frame_copies(const CopyJobs &jobs, hipStream_t stream);
 
+// Temporal rotary re-encoding of `rows` head rows of d elements: pairs
+// (2i, 2i+1), i < pairs, rotated by shift * base^(-i / pairs); src and dst are
+// 16-byte aligned and do not overlap.
+struct RotateJob {
+    const void *src = nullptr;
+    void *dst = nullptr;
+    int64_t rows = 0;
+    int32_t d = 0;
+    rtr_dtype dt = RTR_BF16;
+    int32_t pairs = 0;
+    double base = 10000.0;
+    int64_t shift = 0;
+};
+
+hipError_t launch_ref_rotate(const RotateJob &j, hipStream_t stream);
+
 }  // namespace rtr

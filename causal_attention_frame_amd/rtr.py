@@ -61,6 +61,7 @@ _SIGNATURES = {
                                             _c_f32, _vp, ctypes.c_size_t, _vp]),
     "rtr_attn_stream_step_blocked": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
                                                     ctypes.c_int, _c_f32, _vp, ctypes.c_size_t, _vp]),
+    "rtr_kv_set_ref_rope": (ctypes.c_int, [_vp, _vp, _c_i32, _c_f32, _c_i64]),
     "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
     "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
     "rtr_kv_set_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
@@ -306,6 +307,15 @@ def rtr_attn_stream_step_blocked(kv, q, k, v, chunk_frames, block_frames, o=None
                                               float(scale), ws, ws_bytes, _stream(stream, q.device)),
            "rtr_attn_stream_step_blocked")
     return o, lse
+
+
+def rtr_kv_set_ref_rope(kv, k_ref_view, rope_pairs=22, rope_base=10000.0, position_offset=1):
+    """Keep the anchored reference in front of the oldest visible frame (rotary
+    position re-encoding into k_ref_view); k_ref_view None switches it off."""
+    if k_ref_view is not None:
+        kv._view = k_ref_view  # keep the buffer alive with the handle
+    _check(lib().rtr_kv_set_ref_rope(kv.handle, _ptr(k_ref_view), int(rope_pairs), float(rope_base),
+                                     int(position_offset)), "rtr_kv_set_ref_rope")
 
 
 def rtr_kv_reset_ref(kv, mode, k_ref=None, v_ref=None, ref_frames=1, keep_recent=1, stream=None):

@@ -263,6 +263,26 @@ int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse,
                    rtr_dtype out_dtype, float scale, void *workspace, size_t workspace_bytes,
                    rtr_stream stream);
 
+/* Position-aware reference (rotary position encoding along time).  Rotary
+ * encodings are baked into cached K, so in a rolling window the frames keep
+ * their generation-time positions, which is exact for them (scores depend on
+ * position differences only) -- but a reference anchored at the start would
+ * drift ever further from the current frames.  With a view buffer set, every
+ * streaming call first re-encodes the reference K into k_ref_view so that
+ * the reference frames sit directly in front of the oldest frame the call
+ * sees, as the reference frame sits in front of the first frame in the full
+ * sequence, and the call reads the reference K from the view (V unchanged).
+ * Conventions: the caller encodes each frame's Q and K at temporal position
+ * frame_id + position_offset (frame ids count appended frames from 0, see
+ * rtr_kv_state) and reference frame r at position r; the encoding rotates
+ * element pairs (2i, 2i+1) of every head, i < rope_pairs, by position *
+ * rope_base^(-i / rope_pairs).  The reference is re-encoded (one kernel, bytes
+ * of the reference read and written once) only when that position, the
+ * reference or the number of reference frames changes.  k_ref_view:
+ * [R_cap, k, H, d] caller-owned device buffer, or NULL to switch this off. */
+int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, float rope_base,
+                        int64_t position_offset);
+
 /* Metadata snapshot / restore (checkpoint-resume).  set_state validates the
  * snapshot against the cache's W and R_cap and changes nothing on error. */
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out);

@@ -332,3 +332,22 @@ def test_text_cache_metadata_and_rejections():
     assert L.rtr_text_cache_reset(h, None, None, 0, None) == rtr.RTR_OK
     assert L.rtr_text_cache_state(h, ctypes.byref(n), ctypes.byref(g)) == 0 and (n.value, g.value) == (0, 2)
     assert L.rtr_text_cache_destroy(h) == rtr.RTR_OK
+
+
+def test_ref_rope_rejections():
+    kv = _cache(W=3, R=1)
+    L = rtr.lib()
+    h = kv.handle
+    fb = 8 * 2 * 64 * 2
+    view = FAKE + 512 * MB
+    assert L.rtr_kv_set_ref_rope(h, view, 0, 10000.0, 1) == rtr.RTR_EINVAL          # no pairs
+    assert L.rtr_kv_set_ref_rope(h, view, 33, 10000.0, 1) == rtr.RTR_EINVAL         # > d / 2
+    assert L.rtr_kv_set_ref_rope(h, view, 8, 1.0, 1) == rtr.RTR_EINVAL              # base
+    assert L.rtr_kv_set_ref_rope(h, view, 8, 10000.0, -1) == rtr.RTR_EINVAL         # offset
+    assert L.rtr_kv_set_ref_rope(h, view + 8, 8, 10000.0, 1) == rtr.RTR_EINVAL      # misaligned
+    assert L.rtr_kv_set_ref_rope(h, FAKE + 16, 8, 10000.0, 1) == rtr.RTR_EINVAL     # overlaps the ring
+    assert L.rtr_kv_set_ref_rope(h, view, 8, 10000.0, 1) == rtr.RTR_OK
+    assert L.rtr_kv_set_ref_rope(h, None, 0, 0.0, 0) == rtr.RTR_OK                  # off
+    kv0 = _cache(W=3, R=0)
+    assert L.rtr_kv_set_ref_rope(kv0.handle, view, 8, 10000.0, 1) == rtr.RTR_ESTATE
+    assert fb > 0
