@@ -14,13 +14,13 @@
 //   attn_bwd_prep       one 32-row tile per workgroup: LSE in log2 units and D
 //                       per row, and the tile's Q and dO transposed into the
 //                       layout the dK/dV kernel reads as MFMA A operands;
-//   attn_bwd_dkdv_d128  one workgroup per 256 keys of a head, one wave per
-//                       SIMD, 64 keys per wave (two 32-key halves, so every
-//                       Q, dO and transposed fragment read from LDS feeds two
-//                       MFMAs): K and V stay in VGPRs as MFMA B operands, dK^T
-//                       and dV^T (256 floats per lane) in AGPRs, and the
-//                       workgroup walks the 32-row query tiles that see its
-//                       keys, staged into an LDS ring by DMA;
+//   attn_bwd_dkdv_d128  one workgroup per 256 keys of a head, 8 waves of 32
+//                       keys (two per SIMD): K stays in VGPRs as the MFMA B
+//                       operand, V is staged once into LDS in the B operand's
+//                       lane order, dK^T and dV^T (128 floats per lane) live in
+//                       AGPRs, and the workgroup walks the 32-row query tiles
+//                       that see its keys, staged into a 2-stage LDS ring by
+//                       DMA one tile ahead;
 //   attn_bwd_dq_d128    one workgroup per 256 query rows (8 waves x 32): Q and
 //                       dO stay in registers, the workgroup walks the 32-key
 //                       tiles its rows see; dQ^T accumulates in registers.
@@ -88,8 +88,8 @@ __device__ inline int swz_dual(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); 
 
 // acc += A B with the accumulator held in AGPRs.  This file is built with
 // builtin MFMAs in VGPR form (their results feed VALU code); the long-lived
-// dK/dV accumulators of the one-wave-per-SIMD kernel live in AGPRs through
-// this statement instead.  The s_nop covers a VALU write of an A or B operand
+// dK/dV accumulators live in AGPRs through this statement instead, so that the
+// rest of the dK/dV kernel fits the 128 VGPRs of two waves per SIMD.  The s_nop covers a VALU write of an A or B operand
 // just before; the hardware forwards an exactly matching accumulator from the
 // previous MFMA of the same shape.
 __device__ inline void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
@@ -164,38 +164,34 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const BArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK and dV: one workgroup per 256 keys, 4 waves of 64 keys.
+// dK and dV: one workgroup per 256 keys, 8 waves of 32 keys.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_d128(const BArgs a) {
-    constexpr int NS = 8, NT = 4, NSTG = 4;
+    constexpr int NS = 8, NT = 4, NSTG = 2;
     // One LDS array: regions of NSTG stages each -- row-major Q, row-major dO,
-    // transposed Q, transposed dO (8 KB per stage), then the row statistics
-    // (256 B per stage).
+    // transposed Q, transposed dO (8 KB per stage), the row statistics (256 B
+    // per stage) -- then the workgroup's V rows (64 KB): step s of wave w at
+    // RV + (8 w + s) 512 + 8 lane, one lane-linear 16-byte read.
     constexpr int RQ = 0, RDO = NSTG * kTile, RQT = 2 * NSTG * kTile, RDOT = 3 * NSTG * kTile;
     constexpr int RROW = 4 * NSTG * kTile;  // in uint16 units
-    __shared__ __attribute__((aligned(256))) uint16_t smem[4 * NSTG * kTile + NSTG * 128];
+    constexpr int RV = RROW + NSTG * 128;
+    __shared__ __attribute__((aligned(256))) uint16_t smem[RV + 256 * kD];
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..3, one per SIMD
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, two per SIMD
     const int n = lane & 31, g = lane >> 5;
 
     int head, blk;
     xcd_order(blockIdx.x, a.nwg, a.nkb, head, blk);
-    const int kb = a.nkb - 1 - blk;  // highest order index = lowest keys = most rows
+    const int kb = a.nkb - 1 - blk;
     const int k0 = kb * 256;
     const long hoff = (long)head * kD;
 
-    // This lane's keys (column n of the wave's two 32-key halves) and the
-    // first row that sees each.
-    int kj[2], qmin[2];
-    bool kvalid[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        kj[h] = k0 + 64 * wave + 32 * h + n;
-        kvalid[h] = kj[h] < a.T;
-        qmin[h] = (kj[h] / a.kpf) * a.kpf;
-    }
+    // This lane's key (column n of the wave's S tiles) and the first row that sees it.
+    const int kj = k0 + 32 * wave + n;
+    const bool kvalid = kj < a.T;
+    const int qmin = (kj / a.kpf) * a.kpf;
     const int t0 = ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
     const int nt = a.nqt - t0;
     // Tiles that start below the first row of the block's last key frame may
@@ -203,59 +199,53 @@ void attn_bwd_dkdv_d128(const BArgs a) {
     const int last_key = min(k0 + 255, a.T - 1);
     const int nmask = min(nt, max(0, ((last_key / a.kpf) * a.kpf - t0 * 32 + 31) / 32));
 
-    // K and V as B operands: lane (n, g) holds row kj, columns 16 s + 8 g .. + 7.
-    bf16x8 kf[2][NS], vf[2][NS];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const long ro = (long)(kvalid[h] ? kj[h] : a.T - 1) * a.ld + hoff;
+    // K as B operands in registers (lane (n, g): row kj, columns 16 s + 8 g ..),
+    // V rows of the same lanes DMA'd into LDS.
+    const uint32_t lbase = lds_addr((lds_u16 *)smem);
+    bf16x8 kf[NS];
+    {
+        const long ro = (long)(kvalid ? kj : a.T - 1) * a.ld + hoff;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            kf[h][s] = __builtin_bit_cast(bf16x8, gload16(a.k + ro + 16 * s + 8 * g));
-            vf[h][s] = __builtin_bit_cast(bf16x8, gload16(a.v + ro + 16 * s + 8 * g));
+            kf[s] = __builtin_bit_cast(bf16x8, gload16(a.k + ro + 16 * s + 8 * g));
+            dma16((uint64_t)a.v, (uint32_t)((ro + 16 * s + 8 * g) * 2), lbase + 2 * (RV + (wave * NS + s) * 512));
         }
     }
     // Complete these loads here: otherwise the compiler's wait for them sits
     // inside the tile loop, where it would also drain the DMA ring.
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     compiler_fence();
+    const uint32_t pv = lbase + 2 * (RV + wave * NS * 512 + 8 * lane);
 
-    // DMA of one query tile, 9 loads per wave: row-major Q and dO (wave w
-    // fills rows 8w .. 8w + 7, lane (lr, pch) stored chunk pch of row
-    // 8w + 4r + lr), the two transposed tiles (contiguous 8 KB, wave w its
-    // 2 KB) and the row statistics (64 bytes per wave, lanes 0..3).
+    // DMA of one query tile, 5 loads per wave: row-major Q and dO (wave w
+    // fills rows 4w + lr, lane (lr, pch) the stored chunk pch), the two
+    // transposed tiles (contiguous 8 KB, wave w its 1 KB) and the row
+    // statistics (32 bytes per wave, lanes 0 and 1).
     const int lr = lane >> 4, pch = lane & 15;
-    const uint32_t lbase = lds_addr((lds_u16 *)smem);
+    const int prow = 4 * wave + lr;
+    const uint32_t plain_col = (uint32_t)(16 * (pch ^ swz_plain(prow)));
+    const uint32_t l0 = lbase + 1024 * wave;
     auto issue = [&](int i) __attribute__((always_inline)) {
         const int st = i & (NSTG - 1);
         const int tq = min(t0 + i, a.nqt - 1);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int rt = 8 * wave + 4 * r + lr;
-            const int row = min(tq * 32 + rt, a.T - 1);
-            const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + 16u * (pch ^ swz_plain(rt));
-            const uint32_t m = lbase + 2 * st * kTile + 256 * (8 * wave + 4 * r);
-            dma16x2((uint64_t)a.q, (uint64_t)a.dout, off, off, m + 2 * RQ, m + 2 * RDO);
-        }
-        const long tb = ((long)head * a.nqt + tq) * kTile * 2 + 2048 * wave;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const uint32_t m = lbase + 2 * st * kTile + 2048 * wave + 1024 * r;
-            dma16x2((uint64_t)a.qt + tb + 1024 * r, (uint64_t)a.dot + tb + 1024 * r, 16u * lane, 16u * lane,
-                    m + 2 * RQT, m + 2 * RDOT);
-        }
-        const uint64_t rb = (uint64_t)(a.rows + ((long)head * a.nqt + tq) * 64 + 16 * wave);
-        if (lane < 4) dma16(rb, 16u * lane, lbase + 2 * RROW + 256 * st + 64 * wave);
+        const int row = min(tq * 32 + prow, a.T - 1);
+        const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + plain_col;
+        dma16x2((uint64_t)a.q, (uint64_t)a.dout, off, off, l0 + 2 * (RQ + st * kTile), l0 + 2 * (RDO + st * kTile));
+        const long tb = ((long)head * a.nqt + tq) * kTile * 2 + 1024 * wave;
+        dma16x2((uint64_t)a.qt + tb, (uint64_t)a.dot + tb, 16u * lane, 16u * lane, l0 + 2 * (RQT + st * kTile),
+                l0 + 2 * (RDOT + st * kTile));
+        const uint64_t rb = (uint64_t)(a.rows + ((long)head * a.nqt + tq) * 64 + 8 * wave);
+        if (lane < 2) dma16(rb, 16u * lane, lbase + 2 * (RROW + st * 128) + 32 * wave);
     };
 
-    // Fragment addresses in stage 0 (bytes).  Plain read of k-step s: row n,
-    // logical chunk 2s + g, stored at chunk (2s + g) ^ (n mod 16); the dO
-    // region is an immediate offset away.  Transposed read of row d = 32 t + n,
-    // k-step h: logical chunk 2h + g, stored at (2h + g) ^ (n/4 mod 4); t and
-    // the dO^T region are immediate offsets.  Row statistics of rows
+    // Fragment addresses (bytes, stage 0; region and stage offsets are
+    // immediates or a per-step add).  Plain read of k-step s (row n, logical
+    // chunk 2s + g, stored at (2s + g) ^ (n mod 16)) at aq ^ 32 s.  Transposed
+    // read of row d = 32 t + n, k-step h (logical chunk 2h + g, stored at
+    // (2h + g) ^ (n/4 mod 4)) at pt[h] + 2048 t.  Row statistics of rows
     // 8 j + 4 g .. + 3: LSE at pr + 32 j, D 128 bytes further.
-    uint32_t pq[NS], pt[2];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) pq[s] = lbase + 2 * (n * kD + 8 * ((2 * s + g) ^ swz_plain(n)));
+    uint32_t pt[2];
+    const uint32_t aq = lbase + 2 * (n * kD + 8 * (g ^ swz_plain(n)));
 #pragma unroll
     for (int h = 0; h < 2; ++h) pt[h] = lbase + 2 * (RQT + n * 32 + 8 * ((2 * h + g) ^ ((n >> 2) & 3)));
     const uint32_t pr = lbase + 2 * RROW + 16 * g;
@@ -263,36 +253,27 @@ void attn_bwd_dkdv_d128(const BArgs a) {
         return lds_b128((const lds_u16 *)(uintptr_t)addr + imm / 2);
     };
 
-    f32x16 dkt[2][NT], dvt[2][NT];
+    f32x16 dkt[NT], dvt[NT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) dkt[h][t] = dvt[h][t] = f32x16{};
+    for (int t = 0; t < NT; ++t) dkt[t] = dvt[t] = f32x16{};
     const float c = a.c;
 
-    // One query tile: S = Q K^T and dP = dO V^T for both key halves (each Q and
-    // dO fragment feeds two MFMAs), P and dS in fp32, then dV^T += dO^T P and
-    // dK^T += Q^T dS (each transposed fragment feeds two MFMAs).
+    // One query tile: S = Q K^T, dP = dO V^T, P = exp2(S c - LSE2) and
+    // dS = P (dP - D) in fp32, then dV^T += dO^T P and dK^T += Q^T dS.
     auto step = [&](int i, auto masked) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(masked)::value;
-        __builtin_amdgcn_s_waitcnt(wait_vm(18));  // this wave's loads of tile i landed
-        lds_barrier();                             // everyone's have; stage of tile i - 1 is free
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's loads of tile i landed
+        lds_barrier();                            // everyone's have; stage of tile i - 1 is free
+        issue(i + 1);                             // into that stage, one tile ahead
         const uint32_t so = (uint32_t)((i & (NSTG - 1)) * kTile * 2);
         const uint32_t rso = (uint32_t)((i & (NSTG - 1)) * 256);
-        f32x16 s0 = {}, s1 = {}, d0 = {}, d1 = {};
+        f32x16 s0 = {}, d0 = {};
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const bf16x8 qa = rd(pq[k] + so, 2 * RQ);
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[0][k], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[1][k], s1, 0, 0, 0);
-        }
+        for (int k = 0; k < NS; ++k)
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd((aq + so) ^ (32u * k), 2 * RQ), kf[k], s0, 0, 0, 0);
 #pragma unroll
-        for (int k = 0; k < NS; ++k) {
-            const bf16x8 da = rd(pq[k] + so, 2 * RDO);
-            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[0][k], d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[1][k], d1, 0, 0, 0);
-        }
-        // P = exp2(S c - LSE2) in place; rows 8 j + 4 g + e of the tile.
+        for (int k = 0; k < NS; ++k)
+            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd((aq + so) ^ (32u * k), 2 * RDO), rd(pv, 1024 * k), d0, 0, 0, 0);
         const int q0 = (t0 + i) * 32 + 4 * g;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -301,61 +282,35 @@ void attn_bwd_dkdv_d128(const BArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int r = 4 * j + e;
                 s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -l2[e]));
-                s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -l2[e]));
-                if (MASK) {
-                    s0[r] = (q0 + 8 * j + e >= qmin[0]) ? s0[r] : 0.f;
-                    s1[r] = (q0 + 8 * j + e >= qmin[1]) ? s1[r] : 0.f;
-                }
+                if (MASK) s0[r] = (q0 + 8 * j + e >= qmin) ? s0[r] : 0.f;
             }
         }
-        bf16x8 pb[2][2], sb[2][2];
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            pb[0][h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s0[8 * h], s0[8 * h + 1]), pack_bf16x2(s0[8 * h + 2], s0[8 * h + 3]),
-                                                        pack_bf16x2(s0[8 * h + 4], s0[8 * h + 5]), pack_bf16x2(s0[8 * h + 6], s0[8 * h + 7])});
-            pb[1][h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s1[8 * h], s1[8 * h + 1]), pack_bf16x2(s1[8 * h + 2], s1[8 * h + 3]),
-                                                        pack_bf16x2(s1[8 * h + 4], s1[8 * h + 5]), pack_bf16x2(s1[8 * h + 6], s1[8 * h + 7])});
-        }
+        for (int h = 0; h < 2; ++h)
+            pb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s0[8 * h], s0[8 * h + 1]), pack_bf16x2(s0[8 * h + 2], s0[8 * h + 3]),
+                                                     pack_bf16x2(s0[8 * h + 4], s0[8 * h + 5]), pack_bf16x2(s0[8 * h + 6], s0[8 * h + 7])});
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8 ao = rd(pt[h] + so, 2 * (RDOT - RQT) + 2048 * t);
-                mfma_acc(dvt[0][t], ao, pb[0][h]);
-                mfma_acc(dvt[1][t], ao, pb[1][h]);
-            }
-        // dS = P (dP - D), with the fp32 P.
+            for (int h = 0; h < 2; ++h) mfma_acc(dvt[t], rd(pt[h] + so, 2 * (RDOT - RQT) + 2048 * t), pb[h]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 dd = *(const lds_f32x4 *)((const lds_u16 *)(uintptr_t)(pr + rso) + 64 + 16 * j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * j + e;
-                d0[r] = s0[r] * (d0[r] - dd[e]);
-                d1[r] = s1[r] * (d1[r] - dd[e]);
-            }
+            for (int e = 0; e < 4; ++e) d0[4 * j + e] = s0[4 * j + e] * (d0[4 * j + e] - dd[e]);
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            sb[0][h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(d0[8 * h], d0[8 * h + 1]), pack_bf16x2(d0[8 * h + 2], d0[8 * h + 3]),
-                                                        pack_bf16x2(d0[8 * h + 4], d0[8 * h + 5]), pack_bf16x2(d0[8 * h + 6], d0[8 * h + 7])});
-            sb[1][h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(d1[8 * h], d1[8 * h + 1]), pack_bf16x2(d1[8 * h + 2], d1[8 * h + 3]),
-                                                        pack_bf16x2(d1[8 * h + 4], d1[8 * h + 5]), pack_bf16x2(d1[8 * h + 6], d1[8 * h + 7])});
-        }
+        for (int h = 0; h < 2; ++h)
+            sb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(d0[8 * h], d0[8 * h + 1]), pack_bf16x2(d0[8 * h + 2], d0[8 * h + 3]),
+                                                     pack_bf16x2(d0[8 * h + 4], d0[8 * h + 5]), pack_bf16x2(d0[8 * h + 6], d0[8 * h + 7])});
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8 aq = rd(pt[h] + so, 2048 * t);
-                mfma_acc(dkt[0][t], aq, sb[0][h]);
-                mfma_acc(dkt[1][t], aq, sb[1][h]);
-            }
-        issue(i + NSTG - 1);
+            for (int h = 0; h < 2; ++h) mfma_acc(dkt[t], rd(pt[h] + so, 2048 * t), sb[h]);
     };
 
     issue(0);
-    issue(1);
-    issue(2);
     int i = 0;
 #pragma unroll 1
     for (; i < nmask; ++i) step(i, std::true_type{});
@@ -366,22 +321,19 @@ void attn_bwd_dkdv_d128(const BArgs a) {
     // AGPRs below (more than the 18 a 16-pass MFMA needs).
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
+    if (!kvalid) return;
+    const long ob = (long)kj * a.ld + hoff;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (!kvalid[h]) continue;
-        const long ob = (long)kj[h] * a.ld + hoff;
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d0 = 32 * t + 8 * j + 4 * g;
-                const f32x16 &k_ = dkt[h][t], &v_ = dvt[h][t];
-                *(u32x2 *)(a.dk + ob + d0) = u32x2{pack_bf16x2(k_[4 * j] * a.scale, k_[4 * j + 1] * a.scale),
-                                                   pack_bf16x2(k_[4 * j + 2] * a.scale, k_[4 * j + 3] * a.scale)};
-                *(u32x2 *)(a.dv + ob + d0) = u32x2{pack_bf16x2(v_[4 * j], v_[4 * j + 1]),
-                                                   pack_bf16x2(v_[4 * j + 2], v_[4 * j + 3])};
-            }
-    }
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = 32 * t + 8 * j + 4 * g;
+            const f32x16 &k_ = dkt[t], &v_ = dvt[t];
+            *(u32x2 *)(a.dk + ob + d0) = u32x2{pack_bf16x2(k_[4 * j] * a.scale, k_[4 * j + 1] * a.scale),
+                                               pack_bf16x2(k_[4 * j + 2] * a.scale, k_[4 * j + 3] * a.scale)};
+            *(u32x2 *)(a.dv + ob + d0) = u32x2{pack_bf16x2(v_[4 * j], v_[4 * j + 1]),
+                                               pack_bf16x2(v_[4 * j + 2], v_[4 * j + 3])};
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -575,7 +527,7 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
     hipLaunchKernelGGL(attn_bwd_prep, dim3(a.nqt, p.H), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     a.nwg = p.H * a.nkb;
-    hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     a.nwg = p.H * a.nqb;
     hipLaunchKernelGGL(attn_bwd_dq_d128, dim3(a.nwg), dim3(512), 0, stream, a);
