@@ -85,3 +85,20 @@ def test_bwd_full_size_sampled():
     rk, rv = attn_bwd_cols(q.values, k.values, v.values, do.values, kpf, cols, heads)
     assert_grad_close(host(dk[cols][:, heads]), rk, "dk cols")
     assert_grad_close(host(dv[cols][:, heads]), rv, "dv cols")
+
+
+def test_bwd_many_heads_sampled():
+    """40 heads (the Wan-14B layer's head count) over two frames and a ragged
+    third: every head's blocks land on the right XCD ranges and rows."""
+    kpf, H = 1560, 40
+    T = 2 * kpf + 100
+    (q, k, v, do), (dq, dk, dv) = _run(T, H, kpf, seed=9, wid=43)
+    rng = np.random.default_rng(10)
+    heads = [0, 17, 39]
+    rows = sorted(set(rng.choice(T, 12, replace=False).tolist()) | {0, kpf, T - 1})
+    assert_grad_close(host(dq[rows][:, heads]), attn_bwd_rows(q.values, k.values, v.values, do.values,
+                                                             kpf, rows, heads), "dq rows")
+    cols = sorted(set(rng.choice(T, 12, replace=False).tolist()) | {0, 2 * kpf, T - 1})
+    rk, rv = attn_bwd_cols(q.values, k.values, v.values, do.values, kpf, cols, heads)
+    assert_grad_close(host(dk[cols][:, heads]), rk, "dk cols")
+    assert_grad_close(host(dv[cols][:, heads]), rv, "dv cols")
