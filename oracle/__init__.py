@@ -40,6 +40,7 @@ from .attention_bwd import (  # noqa: F401
     attn_block_causal_bwd,
     attn_bwd_rows,
     attn_bwd_cols,
+    attn_stream_step_bwd,
 )
 from .rope import rope_rotate, reference_shift  # noqa: F401
 from .listkv import ListKV, TextKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401

@@ -123,3 +123,36 @@ def attn_bwd_cols(q, k, v, do, tokens_per_frame, cols, heads=None, scale=None, g
             dv[:, a] += Pc.T @ _f64(do[ii, h])
             dk[:, a] += sc * (dSc.T @ _f64(q[ii, h]))
     return dk, dv
+
+
+def attn_stream_step_bwd(prefix_k, prefix_v, q, k, v, do, tokens_per_frame, scale=None):
+    """Gradients of one streaming step (the attention a chunk runs against the
+    cached prefix), dense and literal.
+
+    prefix_k/prefix_v: [P, H, d] cached keys/values (anchored reference, then
+    the window); q, k, v, do: [C*k, H, d] for the chunk.  Chunk row r sees every
+    prefix key and the chunk keys of chunk frames <= its own (tokens_per_frame
+    sets the mask unit).  Returns (dq, dk, dv, dk_prefix, dv_prefix), float64.
+    """
+    pk, pv = _f64(prefix_k), _f64(prefix_v)
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    Tq, H, d = q.shape
+    P = pk.shape[0]
+    sc = _scale(d, scale)
+    i = np.arange(Tq)[:, None]
+    j = np.arange(Tq)[None, :]
+    M = np.concatenate([np.zeros((Tq, P)),
+                        np.where(visible(i, j, tokens_per_frame), 0.0, -np.inf)], axis=1)
+    kk = np.concatenate([pk, k], axis=0)
+    vv = np.concatenate([pv, v], axis=0)
+    dq = np.empty_like(q)
+    dkk = np.empty_like(kk)
+    dvv = np.empty_like(vv)
+    for h in range(H):
+        Pm = _probs((q[:, h] @ kk[:, h].T) * sc + M)
+        dvv[:, h] = Pm.T @ do[:, h]
+        dP = do[:, h] @ vv[:, h].T
+        dS = Pm * (dP - np.sum(dP * Pm, axis=1, keepdims=True))
+        dq[:, h] = sc * (dS @ kk[:, h])
+        dkk[:, h] = sc * (dS.T @ q[:, h])
+    return dq, dkk[P:], dvv[P:], dkk[:P], dvv[:P]

@@ -120,3 +120,48 @@ def test_rows_and_cols_variants_equal_dense():
     ck, cv = attn_bwd_cols(q, k, v, g, kpf, cols, [1], group=7)
     np.testing.assert_allclose(ck, dk[cols][:, [1]], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(cv, dv[cols][:, [1]], rtol=1e-12, atol=1e-13)
+
+
+def test_stream_step_bwd_equals_full_form_with_earlier_rows_silent():
+    """Pin: a streaming step over [prefix frames | chunk] is the full form's
+    last chunk; with dO zero on the prefix frames' own rows, the full-form
+    gradients of the chunk rows and of every key are the step's gradients."""
+    from oracle.attention_bwd import attn_stream_step_bwd
+    kpf, H, d, Pf, C = 4, 2, 8, 3, 2
+    T = (Pf + C) * kpf
+    q, k, v, g = _inputs(T, H, d, 60)
+    g[:Pf * kpf] = 0.0
+    dq, dk, dv = attn_block_causal_bwd(q, k, v, g, kpf)
+    c = slice(Pf * kpf, T)
+    sq, sk, sv, spk, spv = attn_stream_step_bwd(k[:Pf * kpf], v[:Pf * kpf], q[c], k[c], v[c], g[c], kpf)
+    np.testing.assert_allclose(sq, dq[c], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sk, dk[c], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sv, dv[c], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(spk, dk[:Pf * kpf], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(spv, dv[:Pf * kpf], rtol=1e-11, atol=1e-12)
+
+
+def test_stream_step_bwd_central_differences():
+    """Pin: central differences of sum(O * G) through the (pinned) streaming
+    forward oracle, for the chunk's q, k, v and for the cached prefix."""
+    from oracle.attention_bwd import attn_stream_step_bwd
+    kpf, H, d, C, P = 3, 1, 4, 2, 5
+    pk, pv = _rand((P, H, d), 70), _rand((P, H, d), 71)
+    q, k, v, g = _inputs(C * kpf, H, d, 72)
+    grads = attn_stream_step_bwd(pk, pv, q, k, v, g, kpf)
+    args = [pk, pv, q, k, v]
+    eps = 1e-6
+
+    def loss(a):
+        o, _ = oracle.attn_stream_step(a[0], a[1], a[2], a[3], a[4], kpf)
+        return float(np.sum(o * g))
+
+    for which, grad in ((2, grads[0]), (3, grads[1]), (4, grads[2]), (0, grads[3]), (1, grads[4])):
+        num = np.zeros_like(grad)
+        for idx in np.ndindex(*grad.shape):
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[which][idx] += eps
+            am[which][idx] -= eps
+            num[idx] = (loss(ap) - loss(am)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
