@@ -27,6 +27,14 @@
 // dQ is produced apart from dK/dV, recomputing S and dP, so that no partial
 // sum leaves a workgroup: no atomics, and the result is deterministic.
 //
+// Streaming step (a chunk attending to the cached reference and window frames
+// in front of it, Key Designs 4): the chunk rows see `prefix` cached keys and
+// the chunk's own keys under the frame mask.  The prefix enters the chunk-key
+// gradients only through LSE and D, so the chunk's dK/dV is the full form over
+// the chunk; the prefix keys, seen by every row, are further dK/dV blocks of
+// the same kernel that read their keys through a table of frame segments; and
+// dQ walks the segment table over all keys.
+//
 // MFMA is v_mfma_f32_32x32x16_bf16.  Lane l of a wave is (n = l mod 32,
 // g = l / 32).  An A operand lane holds row n and k = 8g..8g+7 of a 16-step;
 // a B operand lane column n and the same k; accumulator element r of a lane is
@@ -61,6 +69,16 @@ struct BArgs {
     int64_t ld;        // row stride in elements (H * 128)
     float c;           // scale * log2(e)
     float scale;
+    // Streaming step: keys [0, Tk) lie in segments of seg_len keys (row
+    // j - f seg_len of the [*, H, 128] block at kseg[f] / vseg[f]); the first
+    // `prefix` are seen by every query row.  The full form has Tk = T and no
+    // prefix.  dkp/dvp receive the prefix keys' gradients ([prefix][H][128]);
+    // nkbp counts their 256-key blocks per head (0: not wanted).
+    const void *kseg[kMaxKeyFrames], *vseg[kMaxKeyFrames];
+    int32_t nseg, seg_len;
+    float inv_seg_len;
+    int32_t prefix, Tk, nkbp;
+    uint16_t *dkp, *dvp;
 };
 
 constexpr int kD = 128;
@@ -95,6 +113,27 @@ __device__ inline int swz_dual(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); 
 __device__ inline void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
     asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+
+// Segment holding key j (the float estimate corrected by one step).
+__device__ inline int seg_of(int j, const BArgs &a) {
+    int f = (int)((float)j * a.inv_seg_len);
+    const int rem = j - f * a.seg_len;
+    if (rem < 0) --f;
+    else if (rem >= a.seg_len) ++f;
+    return f;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the clobber is still honoured
+// DMA of 16 bytes per lane from a per-lane 64-bit address to LDS byte address
+// m0 + 16 * lane (rows from a segment table have no common base).
+__device__ inline void dma16_lane(const void *src, uint32_t m0a) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0a)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -166,44 +205,57 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const BArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV: one workgroup per 256 keys, 8 waves of 32 keys.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dkdv_d128(const BArgs a) {
-    constexpr int NS = 8, NT = 4, NSTG = 2;
-    // One LDS array: regions of NSTG stages each -- row-major Q, row-major dO,
-    // transposed Q, transposed dO (8 KB per stage), the row statistics (256 B
-    // per stage) -- then the workgroup's V rows (64 KB): step s of wave w at
-    // RV + (8 w + s) 512 + 8 lane, one lane-linear 16-byte read.
+// One LDS array: regions of NSTG stages each -- row-major Q, row-major dO,
+// transposed Q, transposed dO (8 KB per stage), the row statistics (256 B per
+// stage) -- then the workgroup's V rows (64 KB): step s of wave w at
+// RV + (8 w + s) 512 + 8 lane, one lane-linear 16-byte read.
+constexpr int kDkdvStages = 2;
+constexpr int kDkdvLds = 4 * kDkdvStages * kTile + kDkdvStages * 128 + 256 * kD;  // uint16 units
+
+// Key block kb of a head: the query rows' own keys (PRE false: the full form,
+// or the chunk's keys of a streaming step) or the cached prefix keys (PRE
+// true), which every query row sees and which are read through the segment
+// table.  lbase: LDS byte address of the kDkdvLds array.
+template <bool PRE>
+__device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a, int head, int kb, uint32_t lbase) {
+    constexpr int NS = 8, NT = 4, NSTG = kDkdvStages;
     constexpr int RQ = 0, RDO = NSTG * kTile, RQT = 2 * NSTG * kTile, RDOT = 3 * NSTG * kTile;
     constexpr int RROW = 4 * NSTG * kTile;  // in uint16 units
     constexpr int RV = RROW + NSTG * 128;
-    __shared__ __attribute__((aligned(256))) uint16_t smem[RV + 256 * kD];
+    const bool pre = PRE;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, two per SIMD
     const int n = lane & 31, g = lane >> 5;
-
-    int head, blk;
-    xcd_order(blockIdx.x, a.nwg, a.nkb, head, blk);
-    const int kb = a.nkb - 1 - blk;
     const int k0 = kb * 256;
     const long hoff = (long)head * kD;
 
     // This lane's key (column n of the wave's S tiles) and the first row that sees it.
     const int kj = k0 + 32 * wave + n;
-    const bool kvalid = kj < a.T;
-    const int qmin = (kj / a.kpf) * a.kpf;
-    const int t0 = ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
+    const int nkeys = pre ? a.prefix : a.T;
+    const bool kvalid = kj < nkeys;
+    const int qmin = pre ? 0 : (kj / a.kpf) * a.kpf;
+    const int t0 = pre ? 0 : ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
     const int nt = a.nqt - t0;
     // Tiles that start below the first row of the block's last key frame may
     // hold rows that miss some of its keys: they take the element-wise mask.
     const int last_key = min(k0 + 255, a.T - 1);
-    const int nmask = min(nt, max(0, ((last_key / a.kpf) * a.kpf - t0 * 32 + 31) / 32));
+    const int nmask = pre ? 0 : min(nt, max(0, ((last_key / a.kpf) * a.kpf - t0 * 32 + 31) / 32));
 
     // K as B operands in registers (lane (n, g): row kj, columns 16 s + 8 g ..),
     // V rows of the same lanes DMA'd into LDS.
-    const uint32_t lbase = lds_addr((lds_u16 *)smem);
     bf16x8 kf[NS];
-    {
+    if constexpr (PRE) {
+        const int jj = kvalid ? kj : a.prefix - 1;
+        const int f = seg_of(jj, a);
+        const long o = (long)(jj - f * a.seg_len) * a.ld + hoff + 8 * g;
+        const uint16_t *kr = (const uint16_t *)a.kseg[f] + o, *vr = (const uint16_t *)a.vseg[f] + o;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kf[s] = __builtin_bit_cast(bf16x8, gload16(kr + 16 * s));
+            dma16_lane(vr + 16 * s, lbase + 2 * (RV + (wave * NS + s) * 512));
+        }
+    } else {
         const long ro = (long)(kvalid ? kj : a.T - 1) * a.ld + hoff;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -323,26 +375,45 @@ void attn_bwd_dkdv_d128(const BArgs a) {
 
     if (!kvalid) return;
     const long ob = (long)kj * a.ld + hoff;
+    uint16_t *const dko = pre ? a.dkp : a.dk, *const dvo = pre ? a.dvp : a.dv;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d0 = 32 * t + 8 * j + 4 * g;
             const f32x16 &k_ = dkt[t], &v_ = dvt[t];
-            *(u32x2 *)(a.dk + ob + d0) = u32x2{pack_bf16x2(k_[4 * j] * a.scale, k_[4 * j + 1] * a.scale),
+            *(u32x2 *)(dko + ob + d0) = u32x2{pack_bf16x2(k_[4 * j] * a.scale, k_[4 * j + 1] * a.scale),
                                                pack_bf16x2(k_[4 * j + 2] * a.scale, k_[4 * j + 3] * a.scale)};
-            *(u32x2 *)(a.dv + ob + d0) = u32x2{pack_bf16x2(v_[4 * j], v_[4 * j + 1]),
+            *(u32x2 *)(dvo + ob + d0) = u32x2{pack_bf16x2(v_[4 * j], v_[4 * j + 1]),
                                                pack_bf16x2(v_[4 * j + 2], v_[4 * j + 3])};
         }
 }
 
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_d128(const BArgs a) {
+    __shared__ __attribute__((aligned(256))) uint16_t smem[kDkdvLds];
+    int head, blk;
+    xcd_order(blockIdx.x, a.nwg, a.nkb + a.nkbp, head, blk);
+    // Blocks of cached prefix keys (streaming step; every row sees them, so
+    // they carry the most work) take the highest indices, then the blocks of
+    // the query rows' own keys, earliest keys highest.
+    const uint32_t lbase = lds_addr((lds_u16 *)smem);
+    if (blk >= a.nkb)
+        dkdv_block<true>(a, head, blk - a.nkb, lbase);
+    else
+        dkdv_block<false>(a, head, a.nkb - 1 - blk, lbase);
+}
+
 // ---------------------------------------------------------------------------
-// dQ: one workgroup per 256 query rows.
+// dQ: one workgroup per 256 query rows.  SEG: keys through the segment table
+// (streaming step), otherwise one contiguous [T, H, 128] block.
 // ---------------------------------------------------------------------------
+template <bool SEG>
 __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     constexpr int NS = 8, NT = 4, NSTG = 4;
     __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * kTile];
     __shared__ __attribute__((aligned(16))) uint16_t sV[NSTG * kTile];
+    __shared__ const uint16_t *sSegK[SEG ? kMaxKeyFrames : 1], *sSegV[SEG ? kMaxKeyFrames : 1];
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -359,7 +430,16 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     const long hoff = (long)head * kD;
     const int qi = q0 + 32 * wave + n;
     const bool qv = qi < a.T;
-    auto key_limit = [&](int i) __attribute__((always_inline)) { return (int)min((long)(i / a.kpf + 1) * a.kpf, (long)a.T); };
+    auto key_limit = [&](int i) __attribute__((always_inline)) {
+        return (int)min((long)a.prefix + (long)(i / a.kpf + 1) * a.kpf, (long)a.Tk);
+    };
+    if (SEG) {
+        for (int f = tid; f < a.nseg; f += 512) {
+            sSegK[f] = (const uint16_t *)a.kseg[f];
+            sSegV[f] = (const uint16_t *)a.vseg[f];
+        }
+        __syncthreads();
+    }
     const int lim = key_limit(qv ? qi : a.T - 1);
     const int lim_lo = key_limit(q0);
     const int lim_hi = key_limit(min(q0 + 255, a.T - 1));
@@ -392,9 +472,17 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     const uint32_t lk = lds_addr((lds_u16 *)sK), lv = lds_addr((lds_u16 *)sV);
     auto issue = [&](int j, auto S) __attribute__((always_inline)) {
         constexpr int st = decltype(S)::value;
-        const int row = min(j * 32 + prow, a.T - 1);
-        const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + col2;
-        dma16x2((uint64_t)a.k, (uint64_t)a.v, off, off, lk + st * kTile * 2 + 1024 * wave, lv + st * kTile * 2 + 1024 * wave);
+        const int row = min(j * 32 + prow, a.Tk - 1);
+        if (SEG) {
+            const int f = seg_of(row, a);
+            const long o = (long)(row - f * a.seg_len) * a.ld + hoff + col2 / 2;
+            dma16_lane(sSegK[f] + o, lk + st * kTile * 2 + 1024 * wave);
+            dma16_lane(sSegV[f] + o, lv + st * kTile * 2 + 1024 * wave);
+        } else {
+            const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + col2;
+            dma16x2((uint64_t)a.k, (uint64_t)a.v, off, off, lk + st * kTile * 2 + 1024 * wave,
+                    lv + st * kTile * 2 + 1024 * wave);
+        }
     };
 
     // Plain reads (A operand of S^T = K Q^T and dP^T = V dO^T: key row n,
@@ -523,14 +611,37 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
     a.rows = (float *)p.ws;
     a.qt = (uint16_t *)(a.rows + ntile * 64);
     a.dot = a.qt + ntile * kTile;
+    a.Tk = a.T;
+    a.seg_len = a.T;
+    // A streaming step with an empty prefix is the full form over the chunk.
+    const bool seg = p.nseg > 0 && p.prefix > 0;
+    if (seg) {
+        for (int f = 0; f < p.nseg; ++f) {
+            a.kseg[f] = p.kseg[f];
+            a.vseg[f] = p.vseg[f];
+        }
+        a.nseg = p.nseg;
+        a.seg_len = (int32_t)p.seg_len;
+        a.prefix = (int32_t)p.prefix;
+        a.Tk = a.prefix + a.T;
+        if (p.dk_prefix) {
+            a.nkbp = (int32_t)((p.prefix + 255) / 256);
+            a.dkp = (uint16_t *)p.dk_prefix;
+            a.dvp = (uint16_t *)p.dv_prefix;
+        }
+    }
+    a.inv_seg_len = 1.0f / (float)a.seg_len;
 
     hipLaunchKernelGGL(attn_bwd_prep, dim3(a.nqt, p.H), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
-    a.nwg = p.H * a.nkb;
+    a.nwg = p.H * (a.nkb + a.nkbp);
     hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     a.nwg = p.H * a.nqb;
-    hipLaunchKernelGGL(attn_bwd_dq_d128, dim3(a.nwg), dim3(512), 0, stream, a);
+    if (seg)
+        hipLaunchKernelGGL(attn_bwd_dq_d128<true>, dim3(a.nwg), dim3(512), 0, stream, a);
+    else
+        hipLaunchKernelGGL(attn_bwd_dq_d128<false>, dim3(a.nwg), dim3(512), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -493,6 +493,68 @@ int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, con
     return ok();
 }
 
+namespace {
+
+// Position-aware reference (rtr_kv_set_ref_rope): the rotation applied to the
+// reference K for the current cache state -- the reference sits right in front
+// of the oldest frame a step sees.
+int64_t ref_shift(const rtr_kv_cache *kv) {
+    const int64_t oldest = (kv->count > 0 ? kv->slot_frame_id[kv->head] : kv->next_id) + kv->pos_offset;
+    return oldest - kv->ref_frames;
+}
+
+// Reference keys a step attends to: the stored ones, or their rotated view,
+// re-rotated only when the shift or the reference has changed since the last
+// rotation enqueued.
+int ref_keys(const rtr_kv_cache *kv, hipStream_t stream, const void **kref) {
+    *kref = kv->k_ref;
+    if (!(kv->k_ref_view && kv->ref_frames > 0)) return RTR_OK;
+    const int64_t shift = ref_shift(kv);
+    if (!(kv->view_valid && kv->view_shift == shift && kv->view_gen == kv->ref_gen &&
+          kv->view_frames == kv->ref_frames)) {
+        rtr::RotateJob j;
+        j.src = kv->k_ref;
+        j.dst = kv->k_ref_view;
+        j.rows = (int64_t)kv->ref_frames * kv->kpf * kv->H;
+        j.d = kv->d;
+        j.dt = kv->dt;
+        j.pairs = kv->rope_pairs;
+        j.base = kv->rope_base;
+        j.shift = shift;
+        if (const hipError_t e = rtr::launch_ref_rotate(j, stream)) return hip_fail(e, "reference rotation launch");
+        kv->view_valid = true;
+        kv->view_shift = shift;
+        kv->view_gen = kv->ref_gen;
+        kv->view_frames = kv->ref_frames;
+    }
+    *kref = kv->k_ref_view;
+    return RTR_OK;
+}
+
+// Key segment table of a step, one latent frame per segment: the reference
+// frames, the window frames oldest first, then the chunk's frames.
+int key_segments(const rtr_kv_cache *kv, const void *kref, const void *k, const void *v, int32_t chunk_frames,
+                 const void **kseg, const void **vseg) {
+    const int64_t fb = frame_bytes(kv);
+    int nseg = 0;
+    for (int r = 0; r < kv->ref_frames; ++r) {
+        kseg[nseg] = (const char *)kref + r * fb;
+        vseg[nseg++] = (const char *)kv->v_ref + r * fb;
+    }
+    for (int i = 0; i < kv->count; ++i) {
+        const int slot = (kv->head + i) % kv->W;
+        kseg[nseg] = (const char *)kv->k_ring + slot * fb;
+        vseg[nseg++] = (const char *)kv->v_ring + slot * fb;
+    }
+    for (int c = 0; c < chunk_frames; ++c) {
+        kseg[nseg] = (const char *)k + c * fb;
+        vseg[nseg++] = (const char *)v + c * fb;
+    }
+    return nseg;
+}
+
+}  // namespace
+
 int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
                          float scale, void *workspace, size_t workspace_bytes,
@@ -538,49 +600,12 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
         if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws)) return rc;
     }
 
-    // Position-aware reference: rotate the reference K so that it sits right
-    // in front of the oldest frame this call sees (re-rotated only when that
-    // position or the reference changes).
-    const void *kref = kv->k_ref;
-    if (kv->k_ref_view && kv->ref_frames > 0) {
-        const int64_t oldest = (kv->count > 0 ? kv->slot_frame_id[kv->head] : kv->next_id) + kv->pos_offset;
-        const int64_t shift = oldest - kv->ref_frames;
-        if (!(kv->view_valid && kv->view_shift == shift && kv->view_gen == kv->ref_gen &&
-              kv->view_frames == kv->ref_frames)) {
-            rtr::RotateJob j;
-            j.src = kv->k_ref;
-            j.dst = kv->k_ref_view;
-            j.rows = (int64_t)kv->ref_frames * kv->kpf * kv->H;
-            j.d = kv->d;
-            j.dt = kv->dt;
-            j.pairs = kv->rope_pairs;
-            j.base = kv->rope_base;
-            j.shift = shift;
-            if (const hipError_t e = rtr::launch_ref_rotate(j, (hipStream_t)stream)) return hip_fail(e, "reference rotation launch");
-            kv->view_valid = true;
-            kv->view_shift = shift;
-            kv->view_gen = kv->ref_gen;
-            kv->view_frames = kv->ref_frames;
-        }
-        kref = kv->k_ref_view;
-    }
+    const void *kref = nullptr;
+    if (int rc = ref_keys(kv, (hipStream_t)stream, &kref)) return rc;
 
     rtr::AttnProblem p;
     p.ws = ws;
-    int nseg = 0;
-    for (int r = 0; r < kv->ref_frames; ++r) {
-        p.kseg[nseg] = (const char *)kref + r * fb;
-        p.vseg[nseg++] = (const char *)kv->v_ref + r * fb;
-    }
-    for (int i = 0; i < kv->count; ++i) {
-        const int slot = (kv->head + i) % kv->W;
-        p.kseg[nseg] = (const char *)kv->k_ring + slot * fb;
-        p.vseg[nseg++] = (const char *)kv->v_ring + slot * fb;
-    }
-    for (int c = 0; c < chunk_frames; ++c) {
-        p.kseg[nseg] = (const char *)k + c * fb;
-        p.vseg[nseg++] = (const char *)v + c * fb;
-    }
+    const int nseg = key_segments(kv, kref, k, v, chunk_frames, p.kseg, p.vseg);
     p.q = q;
     p.o = o;
     p.lse = lse;
@@ -597,6 +622,102 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
     p.out_dtype = out_dtype;
     const hipError_t e = rtr::launch_attention(p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                             const void *o, const float *lse, const void *d_o, int32_t chunk_frames,
+                             int32_t block_frames, void *dq, void *dk, void *dv, void *dk_cache,
+                             void *dv_cache, float scale, void *workspace, size_t workspace_bytes,
+                             rtr_stream stream) {
+    if (int rc = check_cache(kv)) return rc;
+    if (kv->dt != RTR_BF16) return fail(RTR_EUNSUPPORTED, "backward supports bf16 only");
+    if (kv->d != 128) return fail(RTR_EUNSUPPORTED, "backward head dim %d not supported (128)", kv->d);
+    if (chunk_frames < 1 || chunk_frames > RTR_MAX_CHUNK)
+        return fail(RTR_EUNSUPPORTED, "chunk_frames=%d outside [1, %d]", chunk_frames, RTR_MAX_CHUNK);
+    if (block_frames < 1) return fail(RTR_EINVAL, "block_frames=%d must be >= 1", block_frames);
+    if (int rc = check_scale(scale)) return rc;
+    const int32_t mask_frames = block_frames < chunk_frames ? block_frames : chunk_frames;
+    const int64_t Tq = (int64_t)chunk_frames * kv->kpf;
+    const int64_t P = (int64_t)(kv->ref_frames + kv->count) * kv->kpf;
+    if (Tq * kv->H * kv->d >= ((int64_t)1 << 31)) return fail(RTR_EUNSUPPORTED, "chunk tokens * H * d must be below 2^31");
+    if ((dk_cache == nullptr) != (dv_cache == nullptr))
+        return fail(RTR_EINVAL, "dk_cache and dv_cache must both be NULL or both non-NULL");
+    const void *in[6] = {q, k, v, o, lse, d_o};
+    for (const void *x : in)
+        if (!x) return fail(RTR_EINVAL, "q, k, v, o, lse and d_o must be non-NULL");
+    void *out[5] = {dq, dk, dv, dk_cache, dv_cache};
+    for (int i = 0; i < 3; ++i)
+        if (!out[i]) return fail(RTR_EINVAL, "dq, dk and dv must be non-NULL");
+    for (const void *x : {q, k, v, o, d_o, (const void *)dq, (const void *)dk, (const void *)dv,
+                          (const void *)dk_cache, (const void *)dv_cache})
+        if (!aligned16(x)) return fail(RTR_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) != 0) return fail(RTR_EINVAL, "lse must be 4-byte aligned");
+    const int64_t fb = frame_bytes(kv);
+    const int64_t tb = fb * chunk_frames, lb = Tq * kv->H * 4, pb = P * kv->H * kv->d * 2;
+    const int64_t out_sz[5] = {tb, tb, tb, dk_cache ? pb : 0, dv_cache ? pb : 0};
+    const void *src[10] = {q, k, v, o, lse, d_o, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
+    const int64_t src_sz[10] = {tb, tb, tb, tb, lb, tb, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 10; ++j)
+            if (overlaps(out[i], out_sz[i], src[j], src_sz[j])) return fail(RTR_EINVAL, "an output overlaps an input or the cache");
+        if (kv->k_ref_view && overlaps(out[i], out_sz[i], kv->k_ref_view, fb * kv->R_cap))
+            return fail(RTR_EINVAL, "an output overlaps the rotated reference");
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(out[i], out_sz[i], out[j], out_sz[j])) return fail(RTR_EINVAL, "outputs overlap");
+    }
+    size_t need = 0;
+    if (const hipError_t e = rtr::attention_bwd_workspace_bytes(Tq, kv->H, &need)) return hip_fail(e, "workspace size");
+    if (!workspace) return fail(RTR_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(RTR_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    for (int j = 0; j < 10; ++j)
+        if (overlaps(workspace, (int64_t)need, src[j], src_sz[j])) return fail(RTR_EINVAL, "workspace overlaps an input or the cache");
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(workspace, (int64_t)need, out[i], out_sz[i])) return fail(RTR_EINVAL, "workspace overlaps an output");
+    if (kv->k_ref_view && overlaps(workspace, (int64_t)need, kv->k_ref_view, fb * kv->R_cap))
+        return fail(RTR_EINVAL, "workspace overlaps the rotated reference");
+
+    const void *kref = nullptr;
+    if (int rc = ref_keys(kv, (hipStream_t)stream, &kref)) return rc;
+    rtr::BwdProblem p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.dout = d_o;
+    p.lse = lse;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.T = Tq;
+    p.tokens_per_frame = (int64_t)mask_frames * kv->kpf;
+    p.H = kv->H;
+    p.scale = resolve_scale(scale, kv->d);
+    p.ws = workspace;
+    p.nseg = key_segments(kv, kref, k, v, chunk_frames, p.kseg, p.vseg);
+    p.seg_len = kv->kpf;
+    p.prefix = P;
+    if (dk_cache && P > 0) {
+        p.dk_prefix = dk_cache;
+        p.dv_prefix = dv_cache;
+    }
+    if (const hipError_t e = rtr::launch_attention_bwd(p, (hipStream_t)stream)) return hip_fail(e, "backward launch");
+    // A rotated reference: its keys' gradient so far is with respect to the
+    // rotated view; the rotation is orthogonal, so rotating back by the same
+    // angle gives the gradient with respect to the stored keys.
+    if (dk_cache && P > 0 && kref != kv->k_ref) {
+        rtr::RotateJob j;
+        j.src = dk_cache;
+        j.dst = dk_cache;
+        j.rows = (int64_t)kv->ref_frames * kv->kpf * kv->H;
+        j.d = kv->d;
+        j.dt = kv->dt;
+        j.pairs = kv->rope_pairs;
+        j.base = kv->rope_base;
+        j.shift = -kv->view_shift;
+        if (const hipError_t e = rtr::launch_ref_rotate(j, (hipStream_t)stream)) return hip_fail(e, "gradient rotation launch");
+    }
     return ok();
 }
 

@@ -61,6 +61,16 @@ struct BwdProblem {
     int32_t H = 0;
     float scale = 0.f;
     void *ws = nullptr;
+    // Streaming step (nseg > 0): q, o, lse, dout and dq hold the chunk's T
+    // rows and k, v, dk, dv the chunk's own keys; every key the rows see --
+    // `prefix` cached keys, then the chunk's -- also lies in the segment table
+    // (as in AttnProblem).  dk_prefix / dv_prefix, when non-null, receive the
+    // prefix keys' gradients, [prefix, H, 128].
+    const void *kseg[kMaxKeyFrames] = {};
+    const void *vseg[kMaxKeyFrames] = {};
+    int32_t nseg = 0;
+    int64_t seg_len = 0, prefix = 0;
+    void *dk_prefix = nullptr, *dv_prefix = nullptr;
 };
 
 hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes);
@@ -78,7 +88,7 @@ hipError_t launch_frame_copies(const CopyJobs &jobs, hipStream_t stream);
 
 // Temporal rotary re-encoding of `rows` head rows of d elements: pairs
 // (2i, 2i+1), i < pairs, rotated by shift * base^(-i / pairs); src and dst are
-// 16-byte aligned and do not overlap.
+// 16-byte aligned and either equal (in place) or disjoint.
 struct RotateJob {
     const void *src = nullptr;
     void *dst = nullptr;

@@ -61,6 +61,9 @@ _SIGNATURES = {
                                             _c_f32, _vp, ctypes.c_size_t, _vp]),
     "rtr_attn_stream_step_blocked": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
                                                     ctypes.c_int, _c_f32, _vp, ctypes.c_size_t, _vp]),
+    "rtr_attn_stream_step_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                                _vp, _vp, _vp, _vp, _vp, _c_f32, _vp, ctypes.c_size_t,
+                                                _vp]),
     "rtr_kv_set_ref_rope": (ctypes.c_int, [_vp, _vp, _c_i32, _c_f32, _c_i64]),
     "rtr_kv_reset_ref": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _c_i32, _c_i32, _vp]),
     "rtr_kv_get_state": (ctypes.c_int, [_vp, ctypes.POINTER(rtr_kv_state)]),
@@ -210,6 +213,35 @@ def rtr_attn_block_causal_bwd(q, k, v, o, lse, d_o, tokens_per_frame, dq=None, d
 
 
 # ---------------------------------------------------------------- the cache
+def rtr_attn_stream_step_bwd(kv, q, k, v, o, lse, d_o, chunk_frames, block_frames=1, dq=None, dk=None,
+                             dv=None, dk_cache=None, dv_cache=None, want_cache_grads=False, scale=0.0,
+                             workspace=None, stream=None):
+    """Gradients of a streaming step from its forward o and lse (the cache in
+    the state it had then).  Returns (dq, dk, dv, dk_cache, dv_cache); the
+    cache gradients ([P, H, d], reference then window frames oldest first) are
+    None unless given or want_cache_grads."""
+    import torch
+    Tq, H, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if want_cache_grads and dk_cache is None:
+        st = rtr_kv_get_state(kv)
+        P = (st.ref_frames + st.count) * kv.kpf
+        dk_cache = torch.empty((P, H, d), dtype=q.dtype, device=q.device)
+        dv_cache = torch.empty((P, H, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, rtr_attn_bwd_workspace_size(Tq, H, d)), dtype=torch.uint8,
+                                device=q.device)
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().rtr_attn_stream_step_bwd(kv.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                          _ptr(d_o), int(chunk_frames), int(block_frames), _ptr(dq),
+                                          _ptr(dk), _ptr(dv), _ptr(dk_cache), _ptr(dv_cache),
+                                          float(scale), ws, ws_bytes, _stream(stream, q.device)),
+           "rtr_attn_stream_step_bwd")
+    return dq, dk, dv, dk_cache, dv_cache
+
+
 class KVCache:
     """One layer's reference-anchored rolling KV cache (handle + buffers).
 

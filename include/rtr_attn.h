@@ -216,6 +216,35 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
                                  rtr_dtype out_dtype, float scale, void *workspace,
                                  size_t workspace_bytes, rtr_stream stream);
 
+/* ------------------------------------------------------------------------
+ * Gradients of one streaming step (Key Designs 2 and 4: the step's Attn over
+ * [reference | window | chunk]; Key Designs 3 trains the causal generator by
+ * rolling it out over this cache, so its gradient passes back through every
+ * step).  kv must be in the state it had when the forward step ran (restore a
+ * snapshot if the ring has moved on); q, k, v: the chunk's [C*k, H, d]; o and
+ * lse: that forward step's output and its natural-log LSE [H, C*k] (from
+ * rtr_attn_stream_step_blocked with the same chunk_frames, block_frames and
+ * scale); d_o: upstream gradient [C*k, H, d].
+ * Outputs (device, caller-owned, overwritten):
+ *   dq, dk, dv : [C*k, H, d], the chunk's gradients
+ *   dk_cache, dv_cache : [P, H, d], P = (ref_frames + count) * k, gradients
+ *             of the cached keys and values in the order the step reads them
+ *             (reference frames, then window frames oldest first); with a
+ *             position-aware reference (rtr_kv_set_ref_rope) dk_cache's
+ *             reference rows are with respect to the stored, unrotated keys.
+ *             Both NULL: the cache is treated as constant and not
+ *             differentiated (P == 0 writes nothing).
+ * bf16 cache, d = 128 only.  workspace: rtr_attn_bwd_workspace_size(C*k, H,
+ * d) bytes, 256-byte aligned, overlapping no argument.  No output may overlap
+ * an input, the cache buffers or another output.  Limits: C*k * H * d < 2^31.
+ * Returns RTR_OK or a negative rtr_status; nothing is enqueued on an error.
+ * ---------------------------------------------------------------------- */
+int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                             const void *o, const float *lse, const void *d_o, int32_t chunk_frames,
+                             int32_t block_frames, void *dq, void *dk, void *dv, void *dk_cache,
+                             void *dv_cache, float scale, void *workspace, size_t workspace_bytes,
+                             rtr_stream stream);
+
 /* Condition switch (Key Designs 4).  First the reference: KEEP leaves it,
  * REPLACE anchors ref_frames (1..R_cap) new frames k_ref, v_ref
  * ([ref_frames, k, H, d] device; both NULL means the caller already wrote

@@ -351,3 +351,48 @@ def test_ref_rope_rejections():
     kv0 = _cache(W=3, R=0)
     assert L.rtr_kv_set_ref_rope(kv0.handle, view, 8, 10000.0, 1) == rtr.RTR_ESTATE
     assert fb > 0
+
+
+def _sbwd(kv, **kw):
+    base = FAKE + 256 * MB
+    a = dict(q=base, k=base + MB, v=base + 2 * MB, o=base + 3 * MB, lse=base + 4 * MB,
+             do=base + 5 * MB, C=2, B=1, dq=base + 6 * MB, dk=base + 7 * MB, dv=base + 8 * MB,
+             dkc=base + 9 * MB, dvc=base + 10 * MB, scale=0.0, ws=base + 16 * MB, ws_bytes=16 * MB,
+             stream=None)
+    a.update(kw)
+    return rtr.lib().rtr_attn_stream_step_bwd(kv.handle, a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                              a["do"], a["C"], a["B"], a["dq"], a["dk"], a["dv"],
+                                              a["dkc"], a["dvc"], a["scale"], a["ws"], a["ws_bytes"],
+                                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(C=0), rtr.RTR_EUNSUPPORTED),
+    (dict(C=rtr.RTR_MAX_CHUNK + 1), rtr.RTR_EUNSUPPORTED),
+    (dict(B=0), rtr.RTR_EINVAL),
+    (dict(q=None), rtr.RTR_EINVAL),
+    (dict(lse=None), rtr.RTR_EINVAL),
+    (dict(dv=None), rtr.RTR_EINVAL),
+    (dict(dvc=None), rtr.RTR_EINVAL),                   # cache gradients come in pairs
+    (dict(dk=FAKE + 256 * MB + 7 * MB + 8), rtr.RTR_EINVAL),   # misaligned
+    (dict(lse=FAKE + 256 * MB + 4 * MB + 1), rtr.RTR_EINVAL),  # misaligned lse
+    (dict(dq=FAKE + 64), rtr.RTR_EINVAL),               # dq overlaps the ring
+    (dict(dkc=FAKE + 256 * MB + 6 * MB + 16), rtr.RTR_EINVAL),  # dk_cache overlaps dq
+    (dict(ws=None), rtr.RTR_EINVAL),
+    (dict(ws=FAKE + 256 * MB + 16 * MB + 16), rtr.RTR_EINVAL),  # not 256-byte aligned
+    (dict(ws_bytes=100), rtr.RTR_EINVAL),
+    (dict(ws=FAKE + 256 * MB + 5 * MB), rtr.RTR_EINVAL),       # overlaps d_o
+    (dict(scale=float("inf")), rtr.RTR_EINVAL),
+])
+def test_stream_step_bwd_rejects_before_launch(kw, code):
+    kv = _cache(W=3, R=1, d=128)
+    rtr.rtr_kv_commit_inplace(kv, 2)
+    assert _sbwd(kv, **kw) == code
+    assert rtr.lib().rtr_last_error()
+
+
+def test_stream_step_bwd_rejects_unsupported_caches():
+    for kv in (_cache(W=3, R=1, d=64), _cache(W=3, R=1, d=128, dtype=rtr.RTR_F32)):
+        assert _sbwd(kv) == rtr.RTR_EUNSUPPORTED
+    assert rtr.lib().rtr_attn_stream_step_bwd(None, *([FAKE] * 6), 1, 1, *([FAKE] * 5), 0.0, FAKE,
+                                              MB, None) == rtr.RTR_EINVAL
