@@ -132,7 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="wan13b_stream_step",
                     choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal",
-                             "full_block_causal_bwd", "wan13b_cross_step", "rollout"],
+                             "full_block_causal_bwd", "wan13b_stream_step_bwd", "wan13b_cross_step",
+                             "rollout"],
                     help="rollout: one step is a whole 240-chunk rollout (stream step, commit, "
                          "and a reference swap every 60 chunks)")
     ap.add_argument("--cpu-heads", type=int, default=12,
@@ -146,6 +147,9 @@ def main():
     ap.add_argument("--ref-rope", action="store_true",
                     help="streaming workloads: position-aware reference (re-encoded in front of the "
                          "window every step; 22 temporal rotary pairs, as Wan's 44 temporal dims)")
+    ap.add_argument("--no-cache-grads", action="store_true",
+                    help="wan13b_stream_step_bwd: treat the cache as constant (no gradients of the "
+                         "cached keys and values)")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -168,6 +172,8 @@ def main():
         return rollout(args, w, dev)
     if args.workload == "full_block_causal_bwd":
         return backward(args, w, dev)
+    if args.workload == "wan13b_stream_step_bwd":
+        return stream_backward(args, w, dev)
     if args.workload == "wan13b_cross_step":
         return cross(args, w, dev)
 
@@ -387,6 +393,119 @@ def backward(args, w, dev):
                                "cores": int(cores), "kind": "oracle",
                                "sample": f"oracle.attn_bwd_rows (dQ) on {len(rows)} rows x "
                                          f"{len(heads)} heads", "seconds": round(dt, 3)}
+    print(json.dumps(out), flush=True)
+
+
+def stream_backward(args, w, dev):
+    """Gradients of one streaming step (the Self-Forcing-style rollout's
+    attention backward): one step is one rtr_attn_stream_step_bwd call --
+    prep, dK/dV of the chunk keys and of the cached keys in one launch, and dQ
+    over the segmented keys -- on resident inputs, o and lse from the library's
+    own streaming step.  Algorithmic work per visible (row, key) pair: 10 d
+    (S recomputed, dP, dV, dK, dQ); without cache gradients the cached keys'
+    pairs count 6 d (S, dP, dQ)."""
+    import torch
+    from causal_attention_frame_amd import inputs as gen
+    from causal_attention_frame_amd import rtr
+
+    kpf, H, d, C, W = w["k"], w["H"], w["d"], w["C"], w["W"]
+    R = args.ref_frames or w["R"]
+    x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"])
+    do_h = gen.normal((C * kpf, H, d), "bf16", 0, w["wid"], 0, gen.TAG_DO)
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    kr = torch.empty((W, kpf, H, d), dtype=torch.bfloat16, device=dev)
+    vr = torch.empty_like(kr)
+    kf = torch.empty((R, kpf, H, d), dtype=torch.bfloat16, device=dev)
+    vf = torch.empty_like(kf)
+    kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, to_dev(x["ref_k"]), to_dev(x["ref_v"]), R, -1)
+    rtr.rtr_kv_append_evict(kv, to_dev(x["ring_k"]), to_dev(x["ring_v"]), W)
+    q, k, v, do = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]), to_dev(do_h)
+    o, lse = rtr.rtr_attn_stream_step(kv, q, k, v, C, want_lse=True)
+    Tq, P = C * kpf, (R + W) * kpf
+    ws = torch.empty(rtr.rtr_attn_bwd_workspace_size(Tq, H, d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    cache_grads = not args.no_cache_grads
+    dkc = torch.empty((P, H, d), dtype=torch.bfloat16, device=dev) if cache_grads else None
+    dvc = torch.empty_like(dkc) if cache_grads else None
+    stream = torch.cuda.current_stream(dev)
+    chunk_pairs = stream_pairs_per_head(kpf, C, 0)
+    prefix_pairs = Tq * P
+    flops = 10 * d * H * chunk_pairs + (10 if cache_grads else 6) * d * H * prefix_pairs
+
+    def step():
+        rtr.rtr_attn_stream_step_bwd(kv, q, k, v, o, lse, do, C, 1, dq, dk, dv, dkc, dvc, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = elapsed * 1e3 / args.steps
+    call_s = float(call_ms.mean()) * 1e-3
+    config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
+              "chunk_frames": C, "window_frames": W, "ref_frames": R, "query_tokens": Tq,
+              "key_tokens": P + Tq, "cache_grads": cache_grads}
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": config,
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(flops / call_s / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic(args.workload) if cache_grads and R == w["R"] else None,
+            "kernel": "attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128<SEG> (one call)",
+            "kernel_avg_us": round(call_s * 1e6, 2),
+            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            "algorithmic_flop_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            cores = os.cpu_count()
+        h = list(range(min(H, args.cpu_heads)))   # dense float64 oracle, one head at a time
+        pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
+        pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
+        args1 = (pk[:, h], pv[:, h], x["q"].values[:, h], x["k"].values[:, h], x["v"].values[:, h],
+                 do_h.values[:, h], kpf)
+        t1 = time.perf_counter()
+        for j in range(len(h)):
+            oracle.attn_stream_step_bwd(*(a[:, j:j + 1] for a in args1[:6]), kpf)
+        dt = time.perf_counter() - t1
+        f1 = 10 * d * len(h) * (chunk_pairs + prefix_pairs)
+        out["cpu_baseline"] = {"value": f1 / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+                               "kind": "oracle",
+                               "sample": f"oracle.attn_stream_step_bwd (dense float64, every "
+                                         f"gradient) on heads 0..{len(h) - 1} of {H}",
+                               "seconds": round(dt, 3)}
     print(json.dumps(out), flush=True)
 
 
