@@ -98,11 +98,12 @@ __device__ inline int swap23(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 
 // row r at chunk c ^ (r mod 16).
 __device__ inline int swz_plain(int r) { return r & 15; }
 // Row-major tile read both plainly (16-byte reads of 16 rows) and transposed
-// (ds_read_b64_tr_b16 over 4 rows x 32 bytes): chunk c of row r at chunk
-// c ^ s(r), s(r) = 2 (r mod 8) + (r / 8 mod 2) -- a permutation of 0..15 over
-// any 16 consecutive rows, whose values shifted right by one also differ
-// over any 4 consecutive rows starting at a multiple of 4.
-__device__ inline int swz_dual(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// (ds_read_b64_tr_b16: one pass serves 32 lanes, 4 rows x 64 bytes): chunk c
+// of row r at chunk c ^ s(r), s(r) = 4 (r mod 4) + (r / 4 mod 4) -- a
+// permutation of 0..15 over any 16 consecutive rows, whose values shifted
+// right by two also differ over any 4 consecutive rows starting at a multiple
+// of 4, so neither read has a bank conflict.
+__device__ inline int swz_dual(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // acc += A B with the accumulator held in AGPRs.  This file is built with
 // builtin MFMAs in VGPR form (their results feed VALU code); the long-lived

@@ -401,10 +401,13 @@ void attn_fwd_bf16(const KArgs a) {
 //   K: the 16-byte chunks of row r are XOR-swizzled by r mod 16: a
 //      ds_read_b128 serves 16 lanes (rows n..n+15 of the MFMA A operand) per
 //      pass over the 64 banks, and the swizzle gives them 16 distinct chunks;
-//   V: the 32-byte chunk pairs of row r are XOR-swizzled by r mod 4 and the
+//   V: the 64-byte chunk quads of row r are XOR-swizzled by r mod 4 and the
 //      tile is read with ds_read_b64_tr_b16, whose 16-lane transpose hands each
 //      lane one d column over 4 keys -- the V^T A operand of the PV MFMA in the
-//      key order of the S^T accumulator, with no transposed copy anywhere.
+//      key order of the S^T accumulator, with no transposed copy anywhere.  A
+//      pass of that read serves 32 lanes, 4 key rows x 64 bytes; the swizzle
+//      puts the 4 rows in 4 distinct 64-byte bank groups (a 32-byte pair
+//      swizzle left rows r and r ^ 1 on the same banks, a 2-way conflict).
 // Synchronisation: one s_barrier per tile, after each wave has waited for its
 // own DMA of that tile (vmcnt), so later prefetches stay in flight.
 //
@@ -531,7 +534,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
 #pragma unroll
     for (int i = 0; i < 1; ++i) {
         kch[i] = pch ^ (4 * (wave & 3) + lr);           // (row mod 16) = 4 (wave mod 4) + lr
-        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
+        vch[i] = (((pch >> 2) ^ lr) << 2) | (pch & 3);  // (row mod 4) = lr
         kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
@@ -592,10 +595,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     for (int s = 0; s < NS; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 15)) << 3);
     const int G = lane >> 4, sl = lane & 15;
     const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
-    const lds_u16 *vfp[2];
+    const lds_u16 *vfp[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-        vfp[t] = vbase + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+    for (int t = 0; t < NT; ++t)
+        vfp[t] = vbase + vrow * D + ((2 * (t ^ (sl >> 2)) + (G & 1)) << 4) + 4 * (sl & 3);
 
     // Softmax with a fixed per-row exponent reference (log2 units): P =
     // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
@@ -627,8 +630,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s) * D);
-                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s + 8) * D);
+                vf[t][s][0] = lds_tr16(vfp[t] + st * TILE + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t] + st * TILE + (16 * s + 8) * D);
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
 #pragma unroll
     for (int i = 0; i < 1; ++i) {
         kch[i] = pch ^ (4 * (wave & 3) + lr);           // (row mod 16) = 4 (wave mod 4) + lr
-        vch[i] = (((pch >> 1) ^ lr) << 1) | (pch & 1);  // (row mod 4) = lr
+        vch[i] = (((pch >> 2) ^ lr) << 2) | (pch & 3);  // (row mod 4) = lr
         kvo[i] = (uint32_t)(((long)lr * a.ld + kch[i] * 8) * 2);
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
@@ -1062,10 +1065,10 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     for (int s = 0; s < NS; ++s) kfp[s] = kbase + n * D + (((2 * s + g) ^ (n & 15)) << 3);
     const int G = lane >> 4, sl = lane & 15;
     const int vrow = 4 * (G >> 1) + (sl >> 2);  // + 16 key-step + 8 half
-    const lds_u16 *vfp[2];
+    const lds_u16 *vfp[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-        vfp[t] = vbase + vrow * D + (((2 * t + (G & 1)) ^ (sl >> 2)) << 4) + 4 * (sl & 3);
+    for (int t = 0; t < NT; ++t)
+        vfp[t] = vbase + vrow * D + ((2 * (t ^ (sl >> 2)) + (G & 1)) << 4) + 4 * (sl & 3);
 
     // Softmax with a fixed per-row exponent reference (log2 units): P =
     // exp2(s * c - mref).  mref is the row max of the row's first key tile, so
@@ -1094,8 +1097,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                vf[t][s][0] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s) * D);
-                vf[t][s][1] = lds_tr16(vfp[t & 1] + st * TILE + (t >> 1) * 64 + (16 * s + 8) * D);
+                vf[t][s][0] = lds_tr16(vfp[t] + st * TILE + (16 * s) * D);
+                vf[t][s][1] = lds_tr16(vfp[t] + st * TILE + (16 * s + 8) * D);
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
