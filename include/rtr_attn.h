@@ -154,8 +154,10 @@ int rtr_attn_block_causal_bwd(const void *q, const void *k, const void *v, const
                               rtr_dtype dtype, float scale, void *workspace,
                               size_t workspace_bytes, rtr_stream stream);
 
-/* Workspace bytes rtr_attn_block_causal_bwd needs: per head and 32-row tile,
- * 256 bytes of row statistics and 16 KiB of transposed Q and dO. */
+/* Workspace bytes rtr_attn_block_causal_bwd (T tokens) and
+ * rtr_attn_stream_step_bwd (T = chunk_frames * k query rows) need: per head
+ * and 32-row tile, 256 bytes of row statistics and 16 KiB of transposed Q and
+ * dO. */
 int rtr_attn_bwd_workspace_size(int64_t T, int32_t H, int32_t d, size_t *bytes);
 
 /* ------------------------------------------------------------------------
