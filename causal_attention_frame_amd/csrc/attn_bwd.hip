@@ -327,6 +327,20 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
 #pragma unroll
         for (int k = 0; k < NS; ++k)
             d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd((aq + so) ^ (32u * k), 2 * RDO), rd(pv, 1024 * k), d0, 0, 0, 0);
+        // Issue order of the two products: fragment reads two (S) or four (dP)
+        // at a time, each pair of MFMAs after the reads it needs.  Left to
+        // itself the compiler read one fragment, waited and multiplied, and in
+        // the prefix-key blocks spilled a K fragment to scratch every tile.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
         const int q0 = (t0 + i) * 32 + 4 * g;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -343,10 +357,23 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
         for (int h = 0; h < 2; ++h)
             pb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s0[8 * h], s0[8 * h + 1]), pack_bf16x2(s0[8 * h + 2], s0[8 * h + 3]),
                                                      pack_bf16x2(s0[8 * h + 4], s0[8 * h + 5]), pack_bf16x2(s0[8 * h + 6], s0[8 * h + 7])});
+        // The accumulating MFMAs are inline assembly, which the scheduler does
+        // not look into: it would read each A fragment right before its MFMA
+        // and wait.  Four fragments are read ahead of their four MFMAs instead
+        // (the scheduling fence keeps the reads in front).
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t2 = 0; t2 < NT; t2 += 2) {
+            bf16x8 fv[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) mfma_acc(dvt[t], rd(pt[h] + so, 2 * (RDOT - RQT) + 2048 * t), pb[h]);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) fv[2 * t + h] = rd(pt[h] + so, 2 * (RDOT - RQT) + 2048 * (t2 + t));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) mfma_acc(dvt[t2 + t], fv[2 * t + h], pb[h]);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const f32x4 dd = *(const lds_f32x4 *)((const lds_u16 *)(uintptr_t)(pr + rso) + 64 + 16 * j);
@@ -358,9 +385,18 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
             sb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(d0[8 * h], d0[8 * h + 1]), pack_bf16x2(d0[8 * h + 2], d0[8 * h + 3]),
                                                      pack_bf16x2(d0[8 * h + 4], d0[8 * h + 5]), pack_bf16x2(d0[8 * h + 6], d0[8 * h + 7])});
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t2 = 0; t2 < NT; t2 += 2) {
+            bf16x8 fk[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) mfma_acc(dkt[t], rd(pt[h] + so, 2048 * t), sb[h]);
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) fk[2 * t + h] = rd(pt[h] + so, 2048 * (t2 + t));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) mfma_acc(dkt[t2 + t], fk[2 * t + h], sb[h]);
+        }
     };
 
     issue(0);
