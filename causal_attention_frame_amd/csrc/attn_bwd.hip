@@ -556,12 +556,28 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
         constexpr bool MASK = decltype(masked)::value;
         __builtin_amdgcn_s_waitcnt(wait_vm(4));
         lds_barrier();
+        // Fragment reads four at a time ahead of their MFMAs (behind a
+        // scheduling fence): left to itself the compiler read one fragment,
+        // waited for it and multiplied, 24 times a tile.
         f32x16 s = {}, dp = {};
 #pragma unroll
-        for (int k = 0; k < NS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(pk[k] + st * kTile), qf[k], s, 0, 0, 0);
+        for (int k2 = 0; k2 < NS; k2 += 4) {
+            bf16x8 fa[4];
 #pragma unroll
-        for (int k = 0; k < NS; ++k)
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_b128(pv[k] + st * kTile), df[k], dp, 0, 0, 0);
+            for (int k = 0; k < 4; ++k) fa[k] = lds_b128(pk[k2 + k] + st * kTile);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], qf[k2 + k], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k2 = 0; k2 < NS; k2 += 4) {
+            bf16x8 fa[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) fa[k] = lds_b128(pv[k2 + k] + st * kTile);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], df[k2 + k], dp, 0, 0, 0);
+        }
         bf16x8 sb[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -570,13 +586,21 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
             sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dd));
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t2 = 0; t2 < NT; t2 += 2) {
+            bf16x8 kt[4];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x8 kt = cat_tr(lds_tr16(ptr[t][0] + st * kTile + 16 * h * kD),
-                                         lds_tr16(ptr[t][1] + st * kTile + 16 * h * kD));
-                dqt[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, sb[h], dqt[t], 0, 0, 0);
-            }
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    kt[2 * t + h] = cat_tr(lds_tr16(ptr[t2 + t][0] + st * kTile + 16 * h * kD),
+                                           lds_tr16(ptr[t2 + t][1] + st * kTile + 16 * h * kD));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    dqt[t2 + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * t + h], sb[h], dqt[t2 + t], 0, 0, 0);
+        }
         issue(j + NSTG - 1, std::integral_constant<int, (st + NSTG - 1) % NSTG>{});
     };
 
