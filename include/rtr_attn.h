@@ -239,7 +239,8 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
  * bf16 cache, d = 128 only.  workspace: rtr_attn_bwd_workspace_size(C*k, H,
  * d) bytes, 256-byte aligned, overlapping no argument.  No output may overlap
  * an input, the cache buffers or another output.  Limits: C*k * H * d < 2^31.
- * Returns RTR_OK or a negative rtr_status; nothing is enqueued on an error.
+ * Returns RTR_OK or a negative rtr_status; every argument is checked before
+ * anything is enqueued (a failing launch reports RTR_EHIP).
  * ---------------------------------------------------------------------- */
 int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                              const void *o, const float *lse, const void *d_o, int32_t chunk_frames,
