@@ -296,8 +296,8 @@ def main():
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel": ("attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16")
-                      + ("" if ws is None else " + attn_combine_d128"),
-            "schedule": "plain" if ws is None else "split-K",
+                      + ("" if ws is None else " (+ attn_combine_d128 when the library splits)"),
+            "schedule": "plain" if ws is None else "workspace given: split-K where the planner predicts a gain",
             "kernel_avg_us": round(attn_avg_s * 1e6, 2),
             "kernel_min_us": round(float(attn_ms.min()) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
