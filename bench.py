@@ -159,8 +159,8 @@ def main():
                          "(head, query block), the faster schedule on these shapes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(the attention shards by head with no exchange; see the design notes).",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(the attention would shard by head, with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
     RTR_OK = 0,
     RTR_EINVAL = -1,        /* bad argument (null, negative size, misaligned, overlap) */
-    RTR_EUNSUPPORTED = -2,  /* valid request outside what this build implements */
+    RTR_EUNSUPPORTED = -2,  /* valid request outside what the library implements */
     RTR_EHIP = -3,          /* HIP runtime or launch failure */
     RTR_ESTATE = -4         /* operation inconsistent with the cache state */
 } rtr_status;
