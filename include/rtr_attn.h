@@ -222,8 +222,11 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
  * Gradients of one streaming step (Key Designs 2 and 4: the step's Attn over
  * [reference | window | chunk]; Key Designs 3 trains the causal generator by
  * rolling it out over this cache, so its gradient passes back through every
- * step).  kv must be in the state it had when the forward step ran (restore a
- * snapshot if the ring has moved on); q, k, v: the chunk's [C*k, H, d]; o and
+ * step).  kv must be as it was when the forward step ran, metadata and the
+ * contents of the slots that step read: call this before the chunk is
+ * committed with rtr_kv_append_evict (which may overwrite the oldest window
+ * frame), or restore both the snapshot (rtr_kv_set_state) and the evicted
+ * frames' data; q, k, v: the chunk's [C*k, H, d]; o and
  * lse: that forward step's output and its natural-log LSE [H, C*k] (from
  * rtr_attn_stream_step_blocked with the same chunk_frames, block_frames and
  * scale); d_o: upstream gradient [C*k, H, d].
