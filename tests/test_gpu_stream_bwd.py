@@ -156,3 +156,25 @@ def test_stream_bwd_wan_shape_two_heads():
                              sl(do.values), kpf)
     _compare([g[:, heads] for g in got], r, True, "wan 1.3B")
     kv.close()
+
+
+def test_stream_bwd_through_a_rollout():
+    """The training-time order: each chunk runs its forward step, then its
+    backward (before the chunk is committed), then the commit; a reference
+    switch keeping one frame happens midway.  Every step's gradients,
+    cache gradients included, match the oracle on the cache as it stood."""
+    kpf, H, W, C = 64, 2, 3, 2
+    kv, ref = _cache(kpf, H, W, 1)
+    _fill(kv, ref, kpf, H, 1, 0, seed=41)
+    for step in range(7):
+        if step == 4:
+            x0 = gen.stream_inputs(kpf, H, D, 1, 1, 1, "bf16", base_seed=99, wid=93)
+            rtr.rtr_kv_reset_ref(kv, REF_REPLACE, dev(x0["ref_k"]), dev(x0["ref_v"]), 1, 1)
+            ref.reset_ref(REF_REPLACE, x0["ref_k"].values, x0["ref_v"].values, keep_recent=1)
+        x, do, got = _step(kv, kpf, H, C, 1, seed=50 + step, cache_grads=True)
+        pk, pv = ref.prefix(kpf, H, D)
+        r = attn_stream_step_bwd(pk, pv, x["q"].values, x["k"].values, x["v"].values, do.values, kpf)
+        _compare(got, r, True, f"step {step}")
+        rtr.rtr_kv_append_evict(kv, dev(x["k"]).view(C, kpf, H, D), dev(x["v"]).view(C, kpf, H, D), C)
+        ref.append(x["k"].values.reshape(C, kpf, H, D), x["v"].values.reshape(C, kpf, H, D))
+    kv.close()
