@@ -39,6 +39,17 @@ def test_library_exports_every_declared_symbol():
     assert rtr.rtr_version() == 100
 
 
+def test_binding_arity_matches_header():
+    """Every prototype in the header takes as many arguments as the ctypes
+    binding declares for it."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(rtr_\w+)\s*\(([^;]*?)\)\s*;", text, flags=re.M | re.S)
+    assert len(decls) == len(rtr._SIGNATURES)
+    for name, args in decls:
+        n = 0 if args.strip() in ("", "void") else len(args.split(","))
+        assert n == len(rtr._SIGNATURES[name][1]), name
+
+
 def test_status_strings():
     L = rtr.lib()
     for code in (0, -1, -2, -3, -4):
