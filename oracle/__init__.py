@@ -15,7 +15,8 @@ Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
   * rope.py       -- temporal rotary encoding and the position of the anchored
     reference in front of the rolling window (position-aware cache).
   * attention_bwd.py -- gradients (dQ, dK, dV) of the Key Designs 2 equation,
-    the pass that Key Designs 3's post-training back-propagates through.
+    the pass that Key Designs 3's post-training back-propagates through, for
+    the full form, the streaming step and the text cross-attention.
   * listkv.py     -- Key Designs 4 ("Reference-preserving KV cache update and
     live style switching"), and Key Designs 1 for the reference as one extra
     latent frame placed before the first frame; its TextKV is the
@@ -41,6 +42,7 @@ from .attention_bwd import (  # noqa: F401
     attn_bwd_rows,
     attn_bwd_cols,
     attn_stream_step_bwd,
+    attn_cross_bwd,
 )
 from .rope import rope_rotate, reference_shift  # noqa: F401
 from .listkv import ListKV, TextKV, REF_KEEP, REF_REPLACE, REF_CLEAR  # noqa: F401

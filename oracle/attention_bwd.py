@@ -156,3 +156,26 @@ def attn_stream_step_bwd(prefix_k, prefix_v, q, k, v, do, tokens_per_frame, scal
         dq[:, h] = sc * (dS @ kk[:, h])
         dkk[:, h] = sc * (dS.T @ q[:, h])
     return dq, dkk[P:], dvv[P:], dkk[:P], dvv[:P]
+
+
+def attn_cross_bwd(q, k_text, v_text, do, scale=None):
+    """Gradients of the text cross-attention (Key Designs 1: the text condition
+    enters through cross attention; the generator's post-training sends its
+    gradient back through it as through the self-attention), dense and
+    literal.  Every query sees every text token, so the mask is empty.
+
+    q, do: [Tq, H, d]; k_text, v_text: [Lt, H, d].
+    Returns (dq, dk_text, dv_text), float64.
+    """
+    q, kk, vv, do = _f64(q), _f64(k_text), _f64(v_text), _f64(do)
+    Tq, H, d = q.shape
+    sc = _scale(d, scale)
+    dq, dk, dv = np.empty_like(q), np.empty_like(kk), np.empty_like(vv)
+    for h in range(H):
+        P = _probs((q[:, h] @ kk[:, h].T) * sc)
+        dv[:, h] = P.T @ do[:, h]
+        dP = do[:, h] @ vv[:, h].T
+        dS = P * (dP - np.sum(dP * P, axis=1, keepdims=True))
+        dq[:, h] = sc * (dS @ kk[:, h])
+        dk[:, h] = sc * (dS.T @ q[:, h])
+    return dq, dk, dv

@@ -165,3 +165,46 @@ def test_stream_step_bwd_central_differences():
             am[which][idx] -= eps
             num[idx] = (loss(ap) - loss(am)) / (2 * eps)
         np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_cross_bwd_central_differences():
+    """Pin: central differences of sum(O * G) through the (pinned) text
+    cross-attention oracle, for q and the text keys and values."""
+    from oracle.attention_bwd import attn_cross_bwd
+    Tq, Lt, H, d = 5, 4, 2, 3
+    q, kt, vt, g = _rand((Tq, H, d), 80), _rand((Lt, H, d), 81), _rand((Lt, H, d), 82), _rand((Tq, H, d), 83)
+    grads = attn_cross_bwd(q, kt, vt, g)
+    args = [q, kt, vt]
+    eps = 1e-6
+
+    def loss(a):
+        o, _ = oracle.attn_cross(a[0], a[1], a[2])
+        return float(np.sum(o * g))
+
+    for which in range(3):
+        num = np.zeros_like(grads[which])
+        for idx in np.ndindex(*num.shape):
+            ap = [x.copy() for x in args]
+            am = [x.copy() for x in args]
+            ap[which][idx] += eps
+            am[which][idx] -= eps
+            num[idx] = (loss(ap) - loss(am)) / (2 * eps)
+        np.testing.assert_allclose(grads[which], num, rtol=1e-6, atol=1e-8)
+
+
+def test_cross_bwd_autograd_and_invariants():
+    """Pin: torch.autograd in float64 through softmax(Q K^T * scale) V written
+    out here, an explicit scale; and the softmax invariants (the text keys'
+    gradients sum to zero, the text values' gradients sum to the summed dO)."""
+    from oracle.attention_bwd import attn_cross_bwd
+    Tq, Lt, H, d = 30, 17, 2, 8
+    q, kt, vt, g = _rand((Tq, H, d), 84), _rand((Lt, H, d), 85), _rand((Lt, H, d), 86), _rand((Tq, H, d), 87)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, kt, vt))
+    s = torch.einsum("thd,shd->hts", tq, tk) * 0.3
+    o = torch.einsum("hts,shd->thd", torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(g))
+    dq, dk, dv = attn_cross_bwd(q, kt, vt, g, scale=0.3)
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-11)
+    np.testing.assert_allclose(dv.sum(axis=0), g.sum(axis=0), atol=1e-11)
