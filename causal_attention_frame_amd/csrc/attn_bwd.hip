@@ -663,8 +663,8 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
     a.T = (int32_t)p.T;
     a.kpf = (int32_t)std::min<int64_t>(p.tokens_per_frame, p.T);
     a.nqt = (int32_t)((p.T + 31) / 32);
-    a.nkb = (int32_t)((p.T + 255) / 256);
-    a.nqb = a.nkb;
+    a.nqb = (int32_t)((p.T + 255) / 256);
+    a.nkb = p.cross ? 0 : a.nqb;  // blocks of the rows' own keys (none for cross-attention)
     a.ld = (int64_t)p.H * kD;
     a.scale = p.scale;
     a.c = p.scale * kLog2e;
@@ -684,7 +684,7 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
         a.nseg = p.nseg;
         a.seg_len = (int32_t)p.seg_len;
         a.prefix = (int32_t)p.prefix;
-        a.Tk = a.prefix + a.T;
+        a.Tk = a.prefix + (p.cross ? 0 : a.T);
         if (p.dk_prefix) {
             a.nkbp = (int32_t)((p.prefix + 255) / 256);
             a.dkp = (uint16_t *)p.dk_prefix;
@@ -696,8 +696,10 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
     hipLaunchKernelGGL(attn_bwd_prep, dim3(a.nqt, p.H), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
     a.nwg = p.H * (a.nkb + a.nkbp);
-    hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
-    if (hipError_t e = hipGetLastError()) return e;
+    if (a.nwg > 0) {  // none: cross-attention whose text is not differentiated
+        hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
     a.nwg = p.H * a.nqb;
     if (seg)
         hipLaunchKernelGGL(attn_bwd_dq_d128<true>, dim3(a.nwg), dim3(512), 0, stream, a);

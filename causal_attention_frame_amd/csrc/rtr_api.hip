@@ -792,6 +792,73 @@ int rtr_text_cache_state(const rtr_text_cache *tc, int32_t *n_tokens, int64_t *g
     return ok();
 }
 
+int rtr_attn_cross_bwd(const rtr_text_cache *tc, const void *q, const void *o, const float *lse,
+                       const void *d_o, int64_t Tq, void *dq, void *dk_text, void *dv_text, float scale,
+                       void *workspace, size_t workspace_bytes, rtr_stream stream) {
+    if (!tc) return fail(RTR_EINVAL, "cache handle is NULL");
+    if (Tq < 0 || Tq > kMaxTokens) return fail(RTR_EINVAL, "Tq=%lld out of range [0, 2^30]", (long long)Tq);
+    if (tc->dt != RTR_BF16) return fail(RTR_EUNSUPPORTED, "backward supports bf16 only");
+    if (tc->d != 128) return fail(RTR_EUNSUPPORTED, "backward head dim %d not supported (128)", tc->d);
+    if (int rc = check_scale(scale)) return rc;
+    if (tc->n == 0) return fail(RTR_ESTATE, "the text cache holds no condition");
+    if (Tq * tc->H * tc->d >= ((int64_t)1 << 31)) return fail(RTR_EUNSUPPORTED, "Tq * H * d must be below 2^31");
+    if ((dk_text == nullptr) != (dv_text == nullptr))
+        return fail(RTR_EINVAL, "dk_text and dv_text must both be NULL or both non-NULL");
+    if (Tq == 0) return ok();
+    const void *in[4] = {q, o, lse, d_o};
+    for (const void *x : in)
+        if (!x) return fail(RTR_EINVAL, "q, o, lse and d_o must be non-NULL");
+    if (!dq) return fail(RTR_EINVAL, "dq must be non-NULL");
+    for (const void *x : {q, o, d_o, (const void *)dq, (const void *)dk_text, (const void *)dv_text})
+        if (!aligned16(x)) return fail(RTR_EINVAL, "tensor pointers must be 16-byte aligned");
+    if (((uintptr_t)lse & 3u) != 0) return fail(RTR_EINVAL, "lse must be 4-byte aligned");
+    const int64_t tok = (int64_t)tc->H * tc->d * 2;
+    const int64_t tb = Tq * tok, lb = Tq * tc->H * 4, nb = (int64_t)tc->n * tok, cap_b = (int64_t)tc->capacity * tok;
+    void *out[3] = {dq, dk_text, dv_text};
+    const int64_t out_sz[3] = {tb, dk_text ? nb : 0, dv_text ? nb : 0};
+    const void *src[6] = {q, o, lse, d_o, tc->k_buf, tc->v_buf};
+    const int64_t src_sz[6] = {tb, tb, lb, tb, cap_b, cap_b};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(out[i], out_sz[i], src[j], src_sz[j])) return fail(RTR_EINVAL, "an output overlaps an input or the cache");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(out[i], out_sz[i], out[j], out_sz[j])) return fail(RTR_EINVAL, "outputs overlap");
+    }
+    size_t need = 0;
+    if (const hipError_t e = rtr::attention_bwd_workspace_bytes(Tq, tc->H, &need)) return hip_fail(e, "workspace size");
+    if (!workspace) return fail(RTR_EINVAL, "workspace is NULL (%zu bytes needed)", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(RTR_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    for (int j = 0; j < 6; ++j)
+        if (overlaps(workspace, (int64_t)need, src[j], src_sz[j])) return fail(RTR_EINVAL, "workspace overlaps an input or the cache");
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(workspace, (int64_t)need, out[i], out_sz[i])) return fail(RTR_EINVAL, "workspace overlaps an output");
+
+    // The text tokens are the only keys, all seen by every query row: one
+    // key segment that is all prefix, no keys of the rows' own.
+    rtr::BwdProblem p;
+    p.q = q;
+    p.o = o;
+    p.dout = d_o;
+    p.lse = lse;
+    p.dq = dq;
+    p.T = Tq;
+    p.tokens_per_frame = Tq;
+    p.H = tc->H;
+    p.scale = resolve_scale(scale, tc->d);
+    p.ws = workspace;
+    p.kseg[0] = tc->k_buf;
+    p.vseg[0] = tc->v_buf;
+    p.nseg = 1;
+    p.seg_len = tc->n;
+    p.prefix = tc->n;
+    p.cross = true;
+    p.dk_prefix = dk_text;
+    p.dv_prefix = dv_text;
+    if (const hipError_t e = rtr::launch_attention_bwd(p, (hipStream_t)stream)) return hip_fail(e, "backward launch");
+    return ok();
+}
+
 int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse, int64_t Tq,
                    rtr_dtype out_dtype, float scale, void *workspace, size_t workspace_bytes,
                    rtr_stream stream) {

@@ -71,6 +71,9 @@ struct BwdProblem {
     int32_t nseg = 0;
     int64_t seg_len = 0, prefix = 0;
     void *dk_prefix = nullptr, *dv_prefix = nullptr;
+    // Cross-attention: the rows have no keys of their own (k, v, dk, dv unused);
+    // every key is one of the `prefix` keys of the segment table.
+    bool cross = false;
 };
 
 hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes);

@@ -75,6 +75,8 @@ _SIGNATURES = {
     "rtr_text_cache_state": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64)]),
     "rtr_attn_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, ctypes.c_int, _c_f32, _vp,
                                       ctypes.c_size_t, _vp]),
+    "rtr_attn_cross_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _c_f32, _vp,
+                                          ctypes.c_size_t, _vp]),
     "rtr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rtr_last_error": (ctypes.c_char_p, []),
     "rtr_version": (ctypes.c_int, []),
@@ -429,3 +431,27 @@ def rtr_attn_cross(tc, q, o=None, lse=None, scale=0.0, out_dtype=None, want_lse=
 
 def rtr_version():
     return lib().rtr_version()
+
+
+def rtr_attn_cross_bwd(tc, q, o, lse, d_o, dq=None, dk_text=None, dv_text=None, want_text_grads=False,
+                       scale=0.0, workspace=None, stream=None):
+    """Gradients of rtr_attn_cross from its o and lse.  Returns (dq, dk_text,
+    dv_text); the text gradients ([n, H, d]) are None unless given or
+    want_text_grads."""
+    import torch
+    Tq, H, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    if want_text_grads and dk_text is None:
+        n, _ = rtr_text_cache_state(tc)
+        dk_text = torch.empty((n, H, d), dtype=q.dtype, device=q.device)
+        dv_text = torch.empty((n, H, d), dtype=q.dtype, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, rtr_attn_bwd_workspace_size(Tq, H, d)), dtype=torch.uint8,
+                                device=q.device)
+    ws, ws_bytes = _workspace(workspace)
+    _check(lib().rtr_attn_cross_bwd(tc.handle, _ptr(q), _ptr(o), _ptr(lse), _ptr(d_o), Tq, _ptr(dq),
+                                    _ptr(dk_text), _ptr(dv_text), float(scale), ws, ws_bytes,
+                                    _stream(stream, q.device)),
+           "rtr_attn_cross_bwd")
+    return dq, dk_text, dv_text
+

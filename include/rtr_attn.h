@@ -298,6 +298,21 @@ int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse,
                    rtr_dtype out_dtype, float scale, void *workspace, size_t workspace_bytes,
                    rtr_stream stream);
 
+/* Gradients of that cross-attention (the generator's post-training, Key
+ * Designs 3, back-propagates through the text injection of Key Designs 1 as
+ * through the self-attention): for an upstream gradient d_o [Tq, H, d] and the
+ * forward's o [Tq, H, d] and natural-log lse [H, Tq] (rtr_attn_cross with the
+ * same scale and bf16 output), dq [Tq, H, d] and, when dk_text and dv_text are
+ * given, the gradients of the current condition's text keys and values
+ * [n, H, d] (both NULL: the text is treated as constant).  bf16 cache, d = 128
+ * only; workspace: rtr_attn_bwd_workspace_size(Tq, H, d) bytes, 256-byte
+ * aligned.  No output may overlap an input, the cache or another output.
+ * Limits: Tq * H * d < 2^31.  Tq == 0 is a no-op; an empty cache is
+ * RTR_ESTATE. */
+int rtr_attn_cross_bwd(const rtr_text_cache *tc, const void *q, const void *o, const float *lse,
+                       const void *d_o, int64_t Tq, void *dq, void *dk_text, void *dv_text, float scale,
+                       void *workspace, size_t workspace_bytes, rtr_stream stream);
+
 /* Position-aware reference (rotary position encoding along time).  Rotary
  * encodings are baked into cached K, so in a rolling window the frames keep
  * their generation-time positions, which is exact for them (scores depend on

@@ -407,3 +407,38 @@ def test_stream_step_bwd_rejects_unsupported_caches():
         assert _sbwd(kv) == rtr.RTR_EUNSUPPORTED
     assert rtr.lib().rtr_attn_stream_step_bwd(None, *([FAKE] * 6), 1, 1, *([FAKE] * 5), 0.0, FAKE,
                                               MB, None) == rtr.RTR_EINVAL
+
+
+def test_cross_bwd_rejections():
+    """Argument checks of rtr_attn_cross_bwd on a host-side text cache (no
+    call reaches a launch)."""
+    L = rtr.lib()
+    H, d = 2, 128
+    tc = rtr.TextCache(FAKE, FAKE + MB, 64, H, d, rtr.RTR_BF16)
+    base = FAKE + 256 * MB
+    a = dict(q=base, o=base + MB, lse=base + 2 * MB, do=base + 3 * MB, Tq=100, dq=base + 4 * MB,
+             dk=base + 5 * MB, dv=base + 6 * MB, scale=0.0, ws=base + 16 * MB, ws_bytes=16 * MB)
+
+    def call(h=tc.handle, **kw):
+        x = dict(a)
+        x.update(kw)
+        return L.rtr_attn_cross_bwd(h, x["q"], x["o"], x["lse"], x["do"], x["Tq"], x["dq"], x["dk"],
+                                    x["dv"], x["scale"], x["ws"], x["ws_bytes"], None)
+
+    assert call() == rtr.RTR_ESTATE                       # no condition set
+    assert L.rtr_text_cache_reset(tc.handle, None, None, 30, None) == rtr.RTR_OK
+    assert call(h=None) == rtr.RTR_EINVAL
+    assert call(Tq=-1) == rtr.RTR_EINVAL
+    assert call(dv=None) == rtr.RTR_EINVAL                # text gradients come in pairs
+    assert call(q=None) == rtr.RTR_EINVAL
+    assert call(dq=None) == rtr.RTR_EINVAL
+    assert call(dq=base + 4 * MB + 8) == rtr.RTR_EINVAL  # misaligned
+    assert call(dk=FAKE + 64) == rtr.RTR_EINVAL          # overlaps the text keys
+    assert call(dk=base + 4 * MB + 64) == rtr.RTR_EINVAL  # overlaps dq
+    assert call(ws=None) == rtr.RTR_EINVAL
+    assert call(ws_bytes=100) == rtr.RTR_EINVAL
+    assert call(scale=float("inf")) == rtr.RTR_EINVAL
+    assert call(Tq=0) == rtr.RTR_OK                       # no-op
+    tc64 = rtr.TextCache(FAKE, FAKE + MB, 64, H, 64, rtr.RTR_BF16)
+    L.rtr_text_cache_reset(tc64.handle, None, None, 30, None)
+    assert call(h=tc64.handle) == rtr.RTR_EUNSUPPORTED
