@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--workload", default="wan13b_stream_step",
                     choices=["wan13b_stream_step", "wan14b_stream_step", "full_block_causal",
                              "full_block_causal_bwd", "wan13b_stream_step_bwd", "wan13b_cross_step",
-                             "rollout"],
+                             "wan13b_cross_step_bwd", "rollout"],
                     help="rollout: one step is a whole 240-chunk rollout (stream step, commit, "
                          "and a reference swap every 60 chunks)")
     ap.add_argument("--cpu-heads", type=int, default=12,
@@ -178,7 +178,7 @@ def main():
         return backward(args, w, dev)
     if args.workload == "wan13b_stream_step_bwd":
         return stream_backward(args, w, dev)
-    if args.workload == "wan13b_cross_step":
+    if args.workload in ("wan13b_cross_step", "wan13b_cross_step_bwd"):
         return cross(args, w, dev)
 
     def to_dev(t):
@@ -520,7 +520,9 @@ def cross(args, w, dev):
     """Text cross-attention of one chunk: one step is one rtr_attn_cross call of
     the chunk's C*k query rows against the text cache's tokens (no mask).  The
     cache reset of a text switch (copy of the new condition's K and V) is timed
-    separately and reported as `text_reset`."""
+    separately and reported as `text_reset`.  The _bwd workload times
+    rtr_attn_cross_bwd instead (dq and the text keys' and values' gradients;
+    10 d flops per (row, text token) pair: S recomputed, dP, dV, dK, dQ)."""
     import torch
     from causal_attention_frame_amd import inputs as gen
     from causal_attention_frame_amd import rtr
@@ -535,10 +537,20 @@ def cross(args, w, dev):
     o = torch.empty_like(q)
     ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
     stream = torch.cuda.current_stream(dev)
-    flops = 4 * d * H * Tq * Lt
+    bwd = args.workload.endswith("_bwd")
+    flops = (10 if bwd else 4) * d * H * Tq * Lt
+    if bwd:
+        o, lse = rtr.rtr_attn_cross(tc, q, want_lse=True)
+        do_h = gen.normal((Tq, H, d), "bf16", 0, w["wid"], 0, gen.TAG_DO)
+        do = torch.from_numpy(do_h.bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        dq, dkt, dvt = torch.empty_like(q), torch.empty_like(kt), torch.empty_like(vt)
+        wsb = torch.empty(rtr.rtr_attn_cross_bwd_workspace_size(Tq, Lt, H, d), dtype=torch.uint8, device=dev)
 
     def step():
-        rtr.rtr_attn_cross(tc, q, o=o, workspace=ws)
+        if bwd:
+            rtr.rtr_attn_cross_bwd(tc, q, o, lse, do, dq, dkt, dvt, workspace=wsb)
+        else:
+            rtr.rtr_attn_cross(tc, q, o=o, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -577,7 +589,7 @@ def cross(args, w, dev):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "wan13b_cross_step", "heads": H, "head_dim": d, "query_tokens": Tq,
+        "config": {"workload": args.workload, "heads": H, "head_dim": d, "query_tokens": Tq,
                    "text_tokens": Lt},
         "roofline": {
             "bound": "mfma",
@@ -586,7 +598,8 @@ def cross(args, w, dev):
             "unit": "TFLOP/s",
             "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": None,
-            "kernel": "attn_fwd_bf16_d128" + ("" if ws is None else " (+ split-K when planned)"),
+            "kernel": ("attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128<SEG> (one call)" if bwd else
+                       "attn_fwd_bf16_d128" + ("" if ws is None else " (+ split-K when planned)")),
             "kernel_avg_us": round(call_s * 1e6, 2),
             "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
             "algorithmic_flop_per_launch": flops,
@@ -605,11 +618,16 @@ def cross(args, w, dev):
             cores = os.cpu_count()
         heads = min(H, args.cpu_heads)
         t1 = time.perf_counter()
-        oracle.attn_cross(x[0].values[:, :heads], x[1].values[:, :heads], x[2].values[:, :heads])
+        if bwd:
+            oracle.attn_cross_bwd(x[0].values[:, :heads], x[1].values[:, :heads], x[2].values[:, :heads],
+                                  do_h.values[:, :heads])
+        else:
+            oracle.attn_cross(x[0].values[:, :heads], x[1].values[:, :heads], x[2].values[:, :heads])
         dt = time.perf_counter() - t1
-        out["cpu_baseline"] = {"value": 4 * d * heads * Tq * Lt / dt / 1e12, "unit": "TFLOP/s",
-                               "cores": int(cores), "kind": "oracle",
-                               "sample": f"oracle.attn_cross (dense float64) on heads 0..{heads - 1} of {H}",
+        name = "oracle.attn_cross_bwd" if bwd else "oracle.attn_cross"
+        out["cpu_baseline"] = {"value": (10 if bwd else 4) * d * heads * Tq * Lt / dt / 1e12,
+                               "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+                               "sample": f"{name} (dense float64) on heads 0..{heads - 1} of {H}",
                                "seconds": round(dt, 3)}
     print(json.dumps(out), flush=True)
 

@@ -79,6 +79,12 @@ struct BArgs {
     float inv_seg_len;
     int32_t prefix, Tk, nkbp;
     uint16_t *dkp, *dvp;
+    // Prefix-key blocks split over the query tiles (few keys, many rows: the
+    // text of a cross-attention): piece p of a block walks tiles
+    // [p tpp, (p + 1) tpp) and leaves unscaled fp32 dK^T / dV^T partials in
+    // part[p][key][head][2][128], summed in piece order by attn_bwd_reduce.
+    int32_t nsplit, tpp;
+    float *part;
 };
 
 constexpr int kD = 128;
@@ -218,7 +224,8 @@ constexpr int kDkdvLds = 4 * kDkdvStages * kTile + kDkdvStages * 128 + 256 * kD;
 // true), which every query row sees and which are read through the segment
 // table.  lbase: LDS byte address of the kDkdvLds array.
 template <bool PRE>
-__device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a, int head, int kb, uint32_t lbase) {
+__device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a, int head, int kb, int piece,
+                                                                 uint32_t lbase) {
     constexpr int NS = 8, NT = 4, NSTG = kDkdvStages;
     constexpr int RQ = 0, RDO = NSTG * kTile, RQT = 2 * NSTG * kTile, RDOT = 3 * NSTG * kTile;
     constexpr int RROW = 4 * NSTG * kTile;  // in uint16 units
@@ -236,8 +243,8 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
     const int nkeys = pre ? a.prefix : a.T;
     const bool kvalid = kj < nkeys;
     const int qmin = pre ? 0 : (kj / a.kpf) * a.kpf;
-    const int t0 = pre ? 0 : ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
-    const int nt = a.nqt - t0;
+    const int t0 = pre ? piece * a.tpp : ((k0 / a.kpf) * a.kpf) / 32;  // first tile that sees a key of the block
+    const int nt = pre ? min(a.tpp, a.nqt - t0) : a.nqt - t0;
     // Tiles that start below the first row of the block's last key frame may
     // hold rows that miss some of its keys: they take the element-wise mask.
     const int last_key = min(k0 + 255, a.T - 1);
@@ -411,6 +418,19 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
     if (!kvalid) return;
+    if (PRE && a.nsplit > 1) {  // one piece of a split block: fp32 partials, reduced later
+        float *const pp = a.part + ((long)piece * a.prefix + kj) * (2 * a.ld) + 2 * hoff;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = 32 * t + 8 * j + 4 * g;
+                const f32x16 &k_ = dkt[t], &v_ = dvt[t];
+                *(f32x4 *)(pp + d0) = f32x4{k_[4 * j], k_[4 * j + 1], k_[4 * j + 2], k_[4 * j + 3]};
+                *(f32x4 *)(pp + kD + d0) = f32x4{v_[4 * j], v_[4 * j + 1], v_[4 * j + 2], v_[4 * j + 3]};
+            }
+        return;
+    }
     const long ob = (long)kj * a.ld + hoff;
     uint16_t *const dko = pre ? a.dkp : a.dk, *const dvo = pre ? a.dvp : a.dv;
 #pragma unroll
@@ -430,15 +450,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_d128(const BArgs a) {
     __shared__ __attribute__((aligned(256))) uint16_t smem[kDkdvLds];
     int head, blk;
-    xcd_order(blockIdx.x, a.nwg, a.nkb + a.nkbp, head, blk);
+    xcd_order(blockIdx.x, a.nwg, a.nkb + a.nkbp * a.nsplit, head, blk);
     // Blocks of cached prefix keys (streaming step; every row sees them, so
     // they carry the most work) take the highest indices, then the blocks of
     // the query rows' own keys, earliest keys highest.
     const uint32_t lbase = lds_addr((lds_u16 *)smem);
     if (blk >= a.nkb)
-        dkdv_block<true>(a, head, blk - a.nkb, lbase);
+        dkdv_block<true>(a, head, (blk - a.nkb) / a.nsplit, (blk - a.nkb) % a.nsplit, lbase);
     else
-        dkdv_block<false>(a, head, a.nkb - 1 - blk, lbase);
+        dkdv_block<false>(a, head, a.nkb - 1 - blk, 0, lbase);
 }
 
 // ---------------------------------------------------------------------------
@@ -640,7 +660,41 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
         }
 }
 
+// Sum of the pieces of split prefix-key blocks, in piece order: four
+// consecutive floats of one (key, head) row per thread; dK scaled, both to bf16.
+__global__ __launch_bounds__(256) void attn_bwd_reduce(const BArgs a) {
+    const long e = (long)blockIdx.x * 256 + threadIdx.x;  // f32x4 index
+    const long per_piece = (long)a.prefix * 2 * a.ld;     // floats per piece
+    if (e * 4 >= per_piece) return;
+    f32x4 acc = {};
+    for (int p = 0; p < a.nsplit; ++p) acc += *(const f32x4 *)(a.part + p * per_piece + e * 4);
+    const long row = e / 64;           // (key, head) row of 256 floats
+    const int c = (int)(e % 64) * 4;   // 0..255: dK columns, then dV columns
+    const long key = row / (a.ld / kD), head = row % (a.ld / kD);
+    const bool isk = c < kD;
+    const float f = isk ? a.scale : 1.f;
+    uint16_t *const dst = (isk ? a.dkp : a.dvp) + key * a.ld + head * kD + (c & (kD - 1));
+    *(u32x2 *)dst = u32x2{pack_bf16x2(acc[0] * f, acc[1] * f), pack_bf16x2(acc[2] * f, acc[3] * f)};
+}
+
+// Pieces per prefix-key block: split only when the blocks alone would leave
+// most of the GPU idle, into pieces of at least 16 query tiles.
+int bwd_split(int64_t T, int32_t H, int64_t prefix, bool cross) {
+    const int64_t nqt = (T + 31) / 32, wg = (int64_t)H * ((prefix + 255) / 256);
+    if (!cross || wg >= 128 || nqt < 32) return 1;
+    const int64_t want = std::min<int64_t>((256 + wg - 1) / wg, nqt / 16);
+    const int64_t tpp = (nqt + want - 1) / want;
+    return (int)((nqt + tpp - 1) / tpp);
+}
+
 }  // namespace
+
+hipError_t attention_cross_bwd_workspace_bytes(int64_t Tq, int64_t n, int32_t H, size_t *bytes) {
+    attention_bwd_workspace_bytes(Tq, H, bytes);
+    const int ns = bwd_split(Tq, H, n, true);
+    if (ns > 1) *bytes = (*bytes + 255) / 256 * 256 + (size_t)ns * n * H * 2 * kD * sizeof(float);
+    return hipSuccess;
+}
 
 hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes) {
     const int64_t nqt = (T + 31) / 32;
@@ -689,15 +743,31 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
             a.nkbp = (int32_t)((p.prefix + 255) / 256);
             a.dkp = (uint16_t *)p.dk_prefix;
             a.dvp = (uint16_t *)p.dv_prefix;
+            a.nsplit = bwd_split(p.T, p.H, p.prefix, p.cross);
+            a.tpp = (a.nqt + a.nsplit - 1) / a.nsplit;
+            if (a.nsplit > 1) {
+                size_t prep = 0;
+                attention_bwd_workspace_bytes(p.T, p.H, &prep);
+                a.part = (float *)((char *)p.ws + (prep + 255) / 256 * 256);
+            }
         }
     }
     a.inv_seg_len = 1.0f / (float)a.seg_len;
+    if (a.nsplit == 0) {
+        a.nsplit = 1;
+        a.tpp = a.nqt;
+    }
 
     hipLaunchKernelGGL(attn_bwd_prep, dim3(a.nqt, p.H), dim3(256), 0, stream, a);
     if (hipError_t e = hipGetLastError()) return e;
-    a.nwg = p.H * (a.nkb + a.nkbp);
+    a.nwg = p.H * (a.nkb + a.nkbp * a.nsplit);
     if (a.nwg > 0) {  // none: cross-attention whose text is not differentiated
         hipLaunchKernelGGL(attn_bwd_dkdv_d128, dim3(a.nwg), dim3(512), 0, stream, a);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
+    if (a.nsplit > 1) {
+        const long n4 = (long)a.prefix * 2 * a.ld / 4;
+        hipLaunchKernelGGL(attn_bwd_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a);
         if (hipError_t e = hipGetLastError()) return e;
     }
     a.nwg = p.H * a.nqb;

@@ -792,6 +792,17 @@ int rtr_text_cache_state(const rtr_text_cache *tc, int32_t *n_tokens, int64_t *g
     return ok();
 }
 
+int rtr_attn_cross_bwd_workspace_size(int64_t Tq, int32_t n_text, int32_t H, int32_t d, size_t *bytes) {
+    if (!bytes) return fail(RTR_EINVAL, "bytes is NULL");
+    *bytes = 0;
+    if (Tq < 0 || Tq > kMaxTokens) return fail(RTR_EINVAL, "Tq=%lld out of range [0, 2^30]", (long long)Tq);
+    if (n_text < 1) return fail(RTR_EINVAL, "n_text=%d must be >= 1", n_text);
+    if (H < 1) return fail(RTR_EINVAL, "H=%d must be >= 1", H);
+    if (d != 128) return fail(RTR_EUNSUPPORTED, "backward head dim %d not supported (128)", d);
+    if (const hipError_t e = rtr::attention_cross_bwd_workspace_bytes(Tq, n_text, H, bytes)) return hip_fail(e, "workspace size");
+    return ok();
+}
+
 int rtr_attn_cross_bwd(const rtr_text_cache *tc, const void *q, const void *o, const float *lse,
                        const void *d_o, int64_t Tq, void *dq, void *dk_text, void *dv_text, float scale,
                        void *workspace, size_t workspace_bytes, rtr_stream stream) {
@@ -825,7 +836,9 @@ int rtr_attn_cross_bwd(const rtr_text_cache *tc, const void *q, const void *o, c
             if (overlaps(out[i], out_sz[i], out[j], out_sz[j])) return fail(RTR_EINVAL, "outputs overlap");
     }
     size_t need = 0;
-    if (const hipError_t e = rtr::attention_bwd_workspace_bytes(Tq, tc->H, &need)) return hip_fail(e, "workspace size");
+    if (const hipError_t e = dk_text ? rtr::attention_cross_bwd_workspace_bytes(Tq, tc->n, tc->H, &need)
+                                     : rtr::attention_bwd_workspace_bytes(Tq, tc->H, &need))
+        return hip_fail(e, "workspace size");
     if (!workspace) return fail(RTR_EINVAL, "workspace is NULL (%zu bytes needed)", need);
     if (((uintptr_t)workspace & 255u) != 0) return fail(RTR_EINVAL, "workspace must be 256-byte aligned");
     if (workspace_bytes < need) return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed", workspace_bytes, need);

@@ -77,6 +77,10 @@ struct BwdProblem {
 };
 
 hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes);
+// Workspace of the cross-attention backward over Tq rows and n text keys:
+// the above plus, when the text key blocks are split over the rows, their
+// fp32 partial gradients.
+hipError_t attention_cross_bwd_workspace_bytes(int64_t Tq, int64_t n, int32_t H, size_t *bytes);
 hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream);
 
 // Copies of whole [k, H, d] frames (16-byte multiples, 16-byte aligned).

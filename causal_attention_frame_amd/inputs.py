@@ -26,6 +26,7 @@ WORKLOADS = {
     "rollout": dict(wid=4, H=12, d=128, k=1560, C=3, W=6, R=1, chunks=240,
                     swap_every=60, dtype="bf16"),
     "wan13b_cross_step": dict(wid=7, H=12, d=128, k=1560, C=3, text_tokens=512, dtype="bf16"),
+    "wan13b_cross_step_bwd": dict(wid=9, H=12, d=128, k=1560, C=3, text_tokens=512, dtype="bf16"),
     "full_block_causal_bwd": dict(wid=6, H=12, d=128, k=1560, frames=22, dtype="bf16"),
     "wan13b_stream_step_bwd": dict(wid=8, H=12, d=128, k=1560, C=3, W=6, R=1, dtype="bf16"),
     "wan14b_stream_step": dict(wid=5, H=40, d=128, k=1560, C=3, W=9, R=1, dtype="bf16",

@@ -75,6 +75,8 @@ _SIGNATURES = {
     "rtr_text_cache_state": (ctypes.c_int, [_vp, ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i64)]),
     "rtr_attn_cross": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i64, ctypes.c_int, _c_f32, _vp,
                                       ctypes.c_size_t, _vp]),
+    "rtr_attn_cross_bwd_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, _c_i32,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "rtr_attn_cross_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp, _vp, _vp, _c_f32, _vp,
                                           ctypes.c_size_t, _vp]),
     "rtr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -433,6 +435,14 @@ def rtr_version():
     return lib().rtr_version()
 
 
+def rtr_attn_cross_bwd_workspace_size(Tq, n_text, H, d=128):
+    """Bytes of device workspace rtr_attn_cross_bwd needs with text gradients."""
+    n = ctypes.c_size_t(0)
+    _check(lib().rtr_attn_cross_bwd_workspace_size(int(Tq), int(n_text), int(H), int(d), ctypes.byref(n)),
+           "rtr_attn_cross_bwd_workspace_size")
+    return n.value
+
+
 def rtr_attn_cross_bwd(tc, q, o, lse, d_o, dq=None, dk_text=None, dv_text=None, want_text_grads=False,
                        scale=0.0, workspace=None, stream=None):
     """Gradients of rtr_attn_cross from its o and lse.  Returns (dq, dk_text,
@@ -446,8 +456,11 @@ def rtr_attn_cross_bwd(tc, q, o, lse, d_o, dq=None, dk_text=None, dv_text=None, 
         dk_text = torch.empty((n, H, d), dtype=q.dtype, device=q.device)
         dv_text = torch.empty((n, H, d), dtype=q.dtype, device=q.device)
     if workspace is None:
-        workspace = torch.empty(max(1, rtr_attn_bwd_workspace_size(Tq, H, d)), dtype=torch.uint8,
-                                device=q.device)
+        if dk_text is not None:
+            nbytes = rtr_attn_cross_bwd_workspace_size(Tq, dk_text.shape[0], H, d)
+        else:
+            nbytes = rtr_attn_bwd_workspace_size(Tq, H, d)
+        workspace = torch.empty(max(1, nbytes), dtype=torch.uint8, device=q.device)
     ws, ws_bytes = _workspace(workspace)
     _check(lib().rtr_attn_cross_bwd(tc.handle, _ptr(q), _ptr(o), _ptr(lse), _ptr(d_o), Tq, _ptr(dq),
                                     _ptr(dk_text), _ptr(dv_text), float(scale), ws, ws_bytes,

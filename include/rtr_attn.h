@@ -305,10 +305,14 @@ int rtr_attn_cross(const rtr_text_cache *tc, const void *q, void *o, float *lse,
  * same scale and bf16 output), dq [Tq, H, d] and, when dk_text and dv_text are
  * given, the gradients of the current condition's text keys and values
  * [n, H, d] (both NULL: the text is treated as constant).  bf16 cache, d = 128
- * only; workspace: rtr_attn_bwd_workspace_size(Tq, H, d) bytes, 256-byte
- * aligned.  No output may overlap an input, the cache or another output.
+ * only; workspace: rtr_attn_cross_bwd_workspace_size(Tq, n, H, d) bytes with
+ * text gradients (their fp32 partial sums when the few text key blocks are
+ * split over the query rows), rtr_attn_bwd_workspace_size(Tq, H, d) without;
+ * 256-byte aligned.  No output may overlap an input, the cache or another
+ * output.
  * Limits: Tq * H * d < 2^31.  Tq == 0 is a no-op; an empty cache is
  * RTR_ESTATE. */
+int rtr_attn_cross_bwd_workspace_size(int64_t Tq, int32_t n_text, int32_t H, int32_t d, size_t *bytes);
 int rtr_attn_cross_bwd(const rtr_text_cache *tc, const void *q, const void *o, const float *lse,
                        const void *d_o, int64_t Tq, void *dq, void *dk_text, void *dv_text, float scale,
                        void *workspace, size_t workspace_bytes, rtr_stream stream);
