@@ -22,10 +22,12 @@ Video Stylization with Autoregressive Diffusion Transformer", RTR-DiT):
     latent frame placed before the first frame; its TextKV is the
     cross-attention cache of the same section.
 
-Every function here is pinned by tests/test_oracle.py, tests/test_oracle_bwd.py,
-tests/test_oracle_cross.py, tests/test_oracle_blocks.py,
-tests/test_oracle_rope.py and tests/test_listkv.py against things other than itself (brute-force loops, textbook special cases,
-closed forms and invariants).
+Every function here is pinned by tests/test_oracle.py (which also holds the
+ListKV pins), tests/test_oracle_bwd.py, tests/test_oracle_cross.py,
+tests/test_oracle_blocks.py and tests/test_oracle_rope.py against things other
+than itself (brute-force loops, textbook special cases, closed forms, hand
+values and invariants); tests/test_oracle_mutants.py plants plausible slips and
+checks that a pin fails for each.
 """
 
 from .attention import (  # noqa: F401

@@ -109,3 +109,42 @@ def test_listkv_mutant_is_caught(monkeypatch, name, fn):
     assert not _fails(pins.test_listkv_matches_hand_schedule)
     monkeypatch.setattr(L.ListKV, name, fn)
     assert _fails(pins.test_listkv_matches_hand_schedule)
+
+
+# Position-aware reference (oracle/rope.py): a placement one frame off, and
+# the two plausible slips in the pair frequencies.
+import oracle.rope as RP  # noqa: E402
+from tests import test_oracle_rope as rope_pins  # noqa: E402
+
+
+def _shift_one_late(oldest_position, ref_frames):
+    return int(oldest_position) - int(ref_frames) + 1
+
+
+def _angles_two_i(positions, pairs, base):
+    i = np.arange(pairs, dtype=np.float64)
+    return np.asarray(positions, dtype=np.float64)[:, None] * np.power(float(base), -2 * i / pairs)[None, :]
+
+
+def _angles_positive(positions, pairs, base):
+    i = np.arange(pairs, dtype=np.float64)
+    return np.asarray(positions, dtype=np.float64)[:, None] * np.power(float(base), i / pairs)[None, :]
+
+
+ROPE_PINS = [
+    (rope_pins.test_rotation_closed_forms, ()),
+    (rope_pins.test_pair_frequencies_hand_values, ()),
+    (rope_pins.test_reference_placement_empty_window_first_chunk, ()),
+    (rope_pins.test_reference_placement_after_a_switch_and_a_rolled_window, ()),
+]
+
+
+@pytest.mark.parametrize("name,fn", [("reference_shift", _shift_one_late),
+                                     ("rope_angles", _angles_two_i),
+                                     ("rope_angles", _angles_positive)],
+                         ids=lambda x: getattr(x, "__name__", x))
+def test_rope_mutant_is_caught(monkeypatch, name, fn):
+    for pin, args in ROPE_PINS:
+        assert not _fails(pin, *args)
+    monkeypatch.setattr(RP, name, fn)
+    assert any(_fails(pin, *args) for pin, args in ROPE_PINS)

@@ -72,3 +72,84 @@ def test_reference_follows_the_window():
         np.testing.assert_allclose(o, outs[2], rtol=1e-10, atol=1e-12)
     # without the shift the reference drifts away and the outputs change
     assert not np.allclose(step(follow=False), outs[2], atol=1e-6)
+
+
+def test_pair_frequencies_hand_values():
+    """Pairs i >= 1 rotate at position * base^(-i / pairs) -- the usual rotary
+    frequencies base^(-2i / n) over the n = 2 * pairs rotated dimensions.  With
+    base 16 and 4 pairs the frequencies are 1, 1/2, 1/4, 1/8; at position 4 pi
+    the angles are 4 pi, 2 pi, pi and pi / 2, so the unit vector (1, 0) of each
+    pair goes to (1, 0), (1, 0), (-1, 0) and (0, 1); at position 2 pi / 3 pair 1
+    turns by pi / 3, to (1/2, sqrt(3)/2)."""
+    from oracle import rope as R
+    P, d = 4, 10
+    e = np.zeros((1, 1, d))
+    e[0, 0, 0:2 * P:2] = 1.0
+    e[0, 0, 2 * P:] = 7.0  # not rotated
+    r = R.rope_rotate(e, [4 * np.pi], P, base=16.0)[0, 0]
+    want = [1.0, 0.0, 1.0, 0.0, -1.0, 0.0, 0.0, 1.0, 7.0, 7.0]
+    np.testing.assert_allclose(r, want, atol=1e-12)
+    r = R.rope_rotate(e, [2 * np.pi / 3], P, base=16.0)[0, 0]
+    np.testing.assert_allclose(r[2:4], [0.5, np.sqrt(3.0) / 2.0], atol=1e-12)
+    # the second element of a pair rotates towards minus the first: (0, 1) at pi / 2 -> (-1, 0)
+    f = np.zeros((1, 1, d))
+    f[0, 0, 7] = 1.0
+    r = R.rope_rotate(f, [4 * np.pi], P, base=16.0)[0, 0]
+    np.testing.assert_allclose(r[6:8], [-1.0, 0.0], atol=1e-12)
+
+
+def _placement_case(R_frames, W, fill, base_id, seed):
+    """Stream step with the reference re-encoded by the oracle's placement
+    against the full-form oracle over [reference frames | window frames |
+    chunk frames] encoded at consecutive positions 0, 1, 2, ... (the reference
+    one frame before the first frame it precedes, Key Designs 1), on the chunk
+    rows."""
+    from oracle import rope as R
+    rng = np.random.default_rng(seed)
+    k, H, d, C, P = 3, 2, 8, 2, 3
+    n = lambda *s: rng.standard_normal(s)
+    raw_ref_k, ref_v = n(R_frames, k, H, d), n(R_frames, k, H, d)
+    # frames in generation order; frame id f is encoded at position f + offset
+    offset = 5
+    nfr = base_id + C
+    fk, fv, fq = n(nfr, k, H, d), n(nfr, k, H, d), n(nfr, k, H, d)
+    enc = lambda x, p: R.rope_rotate(x, np.full(x.shape[0], p), P)
+    win_ids = list(range(base_id - fill, base_id))
+    chunk_ids = list(range(base_id, base_id + C))
+    oldest = (win_ids[0] if win_ids else base_id) + offset
+    # streaming form: cached window keys encoded at their own positions; the
+    # reference, stored at positions 0..R-1, re-encoded in front of the oldest
+    ref0 = np.concatenate([enc(raw_ref_k[r], r) for r in range(R_frames)])
+    ref_placed = R.rope_rotate(ref0, np.full(ref0.shape[0], R.reference_shift(oldest, R_frames)), P)
+    pk = np.concatenate([ref_placed] + [enc(fk[f], f + offset) for f in win_ids])
+    pv = np.concatenate([ref_v.reshape(-1, H, d)] + [fv[f] for f in win_ids])
+    cq = np.concatenate([enc(fq[f], f + offset) for f in chunk_ids])
+    ck = np.concatenate([enc(fk[f], f + offset) for f in chunk_ids])
+    cv = np.concatenate([fv[f] for f in chunk_ids])
+    o, lse = oracle.attn_stream_step(pk, pv, cq, ck, cv, k)
+    # full form over the short sequence at consecutive positions from 0
+    seq = [(raw_ref_k[r], ref_v[r], None) for r in range(R_frames)]
+    seq += [(fk[f], fv[f], fq[f]) for f in win_ids + chunk_ids]
+    K = np.concatenate([enc(s[0], p) for p, s in enumerate(seq)])
+    V = np.concatenate([s[1] for s in seq])
+    Q = np.concatenate([enc(s[2], p) if s[2] is not None else np.zeros((k, H, d))
+                        for p, s in enumerate(seq)])
+    fo, flse = oracle.attn_block_causal(Q, K, V, k)
+    rows = slice(len(seq) * k - C * k, len(seq) * k)
+    # reference frames beyond the first are separate frames of the full form,
+    # which changes only the reference rows; every chunk row sees all of them
+    np.testing.assert_allclose(o, fo[rows], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, flse[:, rows], rtol=1e-10, atol=1e-12)
+
+
+def test_reference_placement_empty_window_first_chunk():
+    _placement_case(R_frames=1, W=3, fill=0, base_id=0, seed=11)
+    _placement_case(R_frames=2, W=3, fill=0, base_id=0, seed=12)
+
+
+def test_reference_placement_after_a_switch_and_a_rolled_window():
+    # empty window later in the stream (a switch that keeps no frame)
+    _placement_case(R_frames=1, W=3, fill=0, base_id=7, seed=13)
+    # a rolled window: frames 4..6 cached, chunk 7..8
+    _placement_case(R_frames=1, W=3, fill=3, base_id=7, seed=14)
+    _placement_case(R_frames=2, W=3, fill=2, base_id=9, seed=15)
