@@ -553,6 +553,21 @@ int key_segments(const rtr_kv_cache *kv, const void *kref, const void *k, const 
     return nseg;
 }
 
+// Whether [p, p + nb) overlaps memory that a step reads from the cache: a
+// window slot in use (the ring's other slots may hold a chunk that a producer
+// writes there before committing it in place), or the reference slot and its
+// rotated view.  A chunk placed there would be read twice, once as cached keys.
+bool aliases_cache(const rtr_kv_cache *kv, const void *p, int64_t nb) {
+    const int64_t fb = frame_bytes(kv);
+    for (int i = 0; i < kv->count; ++i) {
+        const int64_t off = (int64_t)((kv->head + i) % kv->W) * fb;
+        if (overlaps(p, nb, (const char *)kv->k_ring + off, fb) || overlaps(p, nb, (const char *)kv->v_ring + off, fb))
+            return true;
+    }
+    return overlaps(p, nb, kv->k_ref, fb * kv->R_cap) || overlaps(p, nb, kv->v_ref, fb * kv->R_cap) ||
+           (kv->k_ref_view && overlaps(p, nb, kv->k_ref_view, fb * kv->R_cap));
+}
+
 }  // namespace
 
 int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
@@ -582,6 +597,9 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
     const int64_t fb = frame_bytes(kv);
     const int64_t Tq = (int64_t)chunk_frames * kv->kpf;
     const int64_t in_b = fb * chunk_frames;
+    for (const void *x : {q, k, v})
+        if (aliases_cache(kv, x, in_b))
+            return fail(RTR_EINVAL, "q, k or v overlaps a window slot or the reference that the step reads");
     const int64_t out_b = Tq * kv->H * kv->d * esize(out_dtype);
     const int64_t lse_b = Tq * kv->H * 4;
     const void *ins[8] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, kv->k_ref_view};
@@ -655,6 +673,9 @@ int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *
     if (((uintptr_t)lse & 3u) != 0) return fail(RTR_EINVAL, "lse must be 4-byte aligned");
     const int64_t fb = frame_bytes(kv);
     const int64_t tb = fb * chunk_frames, lb = Tq * kv->H * 4, pb = P * kv->H * kv->d * 2;
+    for (const void *x : {q, k, v, o, d_o})
+        if (aliases_cache(kv, x, tb))
+            return fail(RTR_EINVAL, "q, k, v, o or d_o overlaps a window slot or the reference that the step reads");
     const int64_t out_sz[5] = {tb, tb, tb, dk_cache ? pb : 0, dv_cache ? pb : 0};
     const void *src[10] = {q, k, v, o, lse, d_o, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
     const int64_t src_sz[10] = {tb, tb, tb, tb, lb, tb, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};

@@ -183,7 +183,14 @@ int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new,
 
 /* Physical ring slots the next n_frames appends would be written to, in
  * order; frames that the same append would evict again get -1.  Changes
- * nothing.  Lets a producer write K/V straight into the ring. */
+ * nothing.  Lets a producer write K/V straight into the ring (zero-copy
+ * append).  Order: once the window is full these are the slots of the oldest
+ * frames, which every step until the commit still reads, so the producer
+ * writes them only after the last step that reads the current window is
+ * enqueued, on the same stream (or after it completes).  While the window has
+ * free slots, the slots it reports are not read by any step, and a chunk may
+ * be written there first and passed to the step as its k, v.  A step whose q,
+ * k or v overlaps a slot in use or the reference returns RTR_EINVAL. */
 int rtr_kv_next_slots(const rtr_kv_cache *kv, int32_t n_frames, int32_t *slots);
 
 /* Metadata-only commit of n_frames frames that the caller has already written
@@ -200,6 +207,9 @@ int rtr_kv_commit_inplace(rtr_kv_cache *kv, int32_t n_frames);
  * afterwards with rtr_kv_append_evict.  o: [C*k, H, d] out_dtype; lse: [H, C*k]
  * float32 or NULL.  1 <= C <= RTR_MAX_CHUNK; scale <= 0 selects 1/sqrt(d).
  * workspace, workspace_bytes: split-K scratch as for rtr_attn_block_causal.
+ * q, k and v may lie in ring slots that the window does not use (a chunk
+ * written where rtr_kv_next_slots put it), never in a slot in use or in the
+ * reference slot (RTR_EINVAL); o and lse overlap no input and no cache buffer.
  * ---------------------------------------------------------------------- */
 int rtr_attn_stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                          void *o, float *lse, int32_t chunk_frames, rtr_dtype out_dtype,
@@ -241,7 +251,8 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
  *             differentiated (P == 0 writes nothing).
  * bf16 cache, d = 128 only.  workspace: rtr_attn_bwd_workspace_size(C*k, H,
  * d) bytes, 256-byte aligned, overlapping no argument.  No output may overlap
- * an input, the cache buffers or another output.  Limits: C*k * H * d < 2^31.
+ * an input, the cache buffers or another output; q, k, v, o and d_o may not
+ * overlap a window slot in use or the reference slot.  Limits: C*k * H * d < 2^31.
  * Returns RTR_OK or a negative rtr_status; every argument is checked before
  * anything is enqueued (a failing launch reports RTR_EHIP).
  * ---------------------------------------------------------------------- */

@@ -442,3 +442,38 @@ def test_cross_bwd_rejections():
     tc64 = rtr.TextCache(FAKE, FAKE + MB, 64, H, 64, rtr.RTR_BF16)
     L.rtr_text_cache_reset(tc64.handle, None, None, 30, None)
     assert call(h=tc64.handle) == rtr.RTR_EUNSUPPORTED
+
+
+def test_step_rejects_a_chunk_in_a_slot_the_window_uses():
+    """Zero-copy append: a chunk may sit in ring slots the window does not use
+    (where rtr_kv_next_slots puts it), never in a slot in use or in the
+    reference slot, for the step and for its backward."""
+    W, kpf, H, d = 3, 8, 2, 128
+    fb = kpf * H * d * 2
+    kv = _cache(W=W, R=1, kpf=kpf, H=H, d=d)
+    L = rtr.lib()
+    h = kv.handle
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, None, None, 1, -1)
+    rtr.rtr_kv_commit_inplace(kv, 2)                      # slots 0 and 1 in use, slot 2 free
+    assert list(rtr.rtr_kv_next_slots(kv, 1)) == [2]
+    k_ring, v_ring, k_ref = FAKE, FAKE + 64 * fb + 4096, FAKE + 128 * fb + 8192   # as _cache lays them out
+    far = FAKE + 900 * MB
+
+    def step(q=far, k=far + MB, v=far + 2 * MB):
+        return L.rtr_attn_stream_step(h, q, k, v, far + 3 * MB, None, 1, 0, 0.0, None, 0, None)
+
+    assert step(k=k_ring) == rtr.RTR_EINVAL                # slot 0 (oldest) in use
+    assert step(v=v_ring + fb) == rtr.RTR_EINVAL           # slot 1 in use
+    assert step(k=k_ring + fb + fb // 2) == rtr.RTR_EINVAL  # starts inside slot 1
+    assert step(q=k_ring + fb) == rtr.RTR_EINVAL
+    assert step(k=k_ref) == rtr.RTR_EINVAL                 # the reference slot
+    assert "window slot" in L.rtr_last_error().decode()
+    assert _sbwd(kv, k=k_ring + fb) == rtr.RTR_EINVAL
+    assert _sbwd(kv, o=v_ring) == rtr.RTR_EINVAL
+    assert _sbwd(kv, do=k_ref) == rtr.RTR_EINVAL
+    # once the window is full, the reported slot is the oldest frame's
+    rtr.rtr_kv_commit_inplace(kv, 1)
+    assert list(rtr.rtr_kv_next_slots(kv, 1)) == [0]
+    assert step(k=k_ring + 2 * fb) == rtr.RTR_EINVAL
+    assert step(k=k_ring) == rtr.RTR_EINVAL
+    assert _sbwd(kv, v=v_ring + 2 * fb) == rtr.RTR_EINVAL
