@@ -126,6 +126,79 @@ def cpu_baseline(workload, x, w, heads):
             "sample": sample, "seconds": round(dt, 3)}
 
 
+def prewarm(step, dev, seconds):
+    """Untimed back-to-back steps for `seconds` of wall time, so that the GPU
+    has left its idle clock before the counted warm-up steps (an idle MI355X
+    sits at a few hundred MHz and takes tens of milliseconds to ramp up, longer
+    than a short timed region).  Returns the number of steps run."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize(dev)
+    return n
+
+
+def device_info(dev):
+    import torch
+    p = torch.cuda.get_device_properties(dev)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
+def clock_mhz(dev):
+    """Shader clock right now (library clock probe, ~50 us), in MHz."""
+    from causal_attention_frame_amd import rtr
+    return round(rtr.rtr_clock_sample(dev), 1)
+
+
+def timing_stats(ms):
+    return {"kernel_avg_us": round(float(np.mean(ms)) * 1e3, 2),
+            "kernel_median_us": round(float(np.median(ms)) * 1e3, 2),
+            "kernel_min_us": round(float(np.min(ms)) * 1e3, 2)}
+
+
+def cpu_single_thread(workload_x, w):
+    """The float64 oracle on one host thread (BLAS limited to 1 thread): the
+    tiny float32 workload (full form, 144 tokens) and one head of the
+    Wan-1.3B streaming step, as TFLOP/s."""
+    import oracle
+    from causal_attention_frame_amd import inputs as gen
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    out = {}
+    with threadpool_limits(limits=1):
+        tw = gen.WORKLOADS["tiny_fp32"]
+        T = tw["k"] * tw["frames"]
+        q, k, v = gen.full_sequence_inputs(T, tw["H"], tw["d"], "f32", base_seed=0, wid=tw["wid"])
+        t0 = time.perf_counter()
+        reps = 20
+        for _ in range(reps):
+            oracle.attn_block_causal(q.values, k.values, v.values, tw["k"])
+        dt = (time.perf_counter() - t0) / reps
+        f = 4 * tw["d"] * tw["H"] * full_pairs_per_head(T, tw["k"])
+        out["tiny_fp32_full"] = {"value": f / dt / 1e12, "unit": "TFLOP/s", "seconds_per_call": round(dt, 5),
+                                 "sample": f"oracle.attn_block_causal, {T} tokens x {tw['H']} heads"}
+        if workload_x is not None:
+            x, H, d, kpf = workload_x["x"], w["H"], w["d"], w["k"]
+            sl = slice(0, 1)
+            pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])[:, sl]
+            pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])[:, sl]
+            t0 = time.perf_counter()
+            oracle.attn_stream_step(pk, pv, x["q"].values[:, sl], x["k"].values[:, sl], x["v"].values[:, sl], kpf)
+            dt = time.perf_counter() - t0
+            C = x["q"].shape[0] // kpf
+            f = 4 * d * stream_pairs_per_head(kpf, C, x["ref_k"].shape[0] + w["W"])
+            out["stream_step_one_head"] = {"value": f / dt / 1e12, "unit": "TFLOP/s", "seconds": round(dt, 3),
+                                           "sample": f"oracle.attn_stream_step, head 0 of {H}, all {C * kpf} rows"}
+    out["cores"] = 1
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +213,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=12,
                     help="heads of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="untimed wall-clock seconds of steps before the warm-up steps (GPU clock ramp)")
     ap.add_argument("--chunk-frames", type=int, default=0,
                     help="streaming forward workloads: frames per chunk (default: the workload's; "
                          "1 is the lowest-latency streaming step)")
@@ -240,9 +315,13 @@ def main():
         def commit():
             pass
 
-    for _ in range(args.warmup):
+    def whole_step():
         attention()
         commit()
+
+    nwarm = prewarm(whole_step, dev, args.prewarm_s)
+    for _ in range(args.warmup):
+        whole_step()
     torch.cuda.synchronize(dev)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -250,6 +329,7 @@ def main():
     evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
+    mhz_before = clock_mhz(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
@@ -260,6 +340,7 @@ def main():
         evc[i][1].record(stream)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    mhz_after = clock_mhz(dev)
 
     attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
     commit_ms = np.array([a.elapsed_time(b) for a, b in evc])
@@ -298,10 +379,11 @@ def main():
             "kernel": ("attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16")
                       + ("" if ws is None else " (+ attn_combine_d128 when the library splits)"),
             "schedule": "plain" if ws is None else "workspace given: split-K where the planner predicts a gain",
-            "kernel_avg_us": round(attn_avg_s * 1e6, 2),
-            "kernel_min_us": round(float(attn_ms.min()) * 1e3, 2),
+            **timing_stats(attn_ms),
             "algorithmic_flop_per_launch": flops,
         },
+        "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
+                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if append_bytes:
         cs = float(np.median(commit_ms)) * 1e-3
@@ -312,6 +394,10 @@ def main():
                             "algorithmic_bytes": append_bytes}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, x, w, args.cpu_heads)
+        if args.workload == "wan13b_stream_step":
+            st = cpu_single_thread({"x": x}, w)
+            if st is not None:
+                out["cpu_baseline_single_thread"] = st
     print(json.dumps(out), flush=True)
 
 
@@ -339,9 +425,11 @@ def backward(args, w, dev):
     def step():
         rtr.rtr_attn_block_causal_bwd(q, k, v, o, lse, do, kpf, dq, dk, dv, workspace=ws)
 
+    nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -351,6 +439,7 @@ def backward(args, w, dev):
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    mhz_after = clock_mhz(dev)
     call_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = elapsed * 1e3 / args.steps
     call_s = float(call_ms.mean()) * 1e-3
@@ -377,10 +466,11 @@ def backward(args, w, dev):
             "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic("full_block_causal_bwd"),
             "kernel": "attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128 (one call)",
-            "kernel_avg_us": round(call_s * 1e6, 2),
-            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            **timing_stats(call_ms),
             "algorithmic_flop_per_launch": flops,
         },
+        "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
+                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -446,9 +536,11 @@ def stream_backward(args, w, dev):
     def step():
         rtr.rtr_attn_stream_step_bwd(kv, q, k, v, o, lse, do, C, 1, dq, dk, dv, dkc, dvc, workspace=ws)
 
+    nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -458,6 +550,7 @@ def stream_backward(args, w, dev):
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    mhz_after = clock_mhz(dev)
     call_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = elapsed * 1e3 / args.steps
     call_s = float(call_ms.mean()) * 1e-3
@@ -486,10 +579,11 @@ def stream_backward(args, w, dev):
             "frac": round(flops / call_s / 1e12 / PEAK_BF16_TFLOPS, 4),
             "traffic": read_traffic(args.workload) if cache_grads and R == w["R"] else None,
             "kernel": "attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128<SEG> (one call)",
-            "kernel_avg_us": round(call_s * 1e6, 2),
-            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            **timing_stats(call_ms),
             "algorithmic_flop_per_launch": flops,
         },
+        "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
+                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -552,9 +646,11 @@ def cross(args, w, dev):
         else:
             rtr.rtr_attn_cross(tc, q, o=o, workspace=ws)
 
+    nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
+    mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -564,6 +660,7 @@ def cross(args, w, dev):
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    mhz_after = clock_mhz(dev)
     call_ms = np.array([a.elapsed_time(b) for a, b in ev])
     # text switch: re-initialise the cache with a condition of the same length
     er = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -600,10 +697,11 @@ def cross(args, w, dev):
             "traffic": None,
             "kernel": ("attn_bwd_prep + attn_bwd_dkdv_d128 + attn_bwd_dq_d128<SEG> (one call)" if bwd else
                        "attn_fwd_bf16_d128" + ("" if ws is None else " (+ split-K when planned)")),
-            "kernel_avg_us": round(call_s * 1e6, 2),
-            "kernel_min_us": round(float(call_ms.min()) * 1e3, 2),
+            **timing_stats(call_ms),
             "algorithmic_flop_per_launch": flops,
         },
+        "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
+                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
         "text_reset": {"bound": "hbm", "median_us": round(reset_s * 1e6, 2),
                        "achieved": round(reset_bytes / reset_s / 1e9, 1), "unit": "GB/s",
                        "peak": PEAK_HBM_GBS, "algorithmic_bytes": reset_bytes},
@@ -686,14 +784,17 @@ def rollout(args, w, dev):
                 ev[i][1].record(stream)
             rtr.rtr_kv_append_evict(kv, k, v, C)
 
+    nwarm = prewarm(one_rollout, dev, args.prewarm_s)
     for _ in range(args.warmup):
         one_rollout()
     torch.cuda.synchronize(dev)
+    mhz_before = clock_mhz(dev)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         one_rollout()
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
+    mhz_after = clock_mhz(dev)
     # one more rollout with events around each stream step, for the kernel time
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(chunks)]
@@ -733,6 +834,8 @@ def rollout(args, w, dev):
             "kernel_avg_us": round(attn_s / chunks * 1e6, 2),
             "algorithmic_flop_per_launch": round(flops_total / chunks),
         },
+        "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
+                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     rtr.rtr_kv_destroy(kv)
     if not args.no_cpu_baseline:

@@ -690,7 +690,7 @@ int bwd_split(int64_t T, int32_t H, int64_t prefix, bool cross) {
 }  // namespace
 
 hipError_t attention_cross_bwd_workspace_bytes(int64_t Tq, int64_t n, int32_t H, size_t *bytes) {
-    attention_bwd_workspace_bytes(Tq, H, bytes);
+    if (const hipError_t e = attention_bwd_workspace_bytes(Tq, H, bytes)) return e;
     const int ns = bwd_split(Tq, H, n, true);
     if (ns > 1) *bytes = (*bytes + 255) / 256 * 256 + (size_t)ns * n * H * 2 * kD * sizeof(float);
     return hipSuccess;
@@ -747,7 +747,7 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
             a.tpp = (a.nqt + a.nsplit - 1) / a.nsplit;
             if (a.nsplit > 1) {
                 size_t prep = 0;
-                attention_bwd_workspace_bytes(p.T, p.H, &prep);
+                if (const hipError_t e = attention_bwd_workspace_bytes(p.T, p.H, &prep)) return e;
                 a.part = (float *)((char *)p.ws + (prep + 255) / 256 * 256);
             }
         }

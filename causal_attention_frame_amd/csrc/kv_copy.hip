@@ -95,6 +95,22 @@ __global__ __launch_bounds__(kThreads) void ref_rotate_f32(const RotateArgs a) {
     ((u32x4 *)a.dst)[i] = o;
 }
 
+// Clock probe: one lane reads the shader-clock counter (s_memtime) and the
+// constant 100 MHz counter (s_memrealtime) until `span` ticks of the latter
+// have passed (at most 2^22 reads), and stores both differences.  Their ratio
+// times 100 MHz is the shader clock over that interval.
+__global__ __launch_bounds__(64) void clock_probe(unsigned long long *out, unsigned long long span) {
+    if (threadIdx.x != 0) return;
+    const unsigned long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long t1 = t0, r1 = r0;
+    for (int i = 0; i < (1 << 22) && r1 - r0 < span; ++i) {
+        t1 = __builtin_amdgcn_s_memtime();
+        r1 = __builtin_amdgcn_s_memrealtime();
+    }
+    out[0] = t1 - t0;
+    out[1] = r1 - r0;
+}
+
 }  // namespace
 
 hipError_t launch_ref_rotate(const RotateJob &j, hipStream_t stream) {
@@ -133,6 +149,11 @@ hipError_t launch_frame_copies(const CopyJobs &jobs, hipStream_t stream) {
     const int64_t per_block = kThreads * kUnroll;
     const dim3 grid((unsigned)((a.n16 + per_block - 1) / per_block), (unsigned)jobs.n);
     hipLaunchKernelGGL(frame_copy, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_clock_probe(unsigned long long *out, int64_t span_ticks, hipStream_t stream) {
+    hipLaunchKernelGGL(clock_probe, dim3(1), dim3(64), 0, stream, out, (unsigned long long)span_ticks);
     return hipGetLastError();
 }
 

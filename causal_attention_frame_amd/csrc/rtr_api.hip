@@ -976,6 +976,14 @@ int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, 
     return ok();
 }
 
+int rtr_clock_sample(uint64_t *ticks, int64_t span_ticks, rtr_stream stream) {
+    if (!ticks || ((uintptr_t)ticks & 7u) != 0) return fail(RTR_EINVAL, "ticks must be a non-NULL 8-byte aligned device pointer");
+    if (span_ticks < 1 || span_ticks > 1000000) return fail(RTR_EINVAL, "span_ticks=%lld outside [1, 1e6]", (long long)span_ticks);
+    if (const hipError_t e = rtr::launch_clock_probe((unsigned long long *)ticks, span_ticks, (hipStream_t)stream))
+        return hip_fail(e, "clock probe launch");
+    return ok();
+}
+
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out) {
     if (int rc = check_cache(kv)) return rc;
     if (!out) return fail(RTR_EINVAL, "out is NULL");

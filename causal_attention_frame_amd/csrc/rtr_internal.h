@@ -109,4 +109,8 @@ struct RotateJob {
 
 hipError_t launch_ref_rotate(const RotateJob &j, hipStream_t stream);
 
+// Shader-clock probe: out[0] shader-clock ticks and out[1] 100 MHz ticks over
+// about span_ticks of the latter (device buffer of two 64-bit words).
+hipError_t launch_clock_probe(unsigned long long *out, int64_t span_ticks, hipStream_t stream);
+
 }  // namespace rtr

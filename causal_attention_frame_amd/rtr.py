@@ -82,6 +82,7 @@ _SIGNATURES = {
     "rtr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rtr_last_error": (ctypes.c_char_p, []),
     "rtr_version": (ctypes.c_int, []),
+    "rtr_clock_sample": (ctypes.c_int, [_vp, _c_i64, _vp]),
 }
 
 _lib = None
@@ -467,4 +468,15 @@ def rtr_attn_cross_bwd(tc, q, o, lse, d_o, dq=None, dk_text=None, dv_text=None, 
                                     _stream(stream, q.device)),
            "rtr_attn_cross_bwd")
     return dq, dk_text, dv_text
+
+
+def rtr_clock_sample(device, span_ticks=5000, stream=None):
+    """Shader clock in MHz over ~span_ticks / 100 MHz (default 50 us), measured
+    by the library's clock probe on `device`'s current stream; synchronizes."""
+    import torch
+    buf = torch.zeros(2, dtype=torch.int64, device=device)
+    _check(lib().rtr_clock_sample(_ptr(buf), int(span_ticks), _stream(stream, buf.device)),
+           "rtr_clock_sample")
+    t = buf.cpu().tolist()
+    return 100.0 * t[0] / t[1] if t[1] > 0 else float("nan")
 

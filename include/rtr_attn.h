@@ -353,6 +353,15 @@ int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, 
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out);
 int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in);
 
+/* Measurement helper (not part of the method): enqueues one single-lane
+ * kernel that reads the shader-clock counter and the constant 100 MHz
+ * counter until span_ticks (1..1e6) ticks of the latter have passed, and
+ * writes the two differences to ticks[0] (shader clock) and ticks[1]
+ * (100 MHz), a caller-owned device buffer of two 64-bit words.  The shader
+ * clock over that interval is ticks[0] / ticks[1] * 100 MHz.  Returns
+ * RTR_EINVAL for a NULL or misaligned buffer or a span out of range. */
+int rtr_clock_sample(uint64_t *ticks, int64_t span_ticks, rtr_stream stream);
+
 /* Diagnostics. */
 const char *rtr_status_string(int code);
 const char *rtr_last_error(void);
