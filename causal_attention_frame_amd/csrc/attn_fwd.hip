@@ -28,7 +28,6 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
-#include <vector>
 #include <climits>
 #include <cmath>
 #include <cstddef>
@@ -891,6 +890,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
 constexpr int kD128BM = 256, kD128BN = 32;
 constexpr int kMaxSplitUnits = 256;                       // units of a split launch
 constexpr int kSlotFloats = kD128BM * 128 + 2 * kD128BM;  // partial O, reference, sum
+static_assert(kSlotFloats * sizeof(float) == kSplitSlotBytes, "slot size");
 
 __device__ inline int block_tiles(int qb, const KArgs &a) {
     const int last = min(qb * kD128BM + kD128BM - 1, a.Tq - 1);
@@ -1580,25 +1580,30 @@ constexpr double kSplitMargin = 0.9;
 // Chooses T, P and m by simulating the split schedule (see the work
 // decomposition comment) on the problem's unit lengths; false when the split
 // would not beat the plain launch by a margin.  Plans are cached per shape.
-bool plan_split(const KArgs &k, int64_t H, int G, SplitPlan *out) {
+bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, SplitPlan *out) {
+    // Fixed-size storage throughout: planning allocates nothing (also on the
+    // host), so callers that may not allocate can use the split path.
     struct Entry {
-        int64_t key[6];
+        int64_t key[7];
         bool ok;
         SplitPlan plan;
     };
+    constexpr int kCache = 64;
     static std::mutex mu;
-    static std::vector<Entry> cache;
-    const int64_t key[6] = {k.Tq, k.Tk, k.kpf, k.prefix, H, G};
+    static Entry cache[kCache];
+    static int ncache = 0, next = 0;
+    const int64_t key[7] = {k.Tq, k.Tk, k.kpf, k.prefix, H, G, max_slots};
     {
         std::lock_guard<std::mutex> lock(mu);
-        for (const Entry &e : cache)
-            if (std::equal(key, key + 6, e.key)) {
-                *out = e.plan;
-                return e.ok;
+        for (int i = 0; i < ncache; ++i)
+            if (std::equal(key, key + 7, cache[i].key)) {
+                *out = cache[i].plan;
+                return cache[i].ok;
             }
     }
     const int64_t nqb = k.nqb, U = nqb * H, S = G - U;
-    std::vector<int64_t> nq(nqb);
+    if (nqb > kMaxSplitUnits || S <= 0) return false;
+    int64_t nq[kMaxSplitUnits];
     int64_t nmax = 0, total = 0;
     for (int64_t qb = 0; qb < nqb; ++qb) {
         nq[qb] = host_block_tiles(qb, k);
@@ -1609,20 +1614,26 @@ bool plan_split(const KArgs &k, int64_t H, int G, SplitPlan *out) {
     double best = (double)nmax * kSplitMargin;  // the plain launch's makespan, less a margin
     bool ok = false;
     SplitPlan bp{};
-    std::vector<int32_t> len;
+    const int64_t kmax = std::min<int64_t>(max_slots - U, 2 * kMaxSplitUnits);
+    int32_t len[2 * kMaxSplitUnits];
     const int64_t tlo = std::max<int64_t>(1, (int64_t)(0.7 * (double)total / (double)G));
-    for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128}) {
+    for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256}) {
         for (int64_t T = tlo; T < nmax; ++T) {
-            len.clear();
-            int64_t split_units = 0;
-            for (int64_t h = 0; h < H; ++h)
-                for (int64_t qb = 0; qb < nqb; ++qb) {
+            int64_t K = 0, split_units = 0;
+            bool over = false;
+            for (int64_t h = 0; h < H && !over; ++h)
+                for (int64_t qb = 0; qb < nqb && !over; ++qb) {
                     const int64_t r = nq[qb] - T;
                     if (r > 0) ++split_units;
-                    for (int64_t o = 0; o < r; o += P) len.push_back((int32_t)std::min<int64_t>(P, r - o));
+                    for (int64_t o = 0; o < r; o += P) {
+                        if (K >= kmax) {
+                            over = true;
+                            break;
+                        }
+                        len[K++] = (int32_t)std::min<int64_t>(P, r - o);
+                    }
                 }
-            const int64_t K = (int64_t)len.size();
-            if (K == 0 || U + K > 2 * (int64_t)G) continue;
+            if (over || K == 0) continue;
             double mk = (double)std::min(nmax, T) + ov;  // the mains
             for (int64_t s = 0; s < S; ++s) {             // the spares
                 double f = 0.0;
@@ -1638,12 +1649,12 @@ bool plan_split(const KArgs &k, int64_t H, int G, SplitPlan *out) {
         }
     }
     std::lock_guard<std::mutex> lock(mu);
-    if (cache.size() >= 64) cache.erase(cache.begin());
-    Entry e;
-    std::copy(key, key + 6, e.key);
+    Entry &e = cache[next];
+    next = (next + 1) % kCache;
+    ncache = std::min(ncache + 1, kCache);
+    std::copy(key, key + 7, e.key);
     e.ok = ok;
     e.plan = bp;
-    cache.push_back(e);
     *out = bp;
     return ok;
 }
@@ -1680,7 +1691,8 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
             bool fit = G > U;  // every XCD has a workgroup for each of its mains
             for (int64_t x = 0; fit && x < 8; ++x) fit = (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
             SplitPlan plan{};
-            if (fit && plan_split(k, p.H, (int)G, &plan)) {
+            const int64_t max_slots = p.ws_slots > 0 ? std::min<int64_t>(p.ws_slots, 2 * G) : 2 * G;
+            if (fit && plan_split(k, p.H, (int)G, max_slots, &plan)) {
                 k.ws = (float *)p.ws;
                 k.nprog = (int32_t)G;
                 k.units = (int32_t)U;

@@ -19,6 +19,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -141,7 +142,7 @@ int hip_fail(hipError_t e, const char *what) {
 // the call's other buffers; *use is the pointer to hand to the launch (NULL when
 // none is given or the configuration never splits).
 int check_workspace(void *ws, size_t ws_bytes, int32_t d, rtr_dtype dt, const void *const *bufs,
-                    const int64_t *sizes, int nbufs, void **use) {
+                    const int64_t *sizes, int nbufs, void **use, int32_t ws_slots = 0) {
     *use = nullptr;
     if (!ws) return RTR_OK;
     if (!aligned16(ws)) return fail(RTR_EINVAL, "workspace must be 16-byte aligned");
@@ -150,11 +151,46 @@ int check_workspace(void *ws, size_t ws_bytes, int32_t d, rtr_dtype dt, const vo
             return fail(RTR_EINVAL, "workspace overlaps an input, output or cache buffer");
     size_t need = 0;
     if (const hipError_t e = rtr::attention_workspace_bytes(d, dt, &need)) return hip_fail(e, "workspace size");
+    // a slot-capped workspace: the split launch uses at most ws_slots slots
+    if (ws_slots > 0 && need > 0) need = std::min(need, (size_t)ws_slots * rtr::kSplitSlotBytes);
     if (ws_bytes < need)
         return fail(RTR_EINVAL, "workspace of %zu bytes, %zu needed on this device", ws_bytes, need);
     *use = need ? ws : nullptr;
     return RTR_OK;
 }
+
+// Split-K scratch of rtr_attn_stream_step_noalloc, for callers that cannot
+// allocate: a file-scope device array, one copy per GPU the library runs on,
+// held until the process ends.  kScratchSlots partial-result slots (34 MB);
+// the split planner keeps to that many.  Host code never uses the array's name
+// as an address: scratch_ptr() resolves this device's copy once (with the
+// device current) and keeps it.
+constexpr int32_t kScratchSlots = 256;
+constexpr size_t kScratchBytes = (size_t)kScratchSlots * rtr::kSplitSlotBytes;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+int scratch_ptr(void **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *ptrs[kMaxDevices] = {};
+    int dev = 0;
+    if (const hipError_t e = hipGetDevice(&dev)) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(RTR_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void *p = nullptr;
+        if (const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(RTR_EHIP, "scratch has no device address");
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return RTR_OK;
+}
+
+int stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v, void *o, float *lse,
+                int32_t chunk_frames, int32_t block_frames, rtr_dtype out_dtype, float scale, void *workspace,
+                size_t workspace_bytes, int32_t ws_slots, rtr_stream stream);
 
 }  // namespace
 
@@ -582,6 +618,26 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
                                  void *o, float *lse, int32_t chunk_frames, int32_t block_frames,
                                  rtr_dtype out_dtype, float scale, void *workspace,
                                  size_t workspace_bytes, rtr_stream stream) {
+    return stream_step(kv, q, k, v, o, lse, chunk_frames, block_frames, out_dtype, scale, workspace,
+                       workspace_bytes, 0, stream);
+}
+
+int rtr_attn_stream_step_noalloc(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                                 void *o, float *lse, int32_t chunk_frames, int32_t block_frames,
+                                 rtr_dtype out_dtype, float scale, rtr_stream stream) {
+    void *ws = nullptr;
+    if (int rc = scratch_ptr(&ws)) return rc;
+    return stream_step(kv, q, k, v, o, lse, chunk_frames, block_frames, out_dtype, scale, ws,
+                       kScratchBytes, kScratchSlots, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void *v, void *o, float *lse,
+                int32_t chunk_frames, int32_t block_frames, rtr_dtype out_dtype, float scale, void *workspace,
+                size_t workspace_bytes, int32_t ws_slots, rtr_stream stream) {
     if (int rc = check_cache(kv)) return rc;
     if (chunk_frames < 1 || chunk_frames > RTR_MAX_CHUNK)
         return fail(RTR_EUNSUPPORTED, "chunk_frames=%d outside [1, %d]", chunk_frames, RTR_MAX_CHUNK);
@@ -615,7 +671,8 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
         const void *bufs[9] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, o, lse};
         const int64_t sizes[9] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap,
                                   out_b, lse ? lse_b : 0};
-        if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws)) return rc;
+        if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws, ws_slots))
+            return rc;
     }
 
     const void *kref = nullptr;
@@ -623,6 +680,7 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
 
     rtr::AttnProblem p;
     p.ws = ws;
+    p.ws_slots = ws_slots;
     const int nseg = key_segments(kv, kref, k, v, chunk_frames, p.kseg, p.vseg);
     p.q = q;
     p.o = o;
@@ -642,6 +700,10 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return ok();
 }
+
+}  // namespace
+
+extern "C" {
 
 int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
                              const void *o, const float *lse, const void *d_o, int32_t chunk_frames,

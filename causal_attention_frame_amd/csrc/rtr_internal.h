@@ -40,9 +40,16 @@ struct AttnProblem {
     rtr_dtype in_dtype = RTR_BF16, out_dtype = RTR_BF16;
     // Split-K workspace (attention_workspace_bytes() bytes) or null: with it the
     // head_dim-128 bf16 kernel balances the key tiles over the compute units
-    // and a second kernel merges the partial results.
+    // and a second kernel merges the partial results.  ws_slots > 0 caps the
+    // partial-result slots a split may use (a workspace of that many slots,
+    // kSplitSlotBytes each); 0 means the full attention_workspace_bytes().
     void *ws = nullptr;
+    int32_t ws_slots = 0;
 };
+
+// Bytes of one partial-result slot of the split launch (256 rows x 128 fp32
+// plus two fp32 statistics per row).
+constexpr size_t kSplitSlotBytes = (size_t)(256 * 128 + 2 * 256) * sizeof(float);
 
 hipError_t launch_attention(const AttnProblem &p, hipStream_t stream);
 

@@ -83,6 +83,8 @@ _SIGNATURES = {
     "rtr_last_error": (ctypes.c_char_p, []),
     "rtr_version": (ctypes.c_int, []),
     "rtr_clock_sample": (ctypes.c_int, [_vp, _c_i64, _vp]),
+    "rtr_attn_stream_step_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                                    ctypes.c_int, _c_f32, _vp]),
 }
 
 _lib = None
@@ -324,6 +326,17 @@ def rtr_attn_stream_step(kv, q, k, v, chunk_frames, o=None, lse=None, scale=0.0,
                                       int(chunk_frames), _dtype_code(o), float(scale), ws, ws_bytes,
                                       _stream(stream, q.device)),
            "rtr_attn_stream_step")
+    return o, lse
+
+
+def rtr_attn_stream_step_noalloc(kv, q, k, v, chunk_frames, o, lse=None, block_frames=1, scale=0.0,
+                                 stream=None):
+    """The streaming step with the library's static split-K scratch: o (and
+    lse) are caller-provided, nothing is allocated.  Returns (o, lse)."""
+    _check(lib().rtr_attn_stream_step_noalloc(kv.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                              int(chunk_frames), int(block_frames), _dtype_code(o),
+                                              float(scale), _stream(stream, q.device)),
+           "rtr_attn_stream_step_noalloc")
     return o, lse
 
 

@@ -228,6 +228,22 @@ int rtr_attn_stream_step_blocked(const rtr_kv_cache *kv, const void *q, const vo
                                  rtr_dtype out_dtype, float scale, void *workspace,
                                  size_t workspace_bytes, rtr_stream stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * streaming step of rtr_attn_stream_step_blocked with its split-K scratch in a
+ * static device array inside the library (34 MB per GPU, held from the first
+ * call on that GPU until the process ends) instead of a caller workspace.  It
+ * calls no device allocation routine.  The split planner keeps to that
+ * scratch (256 partial-result slots); a problem that would need more runs
+ * with fewer, longer pieces or unsplit, so no input size exceeds it.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (concurrent streams, or several host threads) race and must be
+ * serialised by the caller.  Other arguments, results and errors as
+ * rtr_attn_stream_step_blocked. */
+int rtr_attn_stream_step_noalloc(const rtr_kv_cache *kv, const void *q, const void *k, const void *v,
+                                 void *o, float *lse, int32_t chunk_frames, int32_t block_frames,
+                                 rtr_dtype out_dtype, float scale, rtr_stream stream);
+
 /* ------------------------------------------------------------------------
  * Gradients of one streaming step (Key Designs 2 and 4: the step's Attn over
  * [reference | window | chunk]; Key Designs 3 trains the causal generator by

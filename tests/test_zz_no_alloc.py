@@ -1,0 +1,93 @@
+"""rtr_attn_stream_step_noalloc: the streaming step with the library's static
+split-K scratch (for callers that cannot allocate), against the same step
+through rtr_attn_stream_step_blocked with a caller workspace, on two calls in
+a row on one cache, the second with a smaller input (a 2-frame chunk, then a
+1-frame chunk, at the Wan-1.3B layer shape), and on a small cache that never
+splits; O and LSE to the bf16 parity bar, and the small case also against the
+float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_attention_frame_amd import inputs as gen
+from causal_attention_frame_amd import rtr
+from tests.gpu_util import assert_bf16_close, dev, guarded_empty, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(kpf, H, d, W, R, wid):
+    x = gen.stream_inputs(kpf, H, d, 2, W, R, "bf16", base_seed=0, wid=wid)
+    kr = torch.zeros((W, kpf, H, d), dtype=torch.bfloat16, device="cuda")
+    vr = torch.zeros_like(kr)
+    kf = torch.zeros((R, kpf, H, d), dtype=torch.bfloat16, device="cuda")
+    vf = torch.zeros_like(kf)
+    kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, dev(x["ref_k"]), dev(x["ref_v"]), R, -1)
+    rtr.rtr_kv_append_evict(kv, dev(x["ring_k"]), dev(x["ring_v"]), W)
+    return kv, x, (kr, vr, kf, vf)
+
+
+def _both(kv, q, k, v, C, H, d):
+    Tq = q.shape[0]
+    o, chk = guarded_empty((Tq, H, d), torch.bfloat16)
+    lse, chk2 = guarded_empty((H, Tq), torch.float32)
+    rtr.rtr_attn_stream_step_noalloc(kv, q, k, v, C, o, lse)
+    ws = rtr.new_workspace(d, rtr.RTR_BF16, q.device)
+    ro, rl = rtr.rtr_attn_stream_step_blocked(kv, q, k, v, C, 1, want_lse=True, workspace=ws)
+    po, _ = rtr.rtr_attn_stream_step(kv, q, k, v, C)      # plain launch, no workspace
+    torch.cuda.synchronize()
+    chk()
+    chk2()
+    assert_bf16_close(host(o), host(ro), f"noalloc vs workspace o (C={C})")
+    assert_bf16_close(host(lse), host(rl), f"noalloc vs workspace lse (C={C})")
+    return o, lse, po
+
+
+def test_noalloc_two_calls_wan_shape_then_smaller():
+    kpf, H, d, W, R = 1560, 12, 128, 6, 1
+    kv, x, bufs = _cache(kpf, H, d, W, R, wid=401)
+    q2, k2, v2 = (dev(gen.normal((2 * kpf, H, d), "bf16", 0, 401, 7, t))
+                  for t in (gen.TAG_Q, gen.TAG_K, gen.TAG_V))
+    o2, l2, p2 = _both(kv, q2, k2, v2, 2, H, d)
+    q1, k1, v1 = q2[:kpf].contiguous(), k2[:kpf].contiguous(), v2[:kpf].contiguous()
+    o1, l1, p1 = _both(kv, q1, k1, v1, 1, H, d)
+    # the 1-frame chunk splits under the scratch's slot budget: its result is
+    # not the plain launch's bit for bit, and within the bar of it
+    assert not torch.equal(o1.view(torch.int16), p1.view(torch.int16))
+    assert_bf16_close(host(o1), host(p1), "noalloc vs plain (C=1)")
+    # the first call's output is untouched by the second
+    o2b, _, _ = _both(kv, q2, k2, v2, 2, H, d)
+    assert torch.equal(o2.view(torch.int16), o2b.view(torch.int16))
+    kv.close()
+
+
+def test_noalloc_small_cache_matches_oracle():
+    kpf, H, d, W, R = 96, 2, 128, 3, 1
+    kv, x, bufs = _cache(kpf, H, d, W, R, wid=402)
+    for C in (2, 1):
+        q, k, v = (x[n].values[:C * kpf] for n in ("q", "k", "v"))
+        qd, kd, vd = (dev(x[n])[:C * kpf].contiguous() for n in ("q", "k", "v"))
+        o, lse, _ = _both(kv, qd, kd, vd, C, H, d)
+        pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
+        pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
+        ro, rl = oracle.attn_stream_step(pk, pv, q, k, v, kpf)
+        assert_bf16_close(host(o), ro, f"noalloc vs oracle o (C={C})")
+        assert_bf16_close(host(lse), rl, f"noalloc vs oracle lse (C={C})")
+    kv.close()
+
+
+def test_noalloc_rejects_before_launch():
+    kpf, H, d, W, R = 96, 2, 128, 3, 1
+    kv, x, (kr, vr, kf, vf) = _cache(kpf, H, d, W, R, wid=403)
+    q = dev(x["q"])
+    o = torch.empty_like(q)
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.rtr_attn_stream_step_noalloc(kv, q, kr[0].view(kpf, H, d), dev(x["v"])[:kpf], 1, o[:kpf])
+    assert e.value.code == rtr.RTR_EINVAL
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.rtr_attn_stream_step_noalloc(kv, q, dev(x["k"]), dev(x["v"]), 0, o)
+    assert e.value.code == rtr.RTR_EUNSUPPORTED
+    kv.close()
