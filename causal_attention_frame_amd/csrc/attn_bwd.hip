@@ -111,16 +111,6 @@ __device__ inline int swz_plain(int r) { return r & 15; }
 // of 4, so neither read has a bank conflict.
 __device__ inline int swz_dual(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// acc += A B with the accumulator held in AGPRs.  This file is built with
-// builtin MFMAs in VGPR form (their results feed VALU code); the long-lived
-// dK/dV accumulators live in AGPRs through this statement instead, so that the
-// rest of the dK/dV kernel fits the 128 VGPRs of two waves per SIMD.  The s_nop covers a VALU write of an A or B operand
-// just before; the hardware forwards an exactly matching accumulator from the
-// previous MFMA of the same shape.
-__device__ inline void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
 // Segment holding key j (the float estimate corrected by one step).
 __device__ inline int seg_of(int j, const BArgs &a) {
     int f = (int)((float)j * a.inv_seg_len);
@@ -413,9 +403,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
 #pragma unroll 1
     for (; i < nt; ++i) step(i, std::false_type{});
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no DMA outlives the workgroup's LDS
-    // Wait states between the last accumulating MFMA and the reads of its
-    // AGPRs below (more than the 18 a 16-pass MFMA needs).
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    acc_settle();  // before the AGPR reads below
 
     if (!kvalid) return;
     if (PRE && a.nsplit > 1) {  // one piece of a split block: fp32 partials, reduced later

@@ -448,6 +448,16 @@ __device__ inline SegPtrs load_seg_ptrs(int f) {
                  : "memory");
     return {k[0], k[1], v[0], v[1]};
 }
+// The same four pointers as plain scalar loads, which the compiler waits for
+// where they are first used.
+__device__ inline SegPtrs load_seg_ptrs_ahead(int f) {
+    typedef __attribute__((address_space(4))) const uint64_t c_u64;
+    typedef __attribute__((address_space(4))) const char c_char;
+    c_char *ka = (c_char *)__builtin_amdgcn_kernarg_segment_ptr();
+    const c_u64 *kp = (const c_u64 *)(ka + offsetof(KArgs, kseg));
+    const c_u64 *vp = (const c_u64 *)(ka + offsetof(KArgs, vseg));
+    return {kp[f], kp[f + 1], vp[f], vp[f + 1]};
+}
 
 
 
@@ -491,6 +501,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
+    // byte strides of the DMA addressing (a segment is below 2^31 bytes)
+    const int32_t ld2 = (int32_t)(a.ld * 2), hoff2 = (int32_t)(hoff * 2);
 
     int qi[NB], lim[NB];
     bool qv[NB];
@@ -502,6 +514,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     }
     const int lim_wg_lo = key_limit(q0, a);
     const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
+    // Key limit of this wave's last valid row (limits grow with the row), 0
+    // for a wave without valid rows: steps past it skip the wave's MFMAs and
+    // softmax (it still loads its share of the tiles and meets the barriers).
+    const int r_last = q0 + 32 * NB * wave + 32 * NB - 1;
+    const int lim_wave = q0 + 32 * NB * wave < a.Tq ? key_limit(min(r_last, a.Tq - 1), a) : 0;
 
     if (!FAST) {
         for (int f = tid; f < a.nseg; f += 512) {
@@ -541,33 +558,40 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
     auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
 
-    // Key cursor of the next tile to prefetch (tiles are prefetched in order
-    // within a sweep): segment cf and key offset co inside it, wave-uniform.
-    // Past the last segment it wraps inside the last one, so look-ahead tiles
-    // beyond the keys still read valid (finite) rows, which the mask discards.
-    int cf = 0, co = 0;
-    SegPtrs sp{};
+    // DMA cursor of this wave's 4-row group (tiles are prefetched in order
+    // within a sweep; wave-uniform): the group's row drow inside segment dseg
+    // (a group never straddles two segments: segments hold a multiple of 4
+    // keys).  prepare() turns it into the K and V addresses of the next tile's
+    // group and moves it one tile on.  Past the last segment it wraps inside
+    // the last one, so look-ahead tiles beyond the keys still read valid
+    // (finite) rows, which the mask discards.  Steps call prepare() before
+    // their barrier, where its scalar work overlaps the wait.
+    // The segment pointers are loaded one tile ahead (nsp), so that their
+    // latency is not waited for at the barrier.
+    int drow = 0, dseg = 0;
+    uint64_t dkp = 0, dvp = 0;
+    SegPtrs nsp{};
     auto reset_cursor = [&]() {
-        cf = 0;
-        co = 0;
+        drow = 4 * wave;
+        dseg = 0;
+        if constexpr (FAST) nsp = load_seg_ptrs_ahead(0);
     };
-    auto load_ptrs = [&]() {
-        if constexpr (FAST) sp = load_seg_ptrs(cf);
+    auto prepare = [&]() {
+        if constexpr (FAST) {
+            const uint64_t off = (uint64_t)(uint32_t)(drow * ld2 + hoff2);
+            dkp = nsp.k0 + off;
+            dvp = nsp.v0 + off;
+            drow += BN;
+            const bool cr = drow >= a.seg_len;
+            drow = cr ? drow - a.seg_len : drow;
+            dseg = cr ? min(dseg + 1, a.nseg - 1) : dseg;
+            nsp = load_seg_ptrs_ahead(dseg);
+        }
     };
     auto issue = [&](int tile, auto S) {
         constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
-            const int row = co + 4 * wave;
-            const bool nxt = row >= a.seg_len;
-            const long rr = nxt ? row - a.seg_len : row;
-            const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-            dma16x2((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
-                          m0v(st, 0));
-            co += BN;
-            if (co >= a.seg_len) {
-                co -= a.seg_len;
-                cf = min(cf + 1, a.nseg - 1);
-            }
+            dma16x2(dkp, dvp, kvo[0], vvo[0], m0k(st, 0), m0v(st, 0));
         } else {
             const int j0 = tile * BN;
 #pragma unroll
@@ -702,12 +726,21 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
-        load_ptrs();  // segment pointers of tile t + 3
+        prepare();  // DMA addresses of tile t + 3
+        // this wave's DMA of tile t+1 has landed (t+2 may still be in flight);
+        // after the barrier every wave's has, and every wave is done with
+        // step t-1, so the stage of tile t-2 is free
         __builtin_amdgcn_s_waitcnt(wait_vm(2));
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
+        if (MASK && (t - 1) * BN >= lim_wave) {
+            // nothing left for this wave: tiles t-1 and later lie past every
+            // one of its rows' limits (only in the masked tail, so that the
+            // unmasked steps stay one basic block)
+            issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
+            return;
+        }
         float mr[NB] = {mref[0]};
         if (MASK) {
             const int t0 = t * BN;
@@ -758,16 +791,44 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     };
     auto sweep = [&](bool first_sweep, auto maxonly) {
         reset_cursor();
-        load_ptrs();
+        prepare();
         issue(0, I0{});
-        load_ptrs();
+        prepare();
         issue(1, I1{});
-        load_ptrs();
+        prepare();
         issue(2, I2{});
         __builtin_amdgcn_s_waitcnt(wait_vm(4));  // tile 0 landed
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
+        if (lim_wave == 0) {
+            // A wave without valid rows only loads its share of the tiles and
+            // meets the barriers of the steps.
+            auto idle = [&](int t, auto S) {
+                constexpr int s0 = decltype(S)::value;
+                prepare();
+                __builtin_amdgcn_s_waitcnt(wait_vm(2));
+                compiler_fence();
+                __builtin_amdgcn_s_barrier();
+                compiler_fence();
+                issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
+            };
+#pragma unroll 1
+            for (int base = 0; base <= ntiles; base += 5) {
+                idle(base, I0{});
+                if (base + 1 > ntiles) break;
+                idle(base + 1, I1{});
+                if (base + 2 > ntiles) break;
+                idle(base + 2, I2{});
+                if (base + 3 > ntiles) break;
+                idle(base + 3, I3{});
+                if (base + 4 > ntiles) break;
+                idle(base + 4, I4{});
+            }
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            compiler_fence();
+            return;
+        }
         {
             bf16x8 kf[NS];
             read_k(I0{}, kf);

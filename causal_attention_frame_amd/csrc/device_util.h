@@ -91,6 +91,20 @@ __device__ inline void dma16(uint64_t b0, uint32_t o0, uint32_t m0a) {
 }
 #pragma clang diagnostic pop
 
+// acc += A B with the accumulator held in AGPRs.  Files that use it are built
+// with builtin MFMAs in VGPR form (their results feed VALU code), and their
+// long-lived accumulators live in AGPRs through this statement instead, which
+// leaves the VGPRs to the rest of the kernel.  The s_nop covers a VALU write of
+// an A or B operand just before; the hardware forwards an exactly matching
+// accumulator from the previous MFMA of the same shape.  Before other code
+// touches the accumulator registers, acc_settle() waits out the last MFMA.
+__device__ inline void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last accumulating MFMA and other reads or writes
+// of its AGPRs (more than the 18 a 16-pass MFMA needs).
+__device__ inline void acc_settle() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
