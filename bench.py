@@ -154,6 +154,38 @@ def clock_mhz(dev):
     return round(rtr.rtr_clock_sample(dev), 1)
 
 
+class ClockSampler:
+    """Shader-clock samples taken while the timed steps run: every `every`-th
+    step, once that step's first launch has started, a 100-us clock probe runs
+    on a side stream (one lane of one compute unit, next to the step's
+    kernels; nothing on the timed stream waits for it)."""
+
+    def __init__(self, dev, steps, every=4):
+        import torch
+        from causal_attention_frame_amd import rtr
+        self.every = every
+        self.side = torch.cuda.Stream(dev)
+        self.buf = torch.zeros((steps // every + 1, 2), dtype=torch.int64, device=dev)
+        self.n = 0
+        self.fn = rtr.lib().rtr_clock_sample
+
+    def maybe(self, i, start_event):
+        import ctypes
+        if i % self.every != 1 % self.every or self.n >= self.buf.shape[0]:
+            return
+        self.side.wait_event(start_event)
+        self.fn(ctypes.c_void_p(self.buf[self.n].data_ptr()), 10000, ctypes.c_void_p(self.side.cuda_stream))
+        self.n += 1
+
+    def summary(self):
+        if self.n == 0:
+            return None
+        t = self.buf[:self.n].cpu().numpy().astype(np.float64)
+        mhz = 100.0 * t[:, 0] / np.maximum(t[:, 1], 1.0)
+        return {"median": round(float(np.median(mhz)), 1), "min": round(float(mhz.min()), 1),
+                "max": round(float(mhz.max()), 1), "samples": int(self.n)}
+
+
 def timing_stats(ms):
     return {"kernel_avg_us": round(float(np.mean(ms)) * 1e3, 2),
             "kernel_median_us": round(float(np.median(ms)) * 1e3, 2),
@@ -330,11 +362,13 @@ def main():
            for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     mhz_before = clock_mhz(dev)
+    clk = ClockSampler(dev, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         attention()
         ev[i][1].record(stream)
+        clk.maybe(i, ev[i][0])
         evc[i][0].record(stream)
         commit()
         evc[i][1].record(stream)
@@ -383,7 +417,7 @@ def main():
             "algorithmic_flop_per_launch": flops,
         },
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
-                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
+                    sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if append_bytes:
         cs = float(np.median(commit_ms)) * 1e-3
@@ -432,11 +466,13 @@ def backward(args, w, dev):
     mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    clk = ClockSampler(dev, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
+        clk.maybe(i, ev[i][0])
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     mhz_after = clock_mhz(dev)
@@ -470,7 +506,7 @@ def backward(args, w, dev):
             "algorithmic_flop_per_launch": flops,
         },
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
-                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
+                    sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -543,11 +579,13 @@ def stream_backward(args, w, dev):
     mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    clk = ClockSampler(dev, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
+        clk.maybe(i, ev[i][0])
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     mhz_after = clock_mhz(dev)
@@ -583,7 +621,7 @@ def stream_backward(args, w, dev):
             "algorithmic_flop_per_launch": flops,
         },
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
-                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
+                    sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -653,11 +691,13 @@ def cross(args, w, dev):
     mhz_before = clock_mhz(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    clk = ClockSampler(dev, args.steps)
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)
+        clk.maybe(i, ev[i][0])
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     mhz_after = clock_mhz(dev)
@@ -701,7 +741,7 @@ def cross(args, w, dev):
             "algorithmic_flop_per_launch": flops,
         },
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
-                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
+                    sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
         "text_reset": {"bound": "hbm", "median_us": round(reset_s * 1e6, 2),
                        "achieved": round(reset_bytes / reset_s / 1e9, 1), "unit": "GB/s",
                        "peak": PEAK_HBM_GBS, "algorithmic_bytes": reset_bytes},
@@ -789,9 +829,13 @@ def rollout(args, w, dev):
         one_rollout()
     torch.cuda.synchronize(dev)
     mhz_before = clock_mhz(dev)
+    clk = ClockSampler(dev, args.steps, every=1)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        e0 = torch.cuda.Event()
+        e0.record(stream)
         one_rollout()
+        clk.maybe(i, e0)
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
     mhz_after = clock_mhz(dev)
@@ -835,7 +879,7 @@ def rollout(args, w, dev):
             "algorithmic_flop_per_launch": round(flops_total / chunks),
         },
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
-                    prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
+                    sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
     rtr.rtr_kv_destroy(kv)
     if not args.no_cpu_baseline:
