@@ -70,3 +70,19 @@ def test_cross_bwd_wan_chunk():
     got, ref = _run(4680, 512, 12, True, seed=9)
     for name, g_, r_ in zip(("dq", "dk_text", "dv_text"), got, ref):
         assert_grad_close(host(g_), r_, name)
+
+
+@pytest.mark.parametrize("Tq,Lt,H,cap", [
+    (4680, 77, 2, None),    # ragged text: the last key block holds 77 of 256 keys
+    (1100, 300, 3, None),   # ragged rows and a second, partial text key block
+    (1200, 100, 2, 256),    # a cache larger than the condition
+])
+def test_cross_bwd_split_pieces_with_ragged_text(Tq, Lt, H, cap):
+    """The text key blocks split over the query rows (fp32 partials summed in
+    fixed order) with text lengths that end inside a key block."""
+    # the split is taken: its workspace carries the fp32 partial gradients
+    assert rtr.rtr_attn_cross_bwd_workspace_size(Tq, Lt, H) > rtr.rtr_attn_bwd_workspace_size(Tq, H)
+    print(f"Tq={Tq} Lt={Lt} H={H} cap={cap}", flush=True)
+    got, ref = _run(Tq, Lt, H, True, seed=Tq + 3 * Lt, cap=cap)
+    for name, g_, r_ in zip(("dq", "dk_text", "dv_text"), got, ref):
+        assert_grad_close(host(g_), r_, name)
