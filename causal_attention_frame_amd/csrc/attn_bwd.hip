@@ -11,7 +11,7 @@
 // of its own frame on, and a row by every key below the end of its frame.
 //
 // Kernels (head_dim 128, bf16 in and out, fp32 accumulation):
-//   attn_bwd_prep       one 32-row tile per workgroup: LSE in log2 units and D
+//   attn_bwd_prep       one 32-row tile per workgroup: -LSE / scale and -D
 //                       per row, and the tile's Q and dO transposed into the
 //                       layout the dK/dV kernel reads as MFMA A operands;
 //   attn_bwd_dkdv_d128  one workgroup per 256 keys of a head, 8 waves of 32
@@ -19,8 +19,9 @@
 //                       operand, V is staged once into LDS in the B operand's
 //                       lane order, dK^T and dV^T (128 floats per lane) live in
 //                       AGPRs, and the workgroup walks the 32-row query tiles
-//                       that see its keys, staged into a 2-stage LDS ring by
-//                       DMA one tile ahead;
+//                       that see its keys in a software pipeline (each MFMA
+//                       phase beside independent VALU work), the tiles staged
+//                       into LDS rings by DMA two tiles ahead;
 //   attn_bwd_dq_d128    one workgroup per 256 query rows (8 waves x 32): Q and
 //                       dO stay in registers, the workgroup walks the 32-key
 //                       tiles its rows see; dQ^T accumulates in registers.
@@ -60,7 +61,10 @@ struct BArgs {
     const uint16_t *q, *k, *v, *o, *dout;
     const float *lse;
     uint16_t *dq, *dk, *dv;
-    float *rows;   // [H][nqt][64]: log2-domain LSE of the tile's 32 rows, then their D
+    // [H][nqt][64]: -LSE / scale of the tile's 32 rows, then their -D.  The
+    // dK/dV kernel loads them as the initial values of the S and dP
+    // accumulators, which then hold S - LSE / scale (P = exp2(c S)) and dP - D.
+    float *rows;
     uint16_t *qt;  // [H][nqt][4096]: transposed Q tiles
     uint16_t *dot; // [H][nqt][4096]: transposed dO tiles
     int32_t T, kpf, nqt;
@@ -130,7 +134,27 @@ __device__ inline void dma16_lane(const void *src, uint32_t m0a) {
                  : "v"(src), "s"(m0a)
                  : "memory", "m0");
 }
+// The DMA form of dma16 (device_util.h) issued by lanes 0 and 1 only: exec is
+// narrowed and restored inside the statement, so that the caller's code stays
+// one basic block (a branch there lets the compiler sink VALU work across the
+// barrier that follows).
+__device__ inline void dma16_lanes01(uint64_t b0, uint32_t o0, uint32_t m0a) {
+    uint64_t saved;
+    asm volatile(
+        "s_mov_b64 %0, exec\n\ts_mov_b64 exec, 3\n\ts_mov_b32 m0, %2\n\ts_nop 4\n\t"
+        "global_load_lds_dwordx4 %1, %3\n\ts_mov_b64 exec, %0"
+        : "=&s"(saved)
+        : "v"(o0), "s"(m0a), "s"(b0)
+        : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// mfma_acc (device_util.h) without its wait states, for operands that no
+// VALU instruction wrote within the last few instructions (LDS loads, or
+// values formed a whole phase earlier).
+__device__ inline void mfma_acc_ready(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
 
 __device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -167,8 +191,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const BArgs a) {
     dsum += __shfl_xor(dsum, 4);
     float *rows = a.rows + ((long)head * a.nqt + tile) * 64;
     if (c8 == 0) {
-        rows[r] = valid ? a.lse[(long)head * a.T + qrow] * kLog2e : INFINITY;
-        rows[32 + r] = valid ? dsum : 0.f;
+        rows[r] = valid ? -a.lse[(long)head * a.T + qrow] / a.scale : -INFINITY;
+        rows[32 + r] = valid ? -dsum : 0.f;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -202,12 +226,11 @@ __global__ __launch_bounds__(256) void attn_bwd_prep(const BArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV: one workgroup per 256 keys, 8 waves of 32 keys.
 // ---------------------------------------------------------------------------
-// One LDS array: regions of NSTG stages each -- row-major Q, row-major dO,
-// transposed Q, transposed dO (8 KB per stage), the row statistics (256 B per
-// stage) -- then the workgroup's V rows (64 KB): step s of wave w at
-// RV + (8 w + s) 512 + 8 lane, one lane-linear 16-byte read.
-constexpr int kDkdvStages = 2;
-constexpr int kDkdvLds = 4 * kDkdvStages * kTile + kDkdvStages * 128 + 256 * kD;  // uint16 units
+// One LDS array: a 3-stage ring of query tiles' row-major and transposed Q
+// (16 KB per stage), a 2-stage ring of their row-major and transposed dO and
+// row statistics (16.25 KB per stage), then the workgroup's V rows (64 KB):
+// step s of wave w at RV + (8 w + s) 512 + 8 lane, one lane-linear 16-byte read.
+constexpr int kDkdvLds = 10 * kTile + 2 * 128 + 256 * kD;  // uint16 units
 
 // Key block kb of a head: the query rows' own keys (PRE false: the full form,
 // or the chunk's keys of a streaming step) or the cached prefix keys (PRE
@@ -216,10 +239,10 @@ constexpr int kDkdvLds = 4 * kDkdvStages * kTile + kDkdvStages * 128 + 256 * kD;
 template <bool PRE>
 __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a, int head, int kb, int piece,
                                                                  uint32_t lbase) {
-    constexpr int NS = 8, NT = 4, NSTG = kDkdvStages;
-    constexpr int RQ = 0, RDO = NSTG * kTile, RQT = 2 * NSTG * kTile, RDOT = 3 * NSTG * kTile;
-    constexpr int RROW = 4 * NSTG * kTile;  // in uint16 units
-    constexpr int RV = RROW + NSTG * 128;
+    constexpr int NS = 8, NT = 4;
+    constexpr int RQ = 0, RQT = 3 * kTile, RDO = 6 * kTile, RDOT = 8 * kTile;  // in uint16 units
+    constexpr int RROW = 10 * kTile;
+    constexpr int RV = RROW + 2 * 128;
     const bool pre = PRE;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -267,40 +290,42 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
     compiler_fence();
     const uint32_t pv = lbase + 2 * (RV + wave * NS * 512 + 8 * lane);
 
-    // DMA of one query tile, 5 loads per wave: row-major Q and dO (wave w
-    // fills rows 4w + lr, lane (lr, pch) the stored chunk pch), the two
-    // transposed tiles (contiguous 8 KB, wave w its 1 KB) and the row
-    // statistics (32 bytes per wave, lanes 0 and 1).
+    // DMA of query tile i into Q stage qs and dO stage ds, 5 loads per wave:
+    // row-major Q and dO (wave w fills rows 4w + lr, lane (lr, pch) the stored
+    // chunk pch), the two transposed tiles (contiguous 8 KB, wave w its 1 KB)
+    // and the row statistics (32 bytes per wave, lanes 0 and 1).
     const int lr = lane >> 4, pch = lane & 15;
     const int prow = 4 * wave + lr;
     const uint32_t plain_col = (uint32_t)(16 * (pch ^ swz_plain(prow)));
     const uint32_t l0 = lbase + 1024 * wave;
-    auto issue = [&](int i) __attribute__((always_inline)) {
-        const int st = i & (NSTG - 1);
+    auto issue = [&](int i, int qs, int ds) __attribute__((always_inline)) {
         const int tq = min(t0 + i, a.nqt - 1);
         const int row = min(tq * 32 + prow, a.T - 1);
         const uint32_t off = (uint32_t)(((long)row * a.ld + hoff) * 2) + plain_col;
-        dma16x2((uint64_t)a.q, (uint64_t)a.dout, off, off, l0 + 2 * (RQ + st * kTile), l0 + 2 * (RDO + st * kTile));
+        dma16x2((uint64_t)a.q, (uint64_t)a.dout, off, off, l0 + 2 * (RQ + qs * kTile), l0 + 2 * (RDO + ds * kTile));
         const long tb = ((long)head * a.nqt + tq) * kTile * 2 + 1024 * wave;
-        dma16x2((uint64_t)a.qt + tb, (uint64_t)a.dot + tb, 16u * lane, 16u * lane, l0 + 2 * (RQT + st * kTile),
-                l0 + 2 * (RDOT + st * kTile));
+        dma16x2((uint64_t)a.qt + tb, (uint64_t)a.dot + tb, 16u * lane, 16u * lane, l0 + 2 * (RQT + qs * kTile),
+                l0 + 2 * (RDOT + ds * kTile));
         const uint64_t rb = (uint64_t)(a.rows + ((long)head * a.nqt + tq) * 64 + 8 * wave);
-        if (lane < 2) dma16(rb, 16u * lane, lbase + 2 * (RROW + st * 128) + 32 * wave);
+        dma16_lanes01(rb, 16u * lane, lbase + 2 * (RROW + ds * 128) + 32 * wave);
     };
 
-    // Fragment addresses (bytes, stage 0; region and stage offsets are
-    // immediates or a per-step add).  Plain read of k-step s (row n, logical
-    // chunk 2s + g, stored at (2s + g) ^ (n mod 16)) at aq ^ 32 s.  Transposed
-    // read of row d = 32 t + n, k-step h (logical chunk 2h + g, stored at
+    // Fragment addresses (bytes; a stage's offset is added per step, the
+    // region's is an immediate).  Plain read of k-step s (row n, logical chunk
+    // 2s + g, stored at (2s + g) ^ (n mod 16)) at aq ^ 32 s.  Transposed read
+    // of row d = 32 t + n, k-step h (logical chunk 2h + g, stored at
     // (2h + g) ^ (n/4 mod 4)) at pt[h] + 2048 t.  Row statistics of rows
     // 8 j + 4 g .. + 3: LSE at pr + 32 j, D 128 bytes further.
     uint32_t pt[2];
     const uint32_t aq = lbase + 2 * (n * kD + 8 * (g ^ swz_plain(n)));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pt[h] = lbase + 2 * (RQT + n * 32 + 8 * ((2 * h + g) ^ ((n >> 2) & 3)));
+    for (int h = 0; h < 2; ++h) pt[h] = lbase + 2 * (n * 32 + 8 * ((2 * h + g) ^ ((n >> 2) & 3)));
     const uint32_t pr = lbase + 2 * RROW + 16 * g;
     auto rd = [](uint32_t addr, int imm) __attribute__((always_inline)) {
         return lds_b128((const lds_u16 *)(uintptr_t)addr + imm / 2);
+    };
+    auto rd4 = [](uint32_t addr, int imm) __attribute__((always_inline)) {
+        return *(const lds_f32x4 *)((const lds_u16 *)(uintptr_t)addr + imm / 2);
     };
 
     f32x16 dkt[NT], dvt[NT];
@@ -308,100 +333,176 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
     for (int t = 0; t < NT; ++t) dkt[t] = dvt[t] = f32x16{};
     const float c = a.c;
 
-    // One query tile: S = Q K^T, dP = dO V^T, P = exp2(S c - LSE2) and
-    // dS = P (dP - D) in fp32, then dV^T += dO^T P and dK^T += Q^T dS.
-    auto step = [&](int i, auto masked) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(masked)::value;
-        __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's loads of tile i landed
-        lds_barrier();                            // everyone's have; stage of tile i - 1 is free
-        issue(i + 1);                             // into that stage, one tile ahead
-        const uint32_t so = (uint32_t)((i & (NSTG - 1)) * kTile * 2);
-        const uint32_t rso = (uint32_t)((i & (NSTG - 1)) * 256);
-        f32x16 s0 = {}, d0 = {};
+    // The walk over the query tiles is software-pipelined so that the MFMAs
+    // of each phase have independent VALU or LDS work beside them (the two
+    // waves of a SIMD otherwise run the same phase at the same time, and the
+    // matrix core idles through both waves' softmax).  Iteration i, with
+    // s = S(i) - LSE / scale already computed (S = Q K^T; the accumulator
+    // starts at -LSE / scale, so P = exp2(c s)):
+    //   1. dP - D = dO(i) V^T - D; the VALU turns s into P;
+    //   2. dV^T += dO(i)^T P; the VALU forms dS = P (dP - D);
+    //   wait for this wave's DMA of tile i+1, barrier (every wave's has
+    //   landed; every wave is done with tile i's dO and with tile i-1's Q),
+    //   DMA of tile i+2 into those stages;
+    //   3. dK^T += Q(i)^T dS and s = S(i+1) - LSE / scale.
+    // Q thus takes three stages (phase 3 reads tiles i and i+1), dO two.  The
+    // last iteration's S(i+1) reads a clamped tile and is discarded.
+    f32x16 s;
+    // s = -LSE / scale of the rows whose statistics lie at bst: the start of
+    // their S accumulation.
+    auto s_init = [&](uint32_t bst) __attribute__((always_inline)) {
+        f32x4 i4[4];
 #pragma unroll
-        for (int k = 0; k < NS; ++k)
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd((aq + so) ^ (32u * k), 2 * RQ), kf[k], s0, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) i4[j] = rd4(bst, 32 * j);
 #pragma unroll
-        for (int k = 0; k < NS; ++k)
-            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd((aq + so) ^ (32u * k), 2 * RDO), rd(pv, 1024 * k), d0, 0, 0, 0);
-        // Issue order of the two products: fragment reads two (S) or four (dP)
-        // at a time, each pair of MFMAs after the reads it needs.  Left to
-        // itself the compiler read one fragment, waited and multiplied, and in
-        // the prefix-key blocks spilled a K fragment to scratch every tile.
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMAs
-        }
+            for (int e = 0; e < 4; ++e) s[4 * j + e] = i4[j][e];
+    };
+
+    // Phase 1's first loads, issued at the end of the previous phase 3: the
+    // -D rows of the tile (the dP accumulator's start) and its first two
+    // fragment pairs.
+    struct Ahead {
+        f32x4 i4[4];
+        bf16x8 fa[2], fb[2];
+    } ah;
+    // Part p (0..3) of those loads for the tile in dO stage ds.
+    auto load_ahead = [&](int p, int ds) __attribute__((always_inline)) {
+        if (p < 2) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-        const int q0 = (t0 + i) * 32 + 4 * g;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 l2 = *(const lds_f32x4 *)((const lds_u16 *)(uintptr_t)(pr + rso) + 16 * j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * j + e;
-                s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -l2[e]));
-                if (MASK) s0[r] = (q0 + 8 * j + e >= qmin) ? s0[r] : 0.f;
-            }
-        }
-        bf16x8 pb[2], sb[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            pb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(s0[8 * h], s0[8 * h + 1]), pack_bf16x2(s0[8 * h + 2], s0[8 * h + 3]),
-                                                     pack_bf16x2(s0[8 * h + 4], s0[8 * h + 5]), pack_bf16x2(s0[8 * h + 6], s0[8 * h + 7])});
-        // The accumulating MFMAs are inline assembly, which the scheduler does
-        // not look into: it would read each A fragment right before its MFMA
-        // and wait.  Four fragments are read ahead of their four MFMAs instead
-        // (the scheduling fence keeps the reads in front).
-#pragma unroll
-        for (int t2 = 0; t2 < NT; t2 += 2) {
-            bf16x8 fv[4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) fv[2 * t + h] = rd(pt[h] + so, 2 * (RDOT - RQT) + 2048 * (t2 + t));
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) mfma_acc(dvt[t2 + t], fv[2 * t + h], pb[h]);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const f32x4 dd = *(const lds_f32x4 *)((const lds_u16 *)(uintptr_t)(pr + rso) + 64 + 16 * j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d0[4 * j + e] = s0[4 * j + e] * (d0[4 * j + e] - dd[e]);
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            sb[h] = __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(d0[8 * h], d0[8 * h + 1]), pack_bf16x2(d0[8 * h + 2], d0[8 * h + 3]),
-                                                     pack_bf16x2(d0[8 * h + 4], d0[8 * h + 5]), pack_bf16x2(d0[8 * h + 6], d0[8 * h + 7])});
-#pragma unroll
-        for (int t2 = 0; t2 < NT; t2 += 2) {
-            bf16x8 fk[4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) fk[2 * t + h] = rd(pt[h] + so, 2048 * (t2 + t));
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) mfma_acc(dkt[t2 + t], fk[2 * t + h], sb[h]);
+            for (int j = 2 * p; j < 2 * p + 2; ++j) ah.i4[j] = rd4(pr + (uint32_t)(ds * 256), 128 + 32 * j);
+        } else {
+            ah.fa[p - 2] = rd((aq + (uint32_t)(ds * kTile * 2)) ^ (32u * (p - 2)), 2 * RDO);
+            ah.fb[p - 2] = rd(pv, 1024 * (p - 2));
         }
     };
 
-    issue(0);
-    int i = 0;
+    auto iter = [&](int i, int qs, int qn, int ds, auto masked) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(masked)::value;
+        const uint32_t sod = (uint32_t)(ds * kTile * 2), soq = (uint32_t)(qs * kTile * 2);
+        const uint32_t bdo = aq + sod;
+        // dO^T at btd + 2 (RDOT - RDO) + 2048 t (the region's full offset would
+        // not fit the 16-bit immediate), Q^T at btq + 2 RQT + 2048 t.
+        const uint32_t btd[2] = {pt[0] + 2 * RDO + sod, pt[1] + 2 * RDO + sod};
+        const uint32_t btq[2] = {pt[0] + soq, pt[1] + soq};
+
+        // Phase 1: dP - D = dO V^T - D (the accumulator starts at -D) under
+        // P = exp2(c s), one element pair per MFMA.
+        f32x16 dp;
+        bf16x8 pb[2];
+        {
+            bf16x8 fa[NS], fb[NS];
+            uint32_t pw[2][4];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                fa[k] = ah.fa[k];
+                fb[k] = ah.fb[k];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dp[4 * j + e] = ah.i4[j][e];
+            fa[2] = rd(bdo ^ (32u * 2), 2 * RDO);
+            fb[2] = rd(pv, 1024 * 2);
+            __builtin_amdgcn_sched_barrier(0);
+            const int q0 = (t0 + i) * 32 + 4 * g;
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], fb[k], dp, 0, 0, 0);
+                if (k + 3 < NS) {
+                    fa[k + 3] = rd(bdo ^ (32u * (k + 3)), 2 * RDO);
+                    fb[k + 3] = rd(pv, 1024 * (k + 3));
+                }
+                const int r = 2 * k, row = q0 + 8 * (r >> 2) + (r & 3);
+                float p0 = __builtin_amdgcn_exp2f(s[r] * c), p1 = __builtin_amdgcn_exp2f(s[r + 1] * c);
+                if (MASK) {
+                    p0 = row >= qmin ? p0 : 0.f;
+                    p1 = row + 1 >= qmin ? p1 : 0.f;
+                }
+                s[r] = p0;
+                s[r + 1] = p1;
+                pw[k >> 2][k & 3] = pack_bf16x2(p0, p1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) pb[h] = __builtin_bit_cast(bf16x8, u32x4{pw[h][0], pw[h][1], pw[h][2], pw[h][3]});
+        }
+
+        // Phase 2: dV^T += dO^T P under dS = P (dP - D), one element pair per
+        // MFMA; the first dK^T fragments are read at its end.
+        bf16x8 sb[2], fk[NS];
+        {
+            bf16x8 fv[NS];
+            uint32_t sw[2][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) fv[k] = rd(btd[k & 1], 2 * (RDOT - RDO) + 2048 * (k >> 1));
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                if (k < 2) mfma_acc(dvt[k >> 1], fv[k], pb[k & 1]);
+                else mfma_acc_ready(dvt[k >> 1], fv[k], pb[k & 1]);
+                if (k + 4 < NS) fv[k + 4] = rd(btd[k & 1], 2 * (RDOT - RDO) + 2048 * ((k + 4) >> 1));
+                else fk[k - 4] = rd(btq[k & 1], 2 * RQT + 2048 * ((k - 4) >> 1));
+                const int r = 2 * k;
+                sw[k >> 2][k & 3] = pack_bf16x2(s[r] * dp[r], s[r + 1] * dp[r + 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) sb[h] = __builtin_bit_cast(bf16x8, u32x4{sw[h][0], sw[h][1], sw[h][2], sw[h][3]});
+        }
+
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));  // this wave's loads of tile i+1 landed
+        lds_barrier();                            // everyone's have; tile i's dO and tile i-1's Q are free
+        issue(i + 2, qn == 2 ? 0 : qn + 1, ds);
+
+        // Phase 3: dK^T += Q^T dS and S(i+1) = Q(i+1) K^T - LSE / scale,
+        // alternating, each fragment read two MFMA pairs ahead.
+        {
+            const uint32_t bq = aq + (uint32_t)(qn * kTile * 2);
+            bf16x8 fq[NS];
+            s_init(pr + (uint32_t)((ds ^ 1) * 256));
+#pragma unroll
+            for (int k = 0; k < 3; ++k) fq[k] = rd(bq ^ (32u * k), 2 * RQ);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                mfma_acc_ready(dkt[k >> 1], fk[k], sb[k & 1]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[k], kf[k], s, 0, 0, 0);
+                if (k + 4 < NS) fk[k + 4] = rd(btq[k & 1], 2 * RQT + 2048 * ((k + 4) >> 1));
+                if (k + 3 < NS) fq[k + 3] = rd(bq ^ (32u * (k + 3)), 2 * RQ);
+                if (k >= 4) load_ahead(k - 4, ds ^ 1);  // tile i+1
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    if (nt > 0) {
+        issue(0, 0, 0);
+        issue(1, 1, 1);
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        lds_barrier();
+        s_init(pr);  // S(0)
+#pragma unroll
+        for (int k = 0; k < NS; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd(aq ^ (32u * k), 2 * RQ), kf[k], s, 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) load_ahead(p, 0);
+    }
+    int i = 0, qs = 0, ds = 0;
 #pragma unroll 1
-    for (; i < nmask; ++i) step(i, std::true_type{});
+    for (; i < nmask; ++i) {
+        const int qn = qs == 2 ? 0 : qs + 1;
+        iter(i, qs, qn, ds, std::true_type{});
+        qs = qn;
+        ds ^= 1;
+    }
 #pragma unroll 1
-    for (; i < nt; ++i) step(i, std::false_type{});
+    for (; i < nt; ++i) {
+        const int qn = qs == 2 ? 0 : qs + 1;
+        iter(i, qs, qn, ds, std::false_type{});
+        qs = qn;
+        ds ^= 1;
+    }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // no DMA outlives the workgroup's LDS
     acc_settle();  // before the AGPR reads below
 
@@ -504,8 +605,8 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     float l2 = INFINITY, dd = 0.f;
     if (qv) {
         const float *rs = a.rows + ((long)head * a.nqt + qi / 32) * 64;
-        l2 = rs[qi & 31];
-        dd = rs[32 + (qi & 31)];
+        l2 = -rs[qi & 31] * a.c;  // LSE in log2 units
+        dd = -rs[32 + (qi & 31)];
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // as in the dK/dV kernel: no load wait inside the loop
     compiler_fence();
