@@ -27,21 +27,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2,
 // and an XCD starts its workgroups in index order as compute units free up.
-// Every XCD gets one contiguous head-major range of work items (head, block)
-// so the blocks of one head (which read the same tensors) share an L2, and
-// runs that range by block index, highest first, across its heads.  Callers
-// number blocks so that the highest index carries the most work.
+// Every XCD gets one contiguous head-major range of work items, so the blocks
+// of one head (which read the same tensors) share an L2, and runs that range
+// by block index, highest first, across its heads.  Callers number blocks so
+// that the highest index carries the most work.  Within a head, work item
+// position p holds block perm(p), alternating between the heaviest and the
+// lightest remaining blocks (nblk-1, 0, nblk-2, 1, ...): an XCD whose range
+// cuts a head in two then gets about its share of that head's work, where
+// ranges of consecutive blocks gave one XCD the heavy half and its neighbour
+// the light half.
 __device__ inline void xcd_order(int b, int nwg, int nblk, int &head, int &blk) {
     const int x = b & 7, i = b >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
     const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
+    const int half = nblk >> 1;
     int rem = i;
     head = lo / nblk;
     blk = lo - head * nblk;  // not reached for a valid b
     for (int q = nblk - 1; q >= 0; --q) {
-        if (hi - 1 - q < 0) continue;
-        const int hmin = lo - q > 0 ? (lo - q + nblk - 1) / nblk : 0;
-        const int hmax = (hi - 1 - q) / nblk;
+        const int p = q >= half ? 2 * (nblk - 1 - q) : 2 * q + 1;  // position of block q
+        if (hi - 1 - p < 0) continue;
+        const int hmin = lo - p > 0 ? (lo - p + nblk - 1) / nblk : 0;
+        const int hmax = (hi - 1 - p) / nblk;
         const int cnt = hmax >= hmin ? hmax - hmin + 1 : 0;
         if (rem < cnt) {
             head = hmin + rem;
