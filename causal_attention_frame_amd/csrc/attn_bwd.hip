@@ -24,7 +24,8 @@
 //                       into LDS rings by DMA two tiles ahead;
 //   attn_bwd_dq_d128    one workgroup per 256 query rows (8 waves x 32): Q and
 //                       dO stay in registers, the workgroup walks the 32-key
-//                       tiles its rows see; dQ^T accumulates in registers.
+//                       tiles its rows see in the same kind of software
+//                       pipeline; dQ^T accumulates in registers.
 // dQ is produced apart from dK/dV, recomputing S and dP, so that no partial
 // sum leaves a workgroup: no atomics, and the result is deterministic.
 //
@@ -660,79 +661,127 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     for (int t = 0; t < NT; ++t) dqt[t] = f32x16{};
     const float c = a.c;
 
-    auto step = [&](int j, auto S, auto masked) __attribute__((always_inline)) {
-        constexpr int st = decltype(S)::value;
+    // The walk over the key tiles is software-pipelined as in the dK/dV
+    // kernel.  Iteration j (stage j mod 4), with s = S^T(j) = K(j) Q^T:
+    //   1. dP^T = V(j) dO^T; the VALU turns s into P = exp2(s c - LSE2);
+    //   wait for this wave's DMA of tile j+1, barrier (every wave's has
+    //   landed; every wave is done with tile j-1), DMA of tile j+3 into the
+    //   stage of tile j-1;
+    //   2. S^T(j+1) = K(j+1) Q^T; the VALU forms dS = P (dP - D);
+    //   3. dQ^T += K(j)^T dS^T.
+    // One element pair of the VALU work per MFMA, each fragment read two
+    // MFMAs ahead.  The last iteration's S^T(j+1) reads a clamped tile and is
+    // discarded.
+    f32x16 s;
+    auto iter = [&](int j, auto S, auto masked) __attribute__((always_inline)) {
+        constexpr int st = decltype(S)::value, st1 = (st + 1) % NSTG;
         constexpr bool MASK = decltype(masked)::value;
-        __builtin_amdgcn_s_waitcnt(wait_vm(4));
-        lds_barrier();
-        // Fragment reads four at a time ahead of their MFMAs (behind a
-        // scheduling fence): left to itself the compiler read one fragment,
-        // waited for it and multiplied, 24 times a tile.
-        f32x16 s = {}, dp = {};
+
+        // Phase 1: dP^T = V dO^T under P = exp2(s c - LSE2).
+        f32x16 dp = {};
+        {
+            bf16x8 fa[NS];
 #pragma unroll
-        for (int k2 = 0; k2 < NS; k2 += 4) {
-            bf16x8 fa[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) fa[k] = lds_b128(pk[k2 + k] + st * kTile);
+            for (int k = 0; k < 2; ++k) fa[k] = lds_b128(pv[k] + st * kTile);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], qf[k2 + k], s, 0, 0, 0);
+            for (int k = 0; k < NS; ++k) {
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], df[k], dp, 0, 0, 0);
+                if (k + 2 < NS) fa[k + 2] = lds_b128(pv[k + 2] + st * kTile);
+                const int r = 2 * k, key = j * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                float p0 = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2)), p1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], c, -l2));
+                if (MASK) {
+                    p0 = key < lim ? p0 : 0.f;
+                    p1 = key + 1 < lim ? p1 : 0.f;
+                }
+                s[r] = p0;
+                s[r + 1] = p1;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-#pragma unroll
-        for (int k2 = 0; k2 < NS; k2 += 4) {
-            bf16x8 fa[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) fa[k] = lds_b128(pv[k2 + k] + st * kTile);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], df[k2 + k], dp, 0, 0, 0);
-        }
+
+        __builtin_amdgcn_s_waitcnt(wait_vm(2));  // this wave's loads of tile j+1 landed
+        lds_barrier();                            // everyone's have; tile j-1 is free
+        issue(j + 3, std::integral_constant<int, (st + 3) % NSTG>{});
+
+        // Phase 2: S^T(j+1) = K(j+1) Q^T under dS = P (dP - D).
+        f32x16 sn = {};
         bf16x8 sb[2];
+        {
+            bf16x8 fa[NS];
+            uint32_t sw[2][4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l2));
-            if (MASK) p = (j * 32 + 8 * (r >> 2) + 4 * g + (r & 3) < lim) ? p : 0.f;
-            sb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dd));
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < NT; t2 += 2) {
-            bf16x8 kt[4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    kt[2 * t + h] = cat_tr(lds_tr16(ptr[t2 + t][0] + st * kTile + 16 * h * kD),
-                                           lds_tr16(ptr[t2 + t][1] + st * kTile + 16 * h * kD));
+            for (int k = 0; k < 2; ++k) fa[k] = lds_b128(pk[k] + st1 * kTile);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int k = 0; k < NS; ++k) {
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], qf[k], sn, 0, 0, 0);
+                if (k + 2 < NS) fa[k + 2] = lds_b128(pk[k + 2] + st1 * kTile);
+                const int r = 2 * k;
+                sw[k >> 2][k & 3] = pack_bf16x2(s[r] * (dp[r] - dd), s[r + 1] * (dp[r + 1] - dd));
+                __builtin_amdgcn_sched_barrier(0);
+            }
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    dqt[t2 + t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[2 * t + h], sb[h], dqt[t2 + t], 0, 0, 0);
+            for (int h = 0; h < 2; ++h) sb[h] = __builtin_bit_cast(bf16x8, u32x4{sw[h][0], sw[h][1], sw[h][2], sw[h][3]});
         }
-        issue(j + NSTG - 1, std::integral_constant<int, (st + NSTG - 1) % NSTG>{});
+
+        // Phase 3: dQ^T += K^T dS^T (fragment k: d block k/2, k-step k mod 2).
+        {
+            bf16x8 kt[NS];
+            auto rd_kt = [&](int k) __attribute__((always_inline)) {
+                return cat_tr(lds_tr16(ptr[k >> 1][0] + st * kTile + 16 * (k & 1) * kD),
+                              lds_tr16(ptr[k >> 1][1] + st * kTile + 16 * (k & 1) * kD));
+            };
+#pragma unroll
+            for (int k = 0; k < 2; ++k) kt[k] = rd_kt(k);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < NS; ++k) {
+                dqt[k >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[k], sb[k & 1], dqt[k >> 1], 0, 0, 0);
+                if (k + 2 < NS) kt[k + 2] = rd_kt(k + 2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        s = sn;
+        // In the masked loop, whose iterations are separated by exit tests,
+        // S^T(j+1) is formed here rather than sunk past an exit.
+        if (MASK) asm volatile("" : "+v"(s));
     };
 
     issue(0, I0{});
     issue(1, I1{});
     issue(2, I2{});
+    __builtin_amdgcn_s_waitcnt(wait_vm(4));  // tile 0 landed
+    lds_barrier();
+    {
+        s = f32x16{};
+#pragma unroll
+        for (int k2 = 0; k2 < NS; k2 += 4) {
+            bf16x8 fa[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) fa[k] = lds_b128(pk[k2 + k]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], qf[k2 + k], s, 0, 0, 0);
+        }
+    }
     int j = 0;
 #pragma unroll 1
     for (; j + 4 <= nfull; j += 4) {
-        step(j, I0{}, std::false_type{});
-        step(j + 1, I1{}, std::false_type{});
-        step(j + 2, I2{}, std::false_type{});
-        step(j + 3, I3{}, std::false_type{});
+        iter(j, I0{}, std::false_type{});
+        iter(j + 1, I1{}, std::false_type{});
+        iter(j + 2, I2{}, std::false_type{});
+        iter(j + 3, I3{}, std::false_type{});
     }
 #pragma unroll 1
     for (; j < ntiles; j += 4) {
-        step(j, I0{}, std::true_type{});
+        iter(j, I0{}, std::true_type{});
         if (j + 1 >= ntiles) break;
-        step(j + 1, I1{}, std::true_type{});
+        iter(j + 1, I1{}, std::true_type{});
         if (j + 2 >= ntiles) break;
-        step(j + 2, I2{}, std::true_type{});
+        iter(j + 2, I2{}, std::true_type{});
         if (j + 3 >= ntiles) break;
-        step(j + 3, I3{}, std::true_type{});
+        iter(j + 3, I3{}, std::true_type{});
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     compiler_fence();
