@@ -176,7 +176,7 @@ class ClockSampler:
         torch.cuda.synchronize(dev)
 
     def maybe(self, i, start_event):
-        if i % self.every != 1 % self.every or self.n >= self.buf.shape[0]:
+        if i % self.every != 0 or self.n >= self.buf.shape[0]:
             return
         self.side.wait_event(start_event)
         self.fn(self.ptrs[self.n], 10000, self.sp)
@@ -189,6 +189,50 @@ class ClockSampler:
         mhz = 100.0 * t[:, 0] / np.maximum(t[:, 1], 1.0)
         return {"median": round(float(np.median(mhz)), 1), "min": round(float(mhz.min()), 1),
                 "max": round(float(mhz.max()), 1), "samples": int(self.n)}
+
+
+# HIP events bracket every EV_EVERY-th timed step only: each record is a marker
+# on the stream that costs a few microseconds of its own, which a step of a
+# few hundred microseconds would otherwise carry on every step (measured on the
+# Wan-1.3B step: 0.418 ms per step with four records per step, 0.401 ms with
+# three records per four steps, the kernel's own time unchanged).
+EV_EVERY = 4
+
+
+class SampledEvents:
+    """Events for the timed loop: on steps i with i % EV_EVERY == 0, one
+    record before the step's first part and one after each part, so that each
+    part's device time is sampled there.  Created before the pre-warm (event
+    creation idles the GPU)."""
+
+    def __init__(self, steps, nparts):
+        import torch
+        n = (steps + EV_EVERY - 1) // EV_EVERY
+        self.ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nparts + 1)] for _ in range(n)]
+
+    def run(self, stream, steps, parts, clk):
+        """The timed steps; returns the wall time in seconds (synchronised)."""
+        import torch
+        torch.cuda.synchronize(stream.device)
+        t0 = time.perf_counter()
+        for i in range(steps):
+            if i % EV_EVERY == 0:
+                e = self.ev[i // EV_EVERY]
+                e[0].record(stream)
+                for j, part in enumerate(parts):
+                    part()
+                    e[j + 1].record(stream)
+                    if j == 0:
+                        clk.maybe(i, e[0])
+            else:
+                for part in parts:
+                    part()
+        torch.cuda.synchronize(stream.device)
+        return time.perf_counter() - t0
+
+    def ms(self, j):
+        """Device milliseconds of part j on the sampled steps."""
+        return np.array([e[j].elapsed_time(e[j + 1]) for e in self.ev])
 
 
 def timing_stats(ms):
@@ -358,31 +402,17 @@ def main():
 
     # everything that idles the GPU (event creation, the clock probes) comes
     # before the pre-warm, so that the load runs on into the timed steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    sev = SampledEvents(args.steps, 2)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
     nwarm = prewarm(whole_step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         whole_step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        attention()
-        ev[i][1].record(stream)
-        clk.maybe(i, ev[i][0])
-        evc[i][0].record(stream)
-        commit()
-        evc[i][1].record(stream)
-    torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
+    elapsed = sev.run(stream, args.steps, [attention, commit], clk)
     mhz_after = clock_mhz(dev)
 
-    attn_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    commit_ms = np.array([a.elapsed_time(b) for a, b in evc])
+    attn_ms = sev.ms(0)
+    commit_ms = sev.ms(1)
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_s = float(attn_ms.mean()) * 1e-3
@@ -464,24 +494,15 @@ def backward(args, w, dev):
     def step():
         rtr.rtr_attn_block_causal_bwd(q, k, v, o, lse, do, kpf, dq, dk, dv, workspace=ws)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-        clk.maybe(i, ev[i][0])
-    torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
+    elapsed = sev.run(stream, args.steps, [step], clk)
     mhz_after = clock_mhz(dev)
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    call_ms = sev.ms(0)
     ms_per_step = elapsed * 1e3 / args.steps
     call_s = float(call_ms.mean()) * 1e-3
     out = {
@@ -577,24 +598,15 @@ def stream_backward(args, w, dev):
     def step():
         rtr.rtr_attn_stream_step_bwd(kv, q, k, v, o, lse, do, C, 1, dq, dk, dv, dkc, dvc, workspace=ws)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-        clk.maybe(i, ev[i][0])
-    torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
+    elapsed = sev.run(stream, args.steps, [step], clk)
     mhz_after = clock_mhz(dev)
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    call_ms = sev.ms(0)
     ms_per_step = elapsed * 1e3 / args.steps
     call_s = float(call_ms.mean()) * 1e-3
     config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
@@ -689,24 +701,15 @@ def cross(args, w, dev):
         else:
             rtr.rtr_attn_cross(tc, q, o=o, workspace=ws)
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-        clk.maybe(i, ev[i][0])
-    torch.cuda.synchronize(dev)
-    elapsed = time.perf_counter() - t0
+    elapsed = sev.run(stream, args.steps, [step], clk)
     mhz_after = clock_mhz(dev)
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    call_ms = sev.ms(0)
     # text switch: re-initialise the cache with a condition of the same length
     er = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
     for a, b in er:
