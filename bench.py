@@ -310,6 +310,10 @@ def main():
     ap.add_argument("--no-cache-grads", action="store_true",
                     help="wan13b_stream_step_bwd: treat the cache as constant (no gradients of the "
                          "cached keys and values)")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="after the timed steps, time the attention kernel of this many more steps, each "
+                         "after overwriting a 512 MiB buffer (L2 and the last-level cache start cold); "
+                         "reported as cold_cache, outside value")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -413,6 +417,21 @@ def main():
 
     attn_ms = sev.ms(0)
     commit_ms = sev.ms(1)
+    cold = None
+    if args.cold > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evk = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.cold)]
+        for i in range(args.cold):
+            flush.fill_(i & 0xFF)
+            evk[i][0].record(stream)
+            attention()
+            evk[i][1].record(stream)
+            commit()
+        torch.cuda.synchronize(dev)
+        cms = np.array([a.elapsed_time(b) for a, b in evk])
+        cold = dict(timing_stats(cms), steps=args.cold, flush_bytes=512 << 20)
+        del flush
     ms_per_step = elapsed * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_avg_s = float(attn_ms.mean()) * 1e-3
@@ -454,6 +473,8 @@ def main():
         "gpu": dict(device_info(dev), sclk_mhz_before_timed=mhz_before, sclk_mhz_after_timed=mhz_after,
                     sclk_mhz_during_timed=clk.summary(), prewarm_steps=nwarm, prewarm_s=args.prewarm_s),
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     if append_bytes:
         cs = float(np.median(commit_ms)) * 1e-3
         out["kv_append"] = {"bound": "hbm", "median_us": round(cs * 1e6, 2),
