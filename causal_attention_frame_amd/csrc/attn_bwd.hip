@@ -316,7 +316,7 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
     // 2s + g, stored at (2s + g) ^ (n mod 16)) at aq ^ 32 s.  Transposed read
     // of row d = 32 t + n, k-step h (logical chunk 2h + g, stored at
     // (2h + g) ^ (n/4 mod 4)) at pt[h] + 2048 t.  Row statistics of rows
-    // 8 j + 4 g .. + 3: LSE at pr + 32 j, D 128 bytes further.
+    // 8 j + 4 g .. + 3: -LSE / scale at pr + 32 j, -D 128 bytes further.
     uint32_t pt[2];
     const uint32_t aq = lbase + 2 * (n * kD + 8 * (g ^ swz_plain(n)));
 #pragma unroll
