@@ -158,14 +158,18 @@ class ClockSampler:
     """Shader-clock samples taken while the timed steps run: every `every`-th
     step, once that step's first launch has started, a 100-us clock probe runs
     on a side stream (one lane of one compute unit, next to the step's
-    kernels; nothing on the timed stream waits for it)."""
+    kernels; nothing on the timed stream waits for it).  begin() marks the
+    step start with an event of its own on steps i % every == phase, which the
+    event-timed steps (i % EV_EVERY == 0) avoid when phase is not 0; maybe()
+    uses a start event the caller already recorded."""
 
-    def __init__(self, dev, steps, every=4):
+    def __init__(self, dev, steps, every=4, phase=0):
         import torch
         from causal_attention_frame_amd import rtr
         import ctypes
-        self.every = every
+        self.every, self.phase = every, phase
         self.side = torch.cuda.Stream(dev)
+        self.marks = [torch.cuda.Event() for _ in range(steps // every + 1)]
         self.buf = torch.zeros((steps // every + 1, 2), dtype=torch.int64, device=dev)
         self.ptrs = [ctypes.c_void_p(self.buf[i].data_ptr()) for i in range(self.buf.shape[0])]
         self.sp = ctypes.c_void_p(self.side.cuda_stream)
@@ -176,11 +180,17 @@ class ClockSampler:
         torch.cuda.synchronize(dev)
 
     def maybe(self, i, start_event):
-        if i % self.every != 0 or self.n >= self.buf.shape[0]:
+        if i % self.every != self.phase or self.n >= self.buf.shape[0]:
             return
         self.side.wait_event(start_event)
         self.fn(self.ptrs[self.n], 10000, self.sp)
         self.n += 1
+
+    def begin(self, i, stream):
+        if i % self.every != self.phase or self.n >= self.buf.shape[0]:
+            return
+        self.marks[self.n].record(stream)
+        self.maybe(i, self.marks[self.n])
 
     def summary(self):
         if self.n == 0:
@@ -222,9 +232,8 @@ class SampledEvents:
                 for j, part in enumerate(parts):
                     part()
                     e[j + 1].record(stream)
-                    if j == 0:
-                        clk.maybe(i, e[0])
             else:
+                clk.begin(i, stream)
                 for part in parts:
                     part()
         torch.cuda.synchronize(stream.device)
@@ -408,7 +417,7 @@ def main():
     # before the pre-warm, so that the load runs on into the timed steps
     sev = SampledEvents(args.steps, 2)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY, phase=EV_EVERY // 2)
     nwarm = prewarm(whole_step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         whole_step()
@@ -517,7 +526,7 @@ def backward(args, w, dev):
 
     sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY, phase=EV_EVERY // 2)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
@@ -621,7 +630,7 @@ def stream_backward(args, w, dev):
 
     sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY, phase=EV_EVERY // 2)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
@@ -724,7 +733,7 @@ def cross(args, w, dev):
 
     sev = SampledEvents(args.steps, 1)
     mhz_before = clock_mhz(dev)
-    clk = ClockSampler(dev, args.steps, every=EV_EVERY)
+    clk = ClockSampler(dev, args.steps, every=EV_EVERY, phase=EV_EVERY // 2)
     nwarm = prewarm(step, dev, args.prewarm_s)
     for _ in range(args.warmup):
         step()
