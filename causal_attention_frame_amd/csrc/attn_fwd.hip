@@ -432,24 +432,12 @@ __device__ inline void dma16_vaddr(const void *src, uint32_t m0) {
 }
 #pragma clang diagnostic pop
 
-// Segment base pointers kseg[f], kseg[f + 1], vseg[f], vseg[f + 1], read from
-// the kernel arguments by the scalar unit and waited for in the same statement.
+// Segment base pointers kseg[f], kseg[f + 1], vseg[f], vseg[f + 1].
 struct SegPtrs {
     uint64_t k0, k1, v0, v1;
 };
-__device__ inline SegPtrs load_seg_ptrs(int f) {
-    const char *ka = (const char *)__builtin_amdgcn_kernarg_segment_ptr();
-    const uint32_t ko = (uint32_t)offsetof(KArgs, kseg) + 8u * (uint32_t)f;
-    const uint32_t vo = (uint32_t)offsetof(KArgs, vseg) + 8u * (uint32_t)f;
-    u64x2 k, v;
-    asm volatile("s_load_dwordx4 %0, %2, %3\n\ts_load_dwordx4 %1, %2, %4\n\ts_waitcnt lgkmcnt(0)"
-                 : "=s"(k), "=s"(v)
-                 : "s"(ka), "s"(ko), "s"(vo)
-                 : "memory");
-    return {k[0], k[1], v[0], v[1]};
-}
-// The same four pointers as plain scalar loads, which the compiler waits for
-// where they are first used.
+// The pointers of segments f and f + 1 as plain scalar loads from the kernel
+// arguments, which the compiler waits for where they are first used.
 __device__ inline SegPtrs load_seg_ptrs_ahead(int f) {
     typedef __attribute__((address_space(4))) const uint64_t c_u64;
     typedef __attribute__((address_space(4))) const char c_char;
@@ -1072,34 +1060,44 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
     auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
 
-    // Key cursor of the next tile to prefetch (tiles are prefetched in order
-    // within a sweep): segment cf and key offset co inside it, wave-uniform.
-    // Past the last segment it wraps inside the last one, so look-ahead tiles
-    // beyond the keys still read valid (finite) rows, which the mask discards.
-    int cf = 0, co = 0;
-    SegPtrs sp{};
+    // DMA cursor of this wave's 4-row group, as in the plain kernel: the
+    // group's row drow inside segment dseg for the next tile to prefetch
+    // (wave-uniform; a group never straddles two segments), turned by
+    // prepare() into the tile's K and V addresses and moved one tile on, with
+    // the segment's base pointers loaded one tile ahead, so that no
+    // scalar-load wait sits at the barrier.  Past the last segment it wraps
+    // inside the last one, so look-ahead tiles beyond the keys still read
+    // valid (finite) rows, which the mask discards.  A segment is below 2^31
+    // bytes.
+    const int32_t ld2 = (int32_t)(a.ld * 2);
+    int32_t hoff2 = 0;
+    int drow = 0, dseg = 0;
+    uint64_t dkp = 0, dvp = 0;
+    SegPtrs nsp{};
     auto reset_cursor = [&](int tile) __attribute__((always_inline)) {
-        const int j = tile * BN;
-        cf = min(j / a.seg_len, a.nseg - 1);
-        co = j - cf * a.seg_len;
+        const int j = tile * BN + 4 * wave;
+        dseg = min(j / a.seg_len, a.nseg - 1);
+        drow = j - dseg * a.seg_len;
+        drow = drow >= a.seg_len ? drow - a.seg_len : drow;
+        hoff2 = (int32_t)(hoff * 2);
+        if constexpr (FAST) nsp = load_seg_ptrs_ahead(dseg);
     };
-    auto load_ptrs = [&]() {
-        if constexpr (FAST) sp = load_seg_ptrs(cf);
+    auto prepare = [&]() __attribute__((always_inline)) {
+        if constexpr (FAST) {
+            const uint64_t off = (uint64_t)(uint32_t)(drow * ld2 + hoff2);
+            dkp = nsp.k0 + off;
+            dvp = nsp.v0 + off;
+            drow += BN;
+            const bool cr = drow >= a.seg_len;
+            drow = cr ? drow - a.seg_len : drow;
+            dseg = cr ? min(dseg + 1, a.nseg - 1) : dseg;
+            nsp = load_seg_ptrs_ahead(dseg);
+        }
     };
     auto issue = [&](int tile, auto S) {
         constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
-            const int row = co + 4 * wave;
-            const bool nxt = row >= a.seg_len;
-            const long rr = nxt ? row - a.seg_len : row;
-            const uint64_t off = (uint64_t)((rr * a.ld + hoff) * 2);
-            dma16x2((nxt ? sp.k1 : sp.k0) + off, (nxt ? sp.v1 : sp.v0) + off, kvo[0], vvo[0], m0k(st, 0),
-                          m0v(st, 0));
-            co += BN;
-            if (co >= a.seg_len) {
-                co -= a.seg_len;
-                cf = min(cf + 1, a.nseg - 1);
-            }
+            dma16x2(dkp, dvp, kvo[0], vvo[0], m0k(st, 0), m0v(st, 0));
         } else {
             const int j0 = tile * BN;
 #pragma unroll
@@ -1231,9 +1229,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
-        load_ptrs();  // segment pointers of tile t + 3
+        prepare();  // DMA addresses of tile t + 3
+        // this wave's DMA of tile t+1 has landed (t+2 may still be in flight);
+        // after the barrier every wave's has, and every wave is done with
+        // step t-1, so the stage of tile t-2 is free
         __builtin_amdgcn_s_waitcnt(wait_vm(2));
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
@@ -1287,11 +1287,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     };
     auto sweep = [&](bool first_sweep, int tb, auto maxonly) __attribute__((always_inline)) {
         reset_cursor(tb);
-        load_ptrs();
+        prepare();
         issue(tb, I0{});
-        load_ptrs();
+        prepare();
         issue(tb + 1, I1{});
-        load_ptrs();
+        prepare();
         issue(tb + 2, I2{});
         __builtin_amdgcn_s_waitcnt(wait_vm(4));  // tile 0 landed
         compiler_fence();
