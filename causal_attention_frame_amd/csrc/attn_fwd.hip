@@ -543,8 +543,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         vvo[i] = (uint32_t)(((long)lr * a.ld + vch[i] * 8) * 2);
     }
     const uint32_t k_lds = lds_addr(kbase), v_lds = lds_addr(vbase);
-    auto m0k = [&](int S, int i) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
-    auto m0v = [&](int S, int i) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
+    auto m0k = [&](int S, int i) __attribute__((always_inline)) { return k_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
+    auto m0v = [&](int S, int i) __attribute__((always_inline)) { return v_lds + (uint32_t)((S * TILE + (4 * wave + 4 * i) * D) * 2); };
 
     // DMA cursor of this wave's 4-row group (tiles are prefetched in order
     // within a sweep; wave-uniform): the group's row drow inside segment dseg
@@ -559,12 +559,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     int drow = 0, dseg = 0;
     uint64_t dkp = 0, dvp = 0;
     SegPtrs nsp{};
-    auto reset_cursor = [&]() {
+    auto reset_cursor = [&]() __attribute__((always_inline)) {
         drow = 4 * wave;
         dseg = 0;
         if constexpr (FAST) nsp = load_seg_ptrs_ahead(0);
     };
-    auto prepare = [&]() {
+    auto prepare = [&]() __attribute__((always_inline)) {
         if constexpr (FAST) {
             const uint64_t off = (uint64_t)(uint32_t)(drow * ld2 + hoff2);
             dkp = nsp.k0 + off;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             nsp = load_seg_ptrs_ahead(dseg);
         }
     };
-    auto issue = [&](int tile, auto S) {
+    auto issue = [&](int tile, auto S) __attribute__((always_inline)) {
         constexpr int st = decltype(S)::value;
         if constexpr (FAST) {
             dma16x2(dkp, dvp, kvo[0], vvo[0], m0k(st, 0), m0v(st, 0));
@@ -629,13 +629,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
     // transposed 8-byte reads each).
-    auto read_k = [&](auto S, bf16x8 *kf) {
+    auto read_k = [&](auto S, bf16x8 *kf) __attribute__((always_inline)) {
         constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int s = 0; s < NS; ++s)
             kf[s] = __builtin_bit_cast(bf16x8, *(lds_u32x4 *)(kfp[s] + st * TILE));
     };
-    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) {
+    auto read_v = [&](auto S, v4i16 (*vf)[2][2]) __attribute__((always_inline)) {
         constexpr int st = decltype(S)::value;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -646,26 +646,26 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             }
     };
     // S^T = K Q^T: lane holds query n of each block and keys 8 (r/4) + 4 g + (r%4).
-    auto qk = [&](const bf16x8 *kf, f32x16 *s) {
+    auto qk = [&](const bf16x8 *kf, f32x16 *s) __attribute__((always_inline)) {
         s[0] = f32x16{};
 #pragma unroll
         for (int st = 0; st < NS; ++st) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[0][st], s[0], 0, 0, 0);
     };
-    auto apply_mask = [&](f32x16 *s, int tile) {
+    auto apply_mask = [&](f32x16 *s, int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 if (tile * BN + 8 * (r >> 2) + 4 * g + (r & 3) >= lim[b]) s[b][r] = -INFINITY;
     };
-    auto rowmax = [&](const f32x16 &s) {
+    auto rowmax = [&](const f32x16 &s) __attribute__((always_inline)) {
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         return pair_max(mx);
     };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr) {
+    auto softmax = [&](const f32x16 *s, bf16x8 (*pf)[2], const float *mr) __attribute__((always_inline)) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             }
     };
     // O^T += V^T P^T.
-    auto pv = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2]) {
+    auto pv = [&](v4i16 (*vf)[2][2], bf16x8 (*pf)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -707,13 +707,28 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // Masked steps: a row whose limit lies at or below the tile start takes an
     // infinite exponent reference (P = 0); the element-wise mask runs only when
     // some row's limit falls inside the tile, at most a few tiles per block.
-    f32x16 scur[NB];
-    bf16x8 pprev[NB][2];
+    //
+    // S and P live in two register sets each.  In the unmasked loop the steps
+    // alternate them (parity PAR reads set PAR and writes set PAR ^ 1), so that
+    // no step ends with a copy of the next tile's S and P into the current
+    // ones, in groups of ten steps (five stages x two parities); the masked
+    // tail (PAR 2) keeps set 0 current and copies, in groups of five, because
+    // its exit tests after every step would keep both sets live.
+    f32x16 sbuf[2][NB];
+    bf16x8 pbuf[2][NB][2];
     v4i16 vcur[NT][2][2];  // V^T fragments of the tile whose PV runs next
-    auto step = [&](int t, auto S, auto masked, auto maxonly) {
+    auto step = [&](int t, auto S, auto masked, auto maxonly, auto par) __attribute__((always_inline)) {
         constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
+        constexpr int PAR = decltype(par)::value;
+        constexpr bool COPY = PAR == 2;
+        f32x16 stmp[NB];
+        bf16x8 ptmp[NB][2];
+        f32x16 *const scur = sbuf[COPY ? 0 : PAR];
+        f32x16 *const snext = COPY ? stmp : sbuf[PAR ^ 1];
+        bf16x8 (*const pprev)[2] = pbuf[COPY ? 0 : PAR];
+        bf16x8 (*const pf)[2] = COPY ? ptmp : pbuf[PAR ^ 1];
         prepare();  // DMA addresses of tile t + 3
         // this wave's DMA of tile t+1 has landed (t+2 may still be in flight);
         // after the barrier every wave's has, and every wave is done with
@@ -746,14 +761,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         bf16x8 kf[NS];
         read_k(std::integral_constant<int, (s0 + 1) % NSTG>{}, kf);
         __builtin_amdgcn_sched_barrier(0);  // the K reads go first
-        f32x16 snext[NB];
         if (MAXONLY) {
             qk(kf, snext);
 #pragma unroll
             for (int b = 0; b < NB; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
             issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
         } else {
-            bf16x8 pf[NB][2];
             pv(vcur, pprev);
             read_v(std::integral_constant<int, s0>{}, vcur);
             softmax(scur, pf, mr);
@@ -770,14 +783,16 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
+            if (COPY) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) pprev[b][h] = pf[b][h];
+                    for (int h = 0; h < 2; ++h) pbuf[0][b][h] = ptmp[b][h];
+            }
         }
-        scur[0] = snext[0];
+        if (COPY) sbuf[0][0] = stmp[0];
     };
-    auto sweep = [&](bool first_sweep, auto maxonly) {
+    auto sweep = [&](bool first_sweep, auto maxonly) __attribute__((always_inline)) {
         reset_cursor();
         prepare();
         issue(0, I0{});
@@ -792,7 +807,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         if (lim_wave == 0) {
             // A wave without valid rows only loads its share of the tiles and
             // meets the barriers of the steps.
-            auto idle = [&](int t, auto S) {
+            auto idle = [&](int t, auto S) __attribute__((always_inline)) {
                 constexpr int s0 = decltype(S)::value;
                 prepare();
                 __builtin_amdgcn_s_waitcnt(wait_vm(2));
@@ -820,44 +835,63 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         {
             bf16x8 kf[NS];
             read_k(I0{}, kf);
-            qk(kf, scur);
+            qk(kf, sbuf[0]);
         }
         if (first_sweep) {
-            if (0 >= nfull) apply_mask(scur, 0);
+            if (0 >= nfull) apply_mask(sbuf[0], 0);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) mref[b] = rowmax(scur[b]) * c;
+            for (int b = 0; b < NB; ++b) mref[b] = rowmax(sbuf[0][b]) * c;
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) pprev[b][h] = bf16x8{};
+            for (int h = 0; h < 2; ++h) pbuf[0][b][h] = bf16x8{};
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int ss = 0; ss < 2; ++ss) vcur[tt][ss][0] = vcur[tt][ss][1] = v4i16{0, 0, 0, 0};
-        // Groups of five steps (static stages): unmasked while the whole group
-        // is visible to every row, masked from there on, up to the step after
-        // the last tile (which only adds the last PV).
+        // Groups of ten steps (static stages and parities): unmasked while the
+        // whole group is visible to every row, masked from there on, up to the
+        // step after the last tile (which only adds the last PV).
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using PC = std::integral_constant<int, 2>;
         int base = 0;
+        if constexpr (FAST) {
 #pragma unroll 1
-        for (; base + 5 <= nfull; base += 5) {
-            step(base, I0{}, std::false_type{}, maxonly);
-            step(base + 1, I1{}, std::false_type{}, maxonly);
-            step(base + 2, I2{}, std::false_type{}, maxonly);
-            step(base + 3, I3{}, std::false_type{}, maxonly);
-            step(base + 4, I4{}, std::false_type{}, maxonly);
+            for (; base + 10 <= nfull; base += 10) {
+                step(base, I0{}, std::false_type{}, maxonly, P0{});
+                step(base + 1, I1{}, std::false_type{}, maxonly, P1{});
+                step(base + 2, I2{}, std::false_type{}, maxonly, P0{});
+                step(base + 3, I3{}, std::false_type{}, maxonly, P1{});
+                step(base + 4, I4{}, std::false_type{}, maxonly, P0{});
+                step(base + 5, I0{}, std::false_type{}, maxonly, P1{});
+                step(base + 6, I1{}, std::false_type{}, maxonly, P0{});
+                step(base + 7, I2{}, std::false_type{}, maxonly, P1{});
+                step(base + 8, I3{}, std::false_type{}, maxonly, P0{});
+                step(base + 9, I4{}, std::false_type{}, maxonly, P1{});
+            }
+        } else {  // per-lane addressing: its extra registers leave no room for two sets
+#pragma unroll 1
+            for (; base + 5 <= nfull; base += 5) {
+                step(base, I0{}, std::false_type{}, maxonly, PC{});
+                step(base + 1, I1{}, std::false_type{}, maxonly, PC{});
+                step(base + 2, I2{}, std::false_type{}, maxonly, PC{});
+                step(base + 3, I3{}, std::false_type{}, maxonly, PC{});
+                step(base + 4, I4{}, std::false_type{}, maxonly, PC{});
+            }
         }
 #pragma unroll 1
         for (; base <= ntiles; base += 5) {
-            step(base, I0{}, std::true_type{}, maxonly);
+            step(base, I0{}, std::true_type{}, maxonly, PC{});
             if (base + 1 > ntiles) break;
-            step(base + 1, I1{}, std::true_type{}, maxonly);
+            step(base + 1, I1{}, std::true_type{}, maxonly, PC{});
             if (base + 2 > ntiles) break;
-            step(base + 2, I2{}, std::true_type{}, maxonly);
+            step(base + 2, I2{}, std::true_type{}, maxonly, PC{});
             if (base + 3 > ntiles) break;
-            step(base + 3, I3{}, std::true_type{}, maxonly);
+            step(base + 3, I3{}, std::true_type{}, maxonly, PC{});
             if (base + 4 > ntiles) break;
-            step(base + 4, I4{}, std::true_type{}, maxonly);
+            step(base + 4, I4{}, std::true_type{}, maxonly, PC{});
         }
         // drain the look-ahead tiles before the stages are reused
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
