@@ -1256,13 +1256,23 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     // Masked steps: a row whose limit lies at or below the tile start takes an
     // infinite exponent reference (P = 0); the element-wise mask runs only when
     // some row's limit falls inside the tile, at most a few tiles per block.
-    f32x16 scur[NB];
-    bf16x8 pprev[NB][2];
+    // S and P in two register sets each, alternated by the unmasked steps as
+    // in the plain kernel (PAR 2: the masked tail keeps set 0 and copies).
+    f32x16 sbuf[2][NB];
+    bf16x8 pbuf[2][NB][2];
     v4i16 vcur[NT][2][2];  // V^T fragments of the tile whose PV runs next
-    auto step = [&](int t, auto S, auto masked, auto maxonly) {
+    auto step = [&](int t, auto S, auto masked, auto maxonly, auto par) __attribute__((always_inline)) {
         constexpr int s0 = decltype(S)::value;
         constexpr bool MASK = decltype(masked)::value;
         constexpr bool MAXONLY = decltype(maxonly)::value;
+        constexpr int PAR = decltype(par)::value;
+        constexpr bool COPY = PAR == 2;
+        f32x16 stmp[NB];
+        bf16x8 ptmp[NB][2];
+        f32x16 *const scur = sbuf[COPY ? 0 : PAR];
+        f32x16 *const snext = COPY ? stmp : sbuf[PAR ^ 1];
+        bf16x8 (*const pprev)[2] = pbuf[COPY ? 0 : PAR];
+        bf16x8 (*const pf)[2] = COPY ? ptmp : pbuf[PAR ^ 1];
         prepare();  // DMA addresses of tile t + 3
         // this wave's DMA of tile t+1 has landed (t+2 may still be in flight);
         // after the barrier every wave's has, and every wave is done with
@@ -1288,14 +1298,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         bf16x8 kf[NS];
         read_k(std::integral_constant<int, (s0 + 1) % NSTG>{}, kf);
         __builtin_amdgcn_sched_barrier(0);  // the K reads go first
-        f32x16 snext[NB];
         if (MAXONLY) {
             qk(kf, snext);
 #pragma unroll
             for (int b = 0; b < NB; ++b) mmax[b] = fmaxf(mmax[b], rowmax(scur[b]));
             issue(t + 3, std::integral_constant<int, (s0 + 3) % NSTG>{});
         } else {
-            bf16x8 pf[NB][2];
             pv(vcur, pprev);
             read_v(std::integral_constant<int, s0>{}, vcur);
             softmax(scur, pf, mr);
@@ -1312,12 +1320,14 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
+            if (COPY) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int h = 0; h < 2; ++h) pprev[b][h] = pf[b][h];
+                    for (int h = 0; h < 2; ++h) pbuf[0][b][h] = ptmp[b][h];
+            }
         }
-        scur[0] = snext[0];
+        if (COPY) sbuf[0][0] = stmp[0];
     };
     auto sweep = [&](bool first_sweep, int tb, auto maxonly) __attribute__((always_inline)) {
         reset_cursor(tb);
@@ -1334,20 +1344,20 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         {
             bf16x8 kf[NS];
             read_k(I0{}, kf);
-            qk(kf, scur);
+            qk(kf, sbuf[0]);
         }
         if (first_sweep) {
-            if (tb >= nfull) apply_mask(scur, tb);
+            if (tb >= nfull) apply_mask(sbuf[0], tb);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const float m = rowmax(scur[b]);
+                const float m = rowmax(sbuf[0][b]);
                 mref[b] = m == -INFINITY ? 0.f : m * c;  // no key of the piece: P = 0 throughout
             }
         }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int h = 0; h < 2; ++h) pprev[b][h] = bf16x8{};
+            for (int h = 0; h < 2; ++h) pbuf[0][b][h] = bf16x8{};
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
@@ -1355,26 +1365,45 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         // Groups of five steps (static stages): unmasked while the whole group
         // is visible to every row, masked from there on, up to the step after
         // the last tile (which only adds the last PV).
+        using P0 = std::integral_constant<int, 0>;
+        using P1 = std::integral_constant<int, 1>;
+        using PC = std::integral_constant<int, 2>;
         int base = tb;
+        if constexpr (FAST) {
 #pragma unroll 1
-        for (; base + 5 <= nfull; base += 5) {
-            step(base, I0{}, std::false_type{}, maxonly);
-            step(base + 1, I1{}, std::false_type{}, maxonly);
-            step(base + 2, I2{}, std::false_type{}, maxonly);
-            step(base + 3, I3{}, std::false_type{}, maxonly);
-            step(base + 4, I4{}, std::false_type{}, maxonly);
+            for (; base + 10 <= nfull; base += 10) {
+                step(base, I0{}, std::false_type{}, maxonly, P0{});
+                step(base + 1, I1{}, std::false_type{}, maxonly, P1{});
+                step(base + 2, I2{}, std::false_type{}, maxonly, P0{});
+                step(base + 3, I3{}, std::false_type{}, maxonly, P1{});
+                step(base + 4, I4{}, std::false_type{}, maxonly, P0{});
+                step(base + 5, I0{}, std::false_type{}, maxonly, P1{});
+                step(base + 6, I1{}, std::false_type{}, maxonly, P0{});
+                step(base + 7, I2{}, std::false_type{}, maxonly, P1{});
+                step(base + 8, I3{}, std::false_type{}, maxonly, P0{});
+                step(base + 9, I4{}, std::false_type{}, maxonly, P1{});
+            }
+        } else {
+#pragma unroll 1
+            for (; base + 5 <= nfull; base += 5) {
+                step(base, I0{}, std::false_type{}, maxonly, PC{});
+                step(base + 1, I1{}, std::false_type{}, maxonly, PC{});
+                step(base + 2, I2{}, std::false_type{}, maxonly, PC{});
+                step(base + 3, I3{}, std::false_type{}, maxonly, PC{});
+                step(base + 4, I4{}, std::false_type{}, maxonly, PC{});
+            }
         }
 #pragma unroll 1
         for (; base <= ntiles; base += 5) {
-            step(base, I0{}, std::true_type{}, maxonly);
+            step(base, I0{}, std::true_type{}, maxonly, PC{});
             if (base + 1 > ntiles) break;
-            step(base + 1, I1{}, std::true_type{}, maxonly);
+            step(base + 1, I1{}, std::true_type{}, maxonly, PC{});
             if (base + 2 > ntiles) break;
-            step(base + 2, I2{}, std::true_type{}, maxonly);
+            step(base + 2, I2{}, std::true_type{}, maxonly, PC{});
             if (base + 3 > ntiles) break;
-            step(base + 3, I3{}, std::true_type{}, maxonly);
+            step(base + 3, I3{}, std::true_type{}, maxonly, PC{});
             if (base + 4 > ntiles) break;
-            step(base + 4, I4{}, std::true_type{}, maxonly);
+            step(base + 4, I4{}, std::true_type{}, maxonly, PC{});
         }
         // drain the look-ahead tiles before the stages are reused
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
