@@ -542,7 +542,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 4 * j + lr;
-            dma16(qbase, (uint32_t)(((long)min(r, rmax) * a.ld + ((pch ^ (r & 15)) << 3)) * 2),
+            dma16(qbase, (uint32_t)(min(r, rmax) * ld2 + ((pch ^ (r & 15)) << 4)),
                   lds_addr(qw) + (uint32_t)(j * 4 * D * 2));
         }
     }
@@ -1074,6 +1074,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     // per-lane base plus an immediate offset below 64 KB.
     __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * TILE];
     __shared__ __attribute__((aligned(16))) uint16_t sV[NSTG * TILE];
+    // Each wave's 32 query rows on their way in (Q) and out (bf16 O).
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[BM * D];
     __shared__ const uint16_t *sSegK[FAST ? 1 : kMaxKeyFrames];
     __shared__ const uint16_t *sSegV[FAST ? 1 : kMaxKeyFrames];
     __shared__ int sRedo;
@@ -1112,6 +1114,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     // the physical 16-byte chunk pch, fetching the logical chunk that the
     // swizzle puts there.
     const int lr = lane >> 4, pch = lane & 15;
+    lds_u16 *const qw = (lds_u16 *)sQ + wave * 32 * D;  // this wave's rows of sQ
+    int qrow0 = 0;                                      // the piece's first row of this wave
     int kch[1], vch[1];
     uint32_t kvo[1], vvo[1];  // per-lane byte offsets from the group's first row
 #pragma unroll
@@ -1372,6 +1376,13 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         compiler_fence();
         __builtin_amdgcn_s_barrier();
         compiler_fence();
+        if (first_sweep) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const bf16x8 v = lds_b128(qw + n * D + (((2 * s + g) ^ (n & 15)) << 3));
+                qf[0][s] = qv[0] ? v : bf16x8{};
+            }
+        }
         {
             bf16x8 kf[NS];
             read_k(I0{}, kf);
@@ -1457,22 +1468,32 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
         ntiles = te;
         nfull = min(te, min(key_limit(q0, a), lim_end) / BN);  // tiles visible to every row
         if (tid == 0) sRedo = 0;
-        // Q^T B operands: lane (n, g) holds q[qi][16 s + 8 g .. + 7].
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const uint16_t *qrow = (const uint16_t *)a.q + (long)(qv[b] ? qi[b] : a.Tq - 1) * a.ld + hoff;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const u32x4 raw = qv[b] ? gload16(qrow + 16 * s + 8 * g) : u32x4{0, 0, 0, 0};
-                qf[b][s] = __builtin_bit_cast(bf16x8, raw);
-            }
-        }
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             l[b] = 0.f;
             mmax[b] = -INFINITY;
         }
         __syncthreads();
+        // Q^T B operands: lane (n, g) holds q[qi][16 s + 8 g .. + 7]; the rows
+        // go through the wave's part of sQ as in the plain kernel (DMA of whole
+        // rows, fragments read back in the first sweep once tile 0 has landed).
+        qrow0 = q0 + 32 * wave;
+        if (qrow0 < a.Tq) {
+            const uint64_t qp = (uint64_t)((const uint16_t *)a.q + (long)qrow0 * a.ld + hoff);
+            const uint64_t qbase = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qp) |
+                                   ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(qp >> 32)) << 32);
+            const int rmax = min(32, a.Tq - qrow0) - 1;
+            // opaque copies: keeps the compiler from hoisting the eight lane
+            // offsets out of the piece loop (they would be spilled)
+            int lrp = lr, pchp = pch;
+            asm volatile("" : "+v"(lrp), "+v"(pchp));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 4 * j + lrp;
+                dma16(qbase, (uint32_t)(min(r, rmax) * ld2 + ((pchp ^ (r & 15)) << 4)),
+                      lds_addr(qw) + (uint32_t)(j * 4 * D * 2));
+            }
+        }
     #pragma unroll
         for (int b = 0; b < NB; ++b)
     #pragma unroll
@@ -1520,25 +1541,40 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
                 continue;
             }
             const float inv = 1.f / lt;
-            const long obase = (long)qi[b] * a.ld + hoff;
+            if (a.out_f32) {
+                const long obase = (long)qi[b] * a.ld + hoff;
+    #pragma unroll
+                for (int t = 0; t < NT; ++t)
+    #pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *(f32x4 *)((float *)a.o + obase + 32 * t + 8 * i + 4 * g) =
+                            f32x4{acc[b][t][4 * i] * inv, acc[b][t][4 * i + 1] * inv,
+                                  acc[b][t][4 * i + 2] * inv, acc[b][t][4 * i + 3] * inv};
+            }
+            if (g == 0 && a.lse) a.lse[(long)head * a.Tq + qi[b]] = mref[b] / kLog2e + logf(lt);
+        }
+        if (slot < 0 && !a.out_f32 && qrow0 < a.Tq) {
+            // bf16 O of a whole unit through the wave's part of sQ, stored as
+            // whole rows (as in the plain kernel)
+            const float inv = 1.f / pair_sum(l[0]);
+            int np = n, gp = g, lrp = lr, pchp = pch;  // opaque, as for the Q DMA
+            asm volatile("" : "+v"(np), "+v"(gp), "+v"(lrp), "+v"(pchp));
     #pragma unroll
             for (int t = 0; t < NT; ++t)
     #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dcol = 32 * t + 8 * i + 4 * g;
-                    const float o0 = acc[b][t][4 * i + 0] * inv, o1 = acc[b][t][4 * i + 1] * inv;
-                    const float o2 = acc[b][t][4 * i + 2] * inv, o3 = acc[b][t][4 * i + 3] * inv;
-                    if (a.out_f32) {
-                        *(f32x4 *)((float *)a.o + obase + dcol) = f32x4{o0, o1, o2, o3};
-                    } else {
-                        const uint32_t b0 = __builtin_bit_cast(uint16_t, (__bf16)o0);
-                        const uint32_t b1 = __builtin_bit_cast(uint16_t, (__bf16)o1);
-                        const uint32_t b2 = __builtin_bit_cast(uint16_t, (__bf16)o2);
-                        const uint32_t b3 = __builtin_bit_cast(uint16_t, (__bf16)o3);
-                        *(u32x2 *)((uint16_t *)a.o + obase + dcol) = u32x2{b0 | (b1 << 16), b2 | (b3 << 16)};
-                    }
-                }
-            if (g == 0 && a.lse) a.lse[(long)head * a.Tq + qi[b]] = mref[b] / kLog2e + logf(lt);
+                for (int i = 0; i < 4; ++i)
+                    *(__attribute__((address_space(3))) u32x2 *)(qw + np * D + (((4 * t + i) ^ (np & 15)) << 3) + 4 * gp) =
+                        u32x2{pack_bf16x2(acc[0][t][4 * i] * inv, acc[0][t][4 * i + 1] * inv),
+                              pack_bf16x2(acc[0][t][4 * i + 2] * inv, acc[0][t][4 * i + 3] * inv)};
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            compiler_fence();
+    #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 4 * j + lrp;
+                const u32x4 v = *(lds_u32x4 *)(qw + r * D + (pchp << 3));
+                if (qrow0 + r < a.Tq)
+                    *(u32x4 *)((uint16_t *)a.o + (long)(qrow0 + r) * a.ld + hoff + ((pchp ^ (r & 15)) << 3)) = v;
+            }
         }
         // Every wave is done with the stages and sRedo before the next piece.
         __syncthreads();
