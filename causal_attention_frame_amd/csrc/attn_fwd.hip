@@ -502,7 +502,6 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         qv[b] = qi[b] < a.Tq;
         lim[b] = key_limit(qv[b] ? qi[b] : a.Tq - 1, a);
     }
-    const int lim_wg_lo = key_limit(q0, a);
     const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
     // Key limit of this wave's last valid row (limits grow with the row), 0
     // for a wave without valid rows: steps past it skip the wave's MFMAs and
@@ -636,8 +635,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     float mref[NB] = {0.f}, l[NB] = {0.f}, mmax[NB] = {-INFINITY};
     const float c = a.c;
 
+    // Every wave takes the block's ntiles + 1 steps (one barrier each); a wave
+    // runs the unmasked steps up to its own first row's limit, so that a block
+    // whose rows span two frames keeps the masked steps to the wave whose rows
+    // do.
     const int ntiles = (lim_wg + BN - 1) / BN;
-    const int nfull = min(ntiles, lim_wg_lo / BN);  // tiles visible to every row here
+    const int nfull = lim_wave > 0 ? min(ntiles, key_limit(q0 + 32 * NB * wave, a) / BN) : 0;
 
     // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
