@@ -69,6 +69,13 @@ struct KArgs {
     int32_t nspare;
     int32_t tail_total;
     int32_t piece;
+    // Row groups of the plain head_dim-128 kernel: pair = 1 pairs light and
+    // heavy 32-row groups in each block (the kernel's PAIR instance; else
+    // blocks of 256 consecutive rows); wpf > 0 aligns the groups to frames,
+    // wpf groups per frame.
+    int32_t pair;
+    int32_t wpf;
+    int32_t nwr;  // row groups per head
 };
 
 __device__ inline int key_limit(int i, const KArgs &a) {
@@ -456,7 +463,7 @@ enum DmaMode : int {
     kDmaLane = 1,  // anything else: per-lane segment lookup, zero rows past the end
 };
 
-template <int MODE>
+template <int MODE, bool PAIR>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
     constexpr int NB = 1;  // 32-row query blocks per wave (8 waves)
@@ -489,25 +496,71 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
 
     int head, qb;
     xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
-    const int q0 = qb * BM;
     const long hoff = (long)head * D;
     // byte strides of the DMA addressing (a segment is below 2^31 bytes)
     const int32_t ld2 = (int32_t)(a.ld * 2), hoff2 = (int32_t)(hoff * 2);
+
+    // Rows.  A head's rows form nwr groups of up to 32 rows: 32 consecutive
+    // rows each, or, with wpf > 0, wpf groups per frame that end with the
+    // frame (a group then never holds rows of two frames, whose key limits
+    // differ).  Blocks of 256 consecutive rows (!PAIR) take groups
+    // 8 qb .. 8 qb + 7.  With PAIR, groups [0, nlight) form the light half
+    // (fewer visible keys) and the rest the heavy half; block qb's waves 0-3
+    // take light groups 4 qb .. 4 qb + 3 and waves 4-7 the heavy groups
+    // nwr - 1 - 4 qb .. nwr - 4 - 4 qb.  Waves w and w + 4 of a workgroup share
+    // a SIMD, so every SIMD then holds one early and one late group and every
+    // block about the same work: for a launch of one round, where blocks of
+    // consecutive rows leave the compute units of the early frames idle while
+    // the last frame's blocks finish.  The host picks the mapping.  A group
+    // outside its half, or past the rows, has no rows here.
+    const int nwr = a.nwr, nlight = (nwr + 1) >> 1;
+    auto group_of = [&](int w) __attribute__((always_inline)) {
+        return !PAIR ? 8 * qb + w : w < 4 ? 4 * qb + w : nwr - 1 - (4 * qb + w - 4);
+    };
+    auto group_ok = [&](int w, int r) __attribute__((always_inline)) {
+        return !PAIR ? r < nwr : w < 4 ? r < nlight : r >= nlight;
+    };
+    // first row and row count of group r
+    auto group_rows = [&](int r, int &r0, int &nr) __attribute__((always_inline)) {
+        if (PAIR && a.wpf > 0) {
+            const int f = r / a.wpf, j = r - f * a.wpf;
+            r0 = f * a.kpf + 32 * j;
+            nr = min(min(32, a.kpf - 32 * j), a.Tq - r0);
+        } else {
+            r0 = 32 * r;
+            nr = min(32, a.Tq - r0);
+        }
+    };
+    const int grp = group_of(wave);
+    int qrow0 = 0, nrows = 0;  // this wave's first row and row count
+    if (group_ok(wave, grp)) group_rows(grp, qrow0, nrows);
+    const bool wvalid = nrows > 0;
 
     int qi[NB], lim[NB];
     bool qv[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        qi[b] = q0 + 32 * NB * wave + 32 * b + n;
-        qv[b] = qi[b] < a.Tq;
+        qi[b] = qrow0 + 32 * b + n;
+        qv[b] = 32 * b + n < nrows;
         lim[b] = key_limit(qv[b] ? qi[b] : a.Tq - 1, a);
     }
-    const int lim_wg = key_limit(min(q0 + BM - 1, a.Tq - 1), a);
     // Key limit of this wave's last valid row (limits grow with the row), 0
     // for a wave without valid rows: steps past it skip the wave's MFMAs and
     // softmax (it still loads its share of the tiles and meets the barriers).
-    const int r_last = q0 + 32 * NB * wave + 32 * NB - 1;
-    const int lim_wave = q0 + 32 * NB * wave < a.Tq ? key_limit(min(r_last, a.Tq - 1), a) : 0;
+    const int lim_wave = wvalid ? key_limit(qrow0 + nrows - 1, a) : 0;
+    // The block's largest limit sets the steps every wave takes: that of its
+    // last row, in its highest group (limits grow with the row; a block
+    // always has a valid light group).  A highest group past the rows gives
+    // the limit of row Tq - 1, which can only add steps that every wave skips.
+    int lim_wg;
+    if (!PAIR) {
+        lim_wg = key_limit(min(BM * qb + BM - 1, a.Tq - 1), a);
+    } else {
+        const int hr = nwr - 1 - 4 * qb;
+        int r0 = 0, nr = 0;
+        group_rows(hr >= nlight ? hr : min(4 * qb + 3, nlight - 1), r0, nr);
+        lim_wg = key_limit(nr > 0 ? r0 + nr - 1 : a.Tq - 1, a);
+    }
 
     if (!FAST) {
         for (int f = tid; f < a.nseg; f += 512) {
@@ -531,13 +584,12 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // bytes.  They land before key tile 0 (older DMAs); the first sweep reads
     // the fragments back.  Rows past Tq read the last row and are zeroed.
     bf16x8 qf[NB][NS];
-    const int qrow0 = q0 + 32 * wave;
     lds_u16 *const qw = (lds_u16 *)sQ + wave * 32 * D;
-    if (qrow0 < a.Tq) {
+    if (wvalid) {
         const uint64_t qp = (uint64_t)((const uint16_t *)a.q + (long)qrow0 * a.ld + hoff);
         const uint64_t qbase = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)qp) |
                                ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(qp >> 32)) << 32);
-        const int rmax = min(32, a.Tq - qrow0) - 1;
+        const int rmax = nrows - 1;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 4 * j + lr;
@@ -640,7 +692,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // whose rows span two frames keeps the masked steps to the wave whose rows
     // do.
     const int ntiles = (lim_wg + BN - 1) / BN;
-    const int nfull = lim_wave > 0 ? min(ntiles, key_limit(q0 + 32 * NB * wave, a) / BN) : 0;
+    const int nfull = lim_wave > 0 ? min(ntiles, key_limit(qrow0, a) / BN) : 0;
 
     // Fragment reads of one tile: K (A operand of S^T = K Q^T, 8 k-steps over d)
     // and V^T (A operand of O^T += V^T P^T, 4 column blocks x 2 key steps, two
@@ -961,7 +1013,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
                         f32x4{acc[0][t][4 * i] * inv, acc[0][t][4 * i + 1] * inv, acc[0][t][4 * i + 2] * inv,
                               acc[0][t][4 * i + 3] * inv};
         }
-    } else if (qrow0 < a.Tq) {
+    } else if (wvalid) {
         // bf16 O through the wave's part of sQ (its Q fragments were read in
         // the first sweep): written in the accumulator layout (row n, columns
         // 32 t + 8 i + 4 g .. + 3, chunks swizzled as for Q), then read back
@@ -979,7 +1031,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         for (int j = 0; j < 8; ++j) {
             const int r = 4 * j + lr;
             const u32x4 v = *(lds_u32x4 *)(qw + r * D + (pch << 3));
-            if (qrow0 + r < a.Tq)
+            if (r < nrows)
                 *(u32x4 *)((uint16_t *)a.o + (long)(qrow0 + r) * a.ld + hoff + ((pch ^ (r & 15)) << 3)) = v;
         }
     }
@@ -1869,6 +1921,70 @@ hipError_t cu_count(int *out) {
     return hipSuccess;
 }
 
+// Row mapping of the plain head_dim-128 launch (KArgs pair, wpf; sets nqb
+// and nwg).  Blocks of 256 consecutive rows, unless the launch fits in one
+// round on the compute units and pairing light with heavy 32-row groups
+// shortens the busiest SIMD by 3 % or more.  A SIMD holds waves w and w + 4
+// of a block; its cost in steps is estimated as min(a, b) + 0.62 |a - b| for
+// groups of a and b key tiles (a step in which only one of its waves works
+// takes 0.62 of a step with both, as measured on the Wan-1.3B step).  Paired
+// groups follow the frames when that pads the rows by at most 1/64.
+void plan_rows(KArgs &k, int64_t H, int cus) {
+    const int64_t Tq = k.Tq, kpf = k.kpf;
+    auto tiles_to = [&](int64_t row) {  // key tiles of the row's limit
+        const int64_t lim = std::min<int64_t>(k.prefix + (row / kpf + 1) * kpf, k.Tk);
+        return (lim + 31) / 32;
+    };
+    auto simd_cost = [](int64_t x, int64_t y) {
+        return (double)std::min(x, y) + 0.62 * (double)(x > y ? x - y : y - x);
+    };
+    k.pair = 0;
+    k.wpf = 0;
+    k.nwr = (int32_t)((Tq + 31) / 32);
+    k.nqb = (int)((Tq + 255) / 256);
+    k.nwg = (int)(k.nqb * H);
+    if ((int64_t)k.nqb * H > cus) return;  // several rounds: the dispatcher balances them
+    const int64_t wpf = (kpf + 31) / 32;
+    const bool aligned = kpf < Tq && (wpf * 32 - kpf) * 64 <= kpf;
+    const int64_t nwr = aligned ? (Tq + kpf - 1) / kpf * wpf : (Tq + 31) / 32;
+    const int64_t nlight = (nwr + 1) / 2, nqb = (nlight + 3) / 4;
+    if (nqb * H > cus) return;
+    auto group_tiles = [&](int64_t r) -> int64_t {  // tiles of group r (0: no rows)
+        int64_t r0, nr;
+        if (aligned) {
+            const int64_t f = r / wpf, j = r - f * wpf;
+            r0 = f * kpf + 32 * j;
+            nr = std::min(std::min<int64_t>(32, kpf - 32 * j), Tq - r0);
+        } else {
+            r0 = 32 * r;
+            nr = std::min<int64_t>(32, Tq - r0);
+        }
+        return nr > 0 ? tiles_to(r0 + nr - 1) : 0;
+    };
+    double contiguous = 0.0, paired = 0.0;
+    for (int64_t b = 0; b < k.nqb; ++b)
+        for (int s = 0; s < 4; ++s) {
+            const int64_t r0 = 256 * b + 32 * s, r1 = r0 + 128;
+            const int64_t x = r0 < Tq ? tiles_to(std::min(r0 + 31, Tq - 1)) : 0;
+            const int64_t y = r1 < Tq ? tiles_to(std::min(r1 + 31, Tq - 1)) : 0;
+            contiguous = std::max(contiguous, simd_cost(x, y));
+        }
+    for (int64_t b = 0; b < nqb; ++b)
+        for (int s = 0; s < 4; ++s) {
+            const int64_t lr = 4 * b + s, hr = nwr - 1 - lr;
+            const int64_t x = lr < nlight ? group_tiles(lr) : 0;
+            const int64_t y = hr >= nlight ? group_tiles(hr) : 0;
+            paired = std::max(paired, simd_cost(x, y));
+        }
+    if (paired <= 0.97 * contiguous) {
+        k.pair = 1;
+        k.wpf = aligned ? (int32_t)wpf : 0;
+        k.nwr = (int32_t)nwr;
+        k.nqb = (int)nqb;
+        k.nwg = (int)(nqb * H);
+    }
+}
+
 template <int D, bool SEG>
 hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
     KArgs k = ka;
@@ -1898,10 +2014,17 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         }
         const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;
         if (k.nprog == 0) {
-            if (fast)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast>), dim3(k.nwg), dim3(512), 0, stream, k);
+            int cu = 0;
+            if (const hipError_t e = cu_count(&cu)) return e;
+            plan_rows(k, p.H, cu);
+            if (fast && k.pair)
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast, true>), dim3(k.nwg), dim3(512), 0, stream, k);
+            else if (fast)
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast, false>), dim3(k.nwg), dim3(512), 0, stream, k);
+            else if (k.pair)
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane, true>), dim3(k.nwg), dim3(512), 0, stream, k);
             else
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane>), dim3(k.nwg), dim3(512), 0, stream, k);
+                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane, false>), dim3(k.nwg), dim3(512), 0, stream, k);
         } else {
             if (fast)
                 hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(512), 0, stream, k);
