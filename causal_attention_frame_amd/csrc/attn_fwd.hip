@@ -69,13 +69,11 @@ struct KArgs {
     int32_t nspare;
     int32_t tail_total;
     int32_t piece;
-    // Row groups of the plain head_dim-128 kernel: pair = 1 pairs light and
-    // heavy 32-row groups in each block (the kernel's PAIR instance; else
-    // blocks of 256 consecutive rows); wpf > 0 aligns the groups to frames,
-    // wpf groups per frame.
-    int32_t pair;
-    int32_t wpf;
-    int32_t nwr;  // row groups per head
+    // Row groups of the plain head_dim-128 kernel (its GMAP instance, picked
+    // by plan_rows): 32-row groups per head (GMAP 1), or groups per frame,
+    // frames and blocks per frame pair (GMAP 2).
+    int32_t nwr;
+    int32_t wpf, nframes, w1;
 };
 
 __device__ inline int key_limit(int i, const KArgs &a) {
@@ -463,7 +461,7 @@ enum DmaMode : int {
     kDmaLane = 1,  // anything else: per-lane segment lookup, zero rows past the end
 };
 
-template <int MODE, bool PAIR>
+template <int MODE, int GMAP>
 __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     constexpr int D = 128, BM = 256, BN = 32, NS = D / 16, NT = D / 32;
     constexpr int NB = 1;  // 32-row query blocks per wave (8 waves)
@@ -500,40 +498,60 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // byte strides of the DMA addressing (a segment is below 2^31 bytes)
     const int32_t ld2 = (int32_t)(a.ld * 2), hoff2 = (int32_t)(hoff * 2);
 
-    // Rows.  A head's rows form nwr groups of up to 32 rows: 32 consecutive
-    // rows each, or, with wpf > 0, wpf groups per frame that end with the
-    // frame (a group then never holds rows of two frames, whose key limits
-    // differ).  Blocks of 256 consecutive rows (!PAIR) take groups
-    // 8 qb .. 8 qb + 7.  With PAIR, groups [0, nlight) form the light half
-    // (fewer visible keys) and the rest the heavy half; block qb's waves 0-3
-    // take light groups 4 qb .. 4 qb + 3 and waves 4-7 the heavy groups
-    // nwr - 1 - 4 qb .. nwr - 4 - 4 qb.  Waves w and w + 4 of a workgroup share
-    // a SIMD, so every SIMD then holds one early and one late group and every
-    // block about the same work: for a launch of one round, where blocks of
-    // consecutive rows leave the compute units of the early frames idle while
-    // the last frame's blocks finish.  The host picks the mapping.  A group
-    // outside its half, or past the rows, has no rows here.
-    const int nwr = a.nwr, nlight = (nwr + 1) >> 1;
-    auto group_of = [&](int w) __attribute__((always_inline)) {
-        return !PAIR ? 8 * qb + w : w < 4 ? 4 * qb + w : nwr - 1 - (4 * qb + w - 4);
-    };
-    auto group_ok = [&](int w, int r) __attribute__((always_inline)) {
-        return !PAIR ? r < nwr : w < 4 ? r < nlight : r >= nlight;
-    };
-    // first row and row count of group r
-    auto group_rows = [&](int r, int &r0, int &nr) __attribute__((always_inline)) {
-        if (PAIR && a.wpf > 0) {
-            const int f = r / a.wpf, j = r - f * a.wpf;
-            r0 = f * a.kpf + 32 * j;
-            nr = min(min(32, a.kpf - 32 * j), a.Tq - r0);
-        } else {
-            r0 = 32 * r;
+    // Rows: each wave takes one group of up to 32 rows of its head.
+    //  GMAP 0: blocks of 256 consecutive rows; wave w takes rows
+    //          256 qb + 32 w .. + 31.
+    //  GMAP 1: the head's nwr groups of 32 consecutive rows split into a light
+    //          half [0, nlight) (fewer visible keys) and a heavy half; block
+    //          qb's waves 0-3 take light groups 4 qb .. 4 qb + 3 and waves 4-7
+    //          heavy groups nwr - 1 - 4 qb .. nwr - 4 - 4 qb.
+    //  GMAP 2: groups follow the frames (wpf groups per frame, the last one
+    //          ending with the frame, so that all rows of a group share one key
+    //          limit); frame f is paired with frame F - 1 - f: w1 blocks per
+    //          pair, waves 0-3 taking groups 4 q .. 4 q + 3 of the early frame
+    //          and waves 4-7 the same groups of the late frame; with F odd the
+    //          middle frame follows in blocks of 8 consecutive groups.
+    // Waves w and w + 4 of a workgroup share a SIMD, so with GMAP 1 and 2 each
+    // SIMD holds an early and a late group and blocks carry about equal work:
+    // for a launch of one round, where blocks of consecutive rows leave the
+    // compute units of the early frames idle while the last frame's blocks
+    // finish.  GMAP 2 also keeps the groups of a block to one pair of frames,
+    // so that no SIMD of a block still has two working waves after the
+    // others have one (every step ends at a barrier of the whole block).  A
+    // group outside its half or frame, or past the rows, has no rows here.
+    const int nlight = (a.nwr + 1) >> 1;
+    // first row and row count of wave w's group
+    auto wave_rows = [&](int w, int &r0, int &nr) __attribute__((always_inline)) {
+        r0 = 0;
+        nr = 0;
+        if constexpr (GMAP == 0) {
+            r0 = BM * qb + 32 * w;
             nr = min(32, a.Tq - r0);
+        } else if constexpr (GMAP == 1) {
+            const int r = w < 4 ? 4 * qb + w : a.nwr - 1 - (4 * qb + w - 4);
+            if (w < 4 ? r < nlight : r >= nlight) {
+                r0 = 32 * r;
+                nr = min(32, a.Tq - r0);
+            }
+        } else {
+            const int np = a.nframes >> 1;
+            int f, j;
+            if (qb < np * a.w1) {
+                const int fp = qb / a.w1, q = qb - fp * a.w1;
+                f = w < 4 ? fp : a.nframes - 1 - fp;
+                j = 4 * q + (w & 3);
+            } else {
+                f = np;
+                j = 8 * (qb - np * a.w1) + w;
+            }
+            if (j < a.wpf) {
+                r0 = f * a.kpf + 32 * j;
+                nr = min(min(32, a.kpf - 32 * j), a.Tq - r0);
+            }
         }
     };
-    const int grp = group_of(wave);
-    int qrow0 = 0, nrows = 0;  // this wave's first row and row count
-    if (group_ok(wave, grp)) group_rows(grp, qrow0, nrows);
+    int qrow0, nrows;  // this wave's first row and row count
+    wave_rows(wave, qrow0, nrows);
     const bool wvalid = nrows > 0;
 
     int qi[NB], lim[NB];
@@ -548,17 +566,24 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // for a wave without valid rows: steps past it skip the wave's MFMAs and
     // softmax (it still loads its share of the tiles and meets the barriers).
     const int lim_wave = wvalid ? key_limit(qrow0 + nrows - 1, a) : 0;
-    // The block's largest limit sets the steps every wave takes: that of its
-    // last row, in its highest group (limits grow with the row; a block
-    // always has a valid light group).  A highest group past the rows gives
-    // the limit of row Tq - 1, which can only add steps that every wave skips.
+    // The block's largest limit sets the steps every wave takes: that of the
+    // last row of its highest group (limits grow with the row): wave 7's
+    // group with GMAP 0, wave 4's with GMAP 1 and 2 (that of a middle-frame
+    // block of GMAP 2 has wave 0's limit), or the highest light group (GMAP
+    // 1).  A highest group past the rows gives the limit of row Tq - 1,
+    // which can only add steps that every wave skips.
     int lim_wg;
-    if (!PAIR) {
+    if constexpr (GMAP == 0) {
         lim_wg = key_limit(min(BM * qb + BM - 1, a.Tq - 1), a);
     } else {
-        const int hr = nwr - 1 - 4 * qb;
         int r0 = 0, nr = 0;
-        group_rows(hr >= nlight ? hr : min(4 * qb + 3, nlight - 1), r0, nr);
+        if constexpr (GMAP == 1) {
+            const int hr = a.nwr - 1 - 4 * qb;
+            r0 = 32 * (hr >= nlight ? hr : min(4 * qb + 3, nlight - 1));
+            nr = min(32, a.Tq - r0);
+        } else {
+            wave_rows(qb < (a.nframes >> 1) * a.w1 ? 4 : 0, r0, nr);
+        }
         lim_wg = key_limit(nr > 0 ? r0 + nr - 1 : a.Tq - 1, a);
     }
 
@@ -1921,68 +1946,114 @@ hipError_t cu_count(int *out) {
     return hipSuccess;
 }
 
-// Row mapping of the plain head_dim-128 launch (KArgs pair, wpf; sets nqb
-// and nwg).  Blocks of 256 consecutive rows, unless the launch fits in one
-// round on the compute units and pairing light with heavy 32-row groups
-// shortens the busiest SIMD by 3 % or more.  A SIMD holds waves w and w + 4
-// of a block; its cost in steps is estimated as min(a, b) + 0.62 |a - b| for
-// groups of a and b key tiles (a step in which only one of its waves works
-// takes 0.62 of a step with both, as measured on the Wan-1.3B step).  Paired
-// groups follow the frames when that pads the rows by at most 1/64.
-void plan_rows(KArgs &k, int64_t H, int cus) {
+// Row mapping of the plain head_dim-128 launch (the GMAP of the kernel above;
+// sets nqb, nwg and the mapping's KArgs).  Blocks of 256 consecutive rows,
+// unless the launch fits in one round on the compute units and a paired
+// mapping shortens the estimated longest block by 3 % or more.  Estimate: a
+// block runs steps while any wave has tiles; a step costs 1 while some SIMD
+// (waves w and w + 4) still has two working waves and 0.62 once every SIMD has
+// at most one (as measured on the Wan-1.3B step): with a_s <= b_s the tiles of
+// SIMD s's two groups, max a_s + 0.62 (max b_s - max a_s).  The frame-paired
+// mapping needs groups aligned to frames that pad at most 1/64 of the rows.
+int plan_rows(KArgs &k, int64_t H, int cus) {
     const int64_t Tq = k.Tq, kpf = k.kpf;
     auto tiles_to = [&](int64_t row) {  // key tiles of the row's limit
         const int64_t lim = std::min<int64_t>(k.prefix + (row / kpf + 1) * kpf, k.Tk);
         return (lim + 31) / 32;
     };
-    auto simd_cost = [](int64_t x, int64_t y) {
-        return (double)std::min(x, y) + 0.62 * (double)(x > y ? x - y : y - x);
-    };
-    k.pair = 0;
-    k.wpf = 0;
-    k.nwr = (int32_t)((Tq + 31) / 32);
-    k.nqb = (int)((Tq + 255) / 256);
-    k.nwg = (int)(k.nqb * H);
-    if ((int64_t)k.nqb * H > cus) return;  // several rounds: the dispatcher balances them
-    const int64_t wpf = (kpf + 31) / 32;
-    const bool aligned = kpf < Tq && (wpf * 32 - kpf) * 64 <= kpf;
-    const int64_t nwr = aligned ? (Tq + kpf - 1) / kpf * wpf : (Tq + 31) / 32;
-    const int64_t nlight = (nwr + 1) / 2, nqb = (nlight + 3) / 4;
-    if (nqb * H > cus) return;
-    auto group_tiles = [&](int64_t r) -> int64_t {  // tiles of group r (0: no rows)
-        int64_t r0, nr;
-        if (aligned) {
-            const int64_t f = r / wpf, j = r - f * wpf;
-            r0 = f * kpf + 32 * j;
-            nr = std::min(std::min<int64_t>(32, kpf - 32 * j), Tq - r0);
-        } else {
-            r0 = 32 * r;
-            nr = std::min<int64_t>(32, Tq - r0);
-        }
+    auto rows_tiles = [&](int64_t r0, int64_t nr) -> int64_t {
         return nr > 0 ? tiles_to(r0 + nr - 1) : 0;
     };
-    double contiguous = 0.0, paired = 0.0;
-    for (int64_t b = 0; b < k.nqb; ++b)
+    // block cost from the tiles of its eight waves
+    auto block_cost = [](const int64_t (&t)[8]) {
+        int64_t ma = 0, mb = 0;
         for (int s = 0; s < 4; ++s) {
-            const int64_t r0 = 256 * b + 32 * s, r1 = r0 + 128;
-            const int64_t x = r0 < Tq ? tiles_to(std::min(r0 + 31, Tq - 1)) : 0;
-            const int64_t y = r1 < Tq ? tiles_to(std::min(r1 + 31, Tq - 1)) : 0;
-            contiguous = std::max(contiguous, simd_cost(x, y));
+            ma = std::max(ma, std::min(t[s], t[s + 4]));
+            mb = std::max(mb, std::max(t[s], t[s + 4]));
         }
-    for (int64_t b = 0; b < nqb; ++b)
-        for (int s = 0; s < 4; ++s) {
-            const int64_t lr = 4 * b + s, hr = nwr - 1 - lr;
-            const int64_t x = lr < nlight ? group_tiles(lr) : 0;
-            const int64_t y = hr >= nlight ? group_tiles(hr) : 0;
-            paired = std::max(paired, simd_cost(x, y));
+        return (double)ma + 0.62 * (double)(mb - ma);
+    };
+    k.nwr = (int32_t)((Tq + 31) / 32);
+    k.wpf = k.nframes = k.w1 = 0;
+    k.nqb = (int)((Tq + 255) / 256);
+    k.nwg = (int)(k.nqb * H);
+    if ((int64_t)k.nqb * H > cus) return 0;  // several rounds: the dispatcher balances them
+    double best = 0.0;
+    for (int64_t b = 0; b < k.nqb; ++b) {
+        int64_t t[8];
+        for (int w = 0; w < 8; ++w) {
+            const int64_t r0 = 256 * b + 32 * w;
+            t[w] = rows_tiles(r0, std::min<int64_t>(32, Tq - r0));
         }
-    if (paired <= 0.97 * contiguous) {
-        k.pair = 1;
-        k.wpf = aligned ? (int32_t)wpf : 0;
-        k.nwr = (int32_t)nwr;
-        k.nqb = (int)nqb;
-        k.nwg = (int)(nqb * H);
+        best = std::max(best, block_cost(t));
     }
+    const double contiguous = best;
+    int gm = 0;
+    int64_t gm_nqb = k.nqb;
+    // GMAP 1
+    {
+        const int64_t nwr = k.nwr, nlight = (nwr + 1) / 2, nqb = (nlight + 3) / 4;
+        double c = 0.0;
+        for (int64_t b = 0; b < nqb; ++b) {
+            int64_t t[8];
+            for (int w = 0; w < 8; ++w) {
+                const int64_t r = w < 4 ? 4 * b + w : nwr - 1 - (4 * b + w - 4);
+                const bool ok = w < 4 ? r < nlight : r >= nlight;
+                t[w] = ok ? rows_tiles(32 * r, std::min<int64_t>(32, Tq - 32 * r)) : 0;
+            }
+            c = std::max(c, block_cost(t));
+        }
+        if (nqb * H <= cus && c < best && c <= 0.97 * contiguous) {
+            best = c;
+            gm = 1;
+            gm_nqb = nqb;
+        }
+    }
+    // GMAP 2
+    const int64_t wpf = (kpf + 31) / 32, F = (Tq + kpf - 1) / kpf;
+    if (F >= 2 && (wpf * 32 - kpf) * 64 <= kpf) {
+        const int64_t np = F / 2, w1 = (wpf + 3) / 4, w2 = F % 2 ? (wpf + 7) / 8 : 0;
+        const int64_t nqb = np * w1 + w2;
+        auto group_tiles = [&](int64_t f, int64_t j) -> int64_t {
+            if (j >= wpf) return 0;
+            const int64_t r0 = f * kpf + 32 * j;
+            return rows_tiles(r0, std::min(std::min<int64_t>(32, kpf - 32 * j), Tq - r0));
+        };
+        double c = 0.0;
+        for (int64_t b = 0; b < nqb; ++b) {
+            int64_t t[8];
+            for (int w = 0; w < 8; ++w) {
+                if (b < np * w1) {
+                    const int64_t fp = b / w1, q = b - fp * w1;
+                    t[w] = group_tiles(w < 4 ? fp : F - 1 - fp, 4 * q + (w & 3));
+                } else {
+                    t[w] = group_tiles(np, 8 * (b - np * w1) + w);
+                }
+            }
+            c = std::max(c, block_cost(t));
+        }
+        if (nqb * H <= cus && c < best && c <= 0.97 * contiguous) {
+            best = c;
+            gm = 2;
+            gm_nqb = nqb;
+            k.wpf = (int32_t)wpf;
+            k.nframes = (int32_t)F;
+            k.w1 = (int32_t)w1;
+        }
+    }
+    k.nqb = (int)gm_nqb;
+    k.nwg = (int)(gm_nqb * H);
+    return gm;
+}
+
+template <int MODE>
+void launch_plain(int gm, const KArgs &k, hipStream_t stream) {
+    if (gm == 2)
+        hipLaunchKernelGGL((attn_fwd_bf16_d128<MODE, 2>), dim3(k.nwg), dim3(512), 0, stream, k);
+    else if (gm == 1)
+        hipLaunchKernelGGL((attn_fwd_bf16_d128<MODE, 1>), dim3(k.nwg), dim3(512), 0, stream, k);
+    else
+        hipLaunchKernelGGL((attn_fwd_bf16_d128<MODE, 0>), dim3(k.nwg), dim3(512), 0, stream, k);
 }
 
 template <int D, bool SEG>
@@ -2016,15 +2087,11 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         if (k.nprog == 0) {
             int cu = 0;
             if (const hipError_t e = cu_count(&cu)) return e;
-            plan_rows(k, p.H, cu);
-            if (fast && k.pair)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast, true>), dim3(k.nwg), dim3(512), 0, stream, k);
-            else if (fast)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaFast, false>), dim3(k.nwg), dim3(512), 0, stream, k);
-            else if (k.pair)
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane, true>), dim3(k.nwg), dim3(512), 0, stream, k);
+            const int gm = plan_rows(k, p.H, cu);
+            if (fast)
+                launch_plain<kDmaFast>(gm, k, stream);
             else
-                hipLaunchKernelGGL((attn_fwd_bf16_d128<kDmaLane, false>), dim3(k.nwg), dim3(512), 0, stream, k);
+                launch_plain<kDmaLane>(gm, k, stream);
         } else {
             if (fast)
                 hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(512), 0, stream, k);
