@@ -1851,7 +1851,7 @@ constexpr double kSplitMargin = 0.9;
 // Chooses T, P and m by simulating the split schedule (see the work
 // decomposition comment) on the problem's unit lengths; false when the split
 // would not beat the plain launch by a margin.  Plans are cached per shape.
-bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, SplitPlan *out) {
+bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, double plain_steps, SplitPlan *out) {
     // Fixed-size storage throughout: planning allocates nothing (also on the
     // host), so callers that may not allocate can use the split path.
     struct Entry {
@@ -1882,7 +1882,7 @@ bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, SplitPlan *
         total += nq[qb] * H;
     }
     const double ov = kPieceOverheadTiles;
-    double best = (double)nmax * kSplitMargin;  // the plain launch's makespan, less a margin
+    double best = plain_steps * kSplitMargin;  // the plain launch's makespan, less a margin
     bool ok = false;
     SplitPlan bp{};
     const int64_t kmax = std::min<int64_t>(max_slots - U, 2 * kMaxSplitUnits);
@@ -1955,7 +1955,56 @@ hipError_t cu_count(int *out) {
 // at most one (as measured on the Wan-1.3B step): with a_s <= b_s the tiles of
 // SIMD s's two groups, max a_s + 0.62 (max b_s - max a_s).  The frame-paired
 // mapping needs groups aligned to frames that pad at most 1/64 of the rows.
-int plan_rows(KArgs &k, int64_t H, int cus) {
+struct RowPlan {
+    int gm;
+    int32_t nqb, nwr, wpf, nframes, w1;
+    double steps;
+};
+
+RowPlan plan_rows_uncached(const KArgs &k, int64_t H, int cus);
+
+// plan_rows with its results kept per problem shape (fixed-size storage, as
+// for the split plans: planning allocates nothing).
+int plan_rows(KArgs &k, int64_t H, int cus, double *steps) {
+    struct Entry {
+        int64_t key[6];
+        RowPlan plan;
+    };
+    constexpr int kCache = 64;
+    static std::mutex mu;
+    static Entry cache[kCache];
+    static int ncache = 0, next = 0;
+    const int64_t key[6] = {k.Tq, k.Tk, k.kpf, k.prefix, H, cus};
+    RowPlan rp{};
+    bool hit = false;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < ncache && !hit; ++i)
+            if (std::equal(key, key + 6, cache[i].key)) {
+                rp = cache[i].plan;
+                hit = true;
+            }
+    }
+    if (!hit) {
+        rp = plan_rows_uncached(k, H, cus);
+        std::lock_guard<std::mutex> lock(mu);
+        Entry &e = cache[next];
+        next = (next + 1) % kCache;
+        ncache = std::min(ncache + 1, kCache);
+        std::copy(key, key + 6, e.key);
+        e.plan = rp;
+    }
+    k.nqb = rp.nqb;
+    k.nwg = (int)(rp.nqb * H);
+    k.nwr = rp.nwr;
+    k.wpf = rp.wpf;
+    k.nframes = rp.nframes;
+    k.w1 = rp.w1;
+    *steps = rp.steps;
+    return rp.gm;
+}
+
+RowPlan plan_rows_uncached(const KArgs &k, int64_t H, int cus) {
     const int64_t Tq = k.Tq, kpf = k.kpf;
     auto tiles_to = [&](int64_t row) {  // key tiles of the row's limit
         const int64_t lim = std::min<int64_t>(k.prefix + (row / kpf + 1) * kpf, k.Tk);
@@ -1973,13 +2022,15 @@ int plan_rows(KArgs &k, int64_t H, int cus) {
         }
         return (double)ma + 0.62 * (double)(mb - ma);
     };
-    k.nwr = (int32_t)((Tq + 31) / 32);
-    k.wpf = k.nframes = k.w1 = 0;
-    k.nqb = (int)((Tq + 255) / 256);
-    k.nwg = (int)(k.nqb * H);
-    if ((int64_t)k.nqb * H > cus) return 0;  // several rounds: the dispatcher balances them
+    RowPlan rp{0, (int32_t)((Tq + 255) / 256), (int32_t)((Tq + 31) / 32), 0, 0, 0, 0.0};
+    if ((int64_t)rp.nqb * H > cus) {
+        // several rounds: the dispatcher balances them; the makespan estimate
+        // is that of the heaviest block
+        rp.steps = (double)tiles_to(Tq - 1);
+        return rp;
+    }
     double best = 0.0;
-    for (int64_t b = 0; b < k.nqb; ++b) {
+    for (int64_t b = 0; b < rp.nqb; ++b) {
         int64_t t[8];
         for (int w = 0; w < 8; ++w) {
             const int64_t r0 = 256 * b + 32 * w;
@@ -1987,12 +2038,11 @@ int plan_rows(KArgs &k, int64_t H, int cus) {
         }
         best = std::max(best, block_cost(t));
     }
+    rp.steps = best;
     const double contiguous = best;
-    int gm = 0;
-    int64_t gm_nqb = k.nqb;
     // GMAP 1
     {
-        const int64_t nwr = k.nwr, nlight = (nwr + 1) / 2, nqb = (nlight + 3) / 4;
+        const int64_t nwr = rp.nwr, nlight = (nwr + 1) / 2, nqb = (nlight + 3) / 4;
         double c = 0.0;
         for (int64_t b = 0; b < nqb; ++b) {
             int64_t t[8];
@@ -2005,8 +2055,9 @@ int plan_rows(KArgs &k, int64_t H, int cus) {
         }
         if (nqb * H <= cus && c < best && c <= 0.97 * contiguous) {
             best = c;
-            gm = 1;
-            gm_nqb = nqb;
+            rp.gm = 1;
+            rp.nqb = (int32_t)nqb;
+            rp.steps = c;
         }
     }
     // GMAP 2
@@ -2034,16 +2085,15 @@ int plan_rows(KArgs &k, int64_t H, int cus) {
         }
         if (nqb * H <= cus && c < best && c <= 0.97 * contiguous) {
             best = c;
-            gm = 2;
-            gm_nqb = nqb;
-            k.wpf = (int32_t)wpf;
-            k.nframes = (int32_t)F;
-            k.w1 = (int32_t)w1;
+            rp.gm = 2;
+            rp.nqb = (int32_t)nqb;
+            rp.wpf = (int32_t)wpf;
+            rp.nframes = (int32_t)F;
+            rp.w1 = (int32_t)w1;
+            rp.steps = c;
         }
     }
-    k.nqb = (int)gm_nqb;
-    k.nwg = (int)(gm_nqb * H);
-    return gm;
+    return rp;
 }
 
 template <int MODE>
@@ -2064,16 +2114,20 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         k.nwg = k.nqb * p.H;
         k.ws = nullptr;
         k.nprog = 0;
+        int cu = 0;
+        if (const hipError_t e = cu_count(&cu)) return e;
+        // the plain launch's row mapping and estimated makespan
+        KArgs kp = k;
+        double plain_steps = 0.0;
+        const int gm = plan_rows(kp, p.H, cu, &plain_steps);
         const int64_t U = (int64_t)k.nqb * p.H;
         if (p.ws && U < kMaxSplitUnits) {
-            int cu = 0;
-            if (const hipError_t e = cu_count(&cu)) return e;
             const int64_t G = std::min<int64_t>(cu, kMaxSplitUnits);
             bool fit = G > U;  // every XCD has a workgroup for each of its mains
             for (int64_t x = 0; fit && x < 8; ++x) fit = (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
             SplitPlan plan{};
             const int64_t max_slots = p.ws_slots > 0 ? std::min<int64_t>(p.ws_slots, 2 * G) : 2 * G;
-            if (fit && plan_split(k, p.H, (int)G, max_slots, &plan)) {
+            if (fit && plan_split(k, p.H, (int)G, max_slots, plain_steps, &plan)) {
                 k.ws = (float *)p.ws;
                 k.nprog = (int32_t)G;
                 k.units = (int32_t)U;
@@ -2085,13 +2139,10 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         }
         const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;
         if (k.nprog == 0) {
-            int cu = 0;
-            if (const hipError_t e = cu_count(&cu)) return e;
-            const int gm = plan_rows(k, p.H, cu);
             if (fast)
-                launch_plain<kDmaFast>(gm, k, stream);
+                launch_plain<kDmaFast>(gm, kp, stream);
             else
-                launch_plain<kDmaLane>(gm, k, stream);
+                launch_plain<kDmaLane>(gm, kp, stream);
         } else {
             if (fast)
                 hipLaunchKernelGGL((attn_fwd_bf16_d128_split<kDmaFast>), dim3(k.nprog), dim3(512), 0, stream, k);
