@@ -323,6 +323,12 @@ def main():
                     help="after the timed steps, time the attention kernel of this many more steps, each "
                          "after overwriting a 512 MiB buffer (L2 and the last-level cache start cold); "
                          "reported as cold_cache, outside value")
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128],
+                    help="streaming forward workloads: head dim, with the heads rescaled to keep the "
+                         "model width (64: twice the heads; the head_dim-64 kernel)")
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"],
+                    help="streaming forward workloads: input and arithmetic type (f32: the float32 "
+                         "kernel, bound by the fp32 vector ALUs)")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -350,22 +356,31 @@ def main():
     if args.workload in ("wan13b_cross_step", "wan13b_cross_step_bwd"):
         return cross(args, w, dev)
 
+    f32 = args.dtype == "f32"
+    if (f32 or args.head_dim) and not args.workload.endswith("stream_step"):
+        sys.exit("--dtype f32 and --head-dim apply to the streaming forward workloads")
+
     def to_dev(t):
+        if f32:
+            return torch.from_numpy(np.ascontiguousarray(t.values, dtype=np.float32)).to(dev)
         return torch.from_numpy(t.bits.view(np.int16)).to(dev).view(torch.bfloat16)
 
     kpf, H, d = w["k"], w["H"], w["d"]
+    if args.head_dim:
+        H, d = H * d // args.head_dim, args.head_dim
+    tdt = torch.float32 if f32 else torch.bfloat16
     stream = torch.cuda.current_stream(dev)
-    ws = rtr.new_workspace(d, rtr.RTR_BF16, dev) if args.split else None
+    ws = rtr.new_workspace(d, rtr.RTR_F32 if f32 else rtr.RTR_BF16, dev) if args.split else None
     if args.workload.endswith("stream_step"):
         C, W, R = (args.chunk_frames or w["C"]), w["W"], (args.ref_frames or w["R"])
-        x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=w["wid"],
+        x = gen.stream_inputs(kpf, H, d, C, W, R, args.dtype, base_seed=0, wid=w["wid"],
                               outlier_frac=w.get("outlier_frac", 0.0),
                               outlier_scale=w.get("outlier_scale", 1.0))
-        kr = torch.empty((W, kpf, H, d), dtype=torch.bfloat16, device=dev)
+        kr = torch.empty((W, kpf, H, d), dtype=tdt, device=dev)
         vr = torch.empty_like(kr)
-        kf = torch.empty((R, kpf, H, d), dtype=torch.bfloat16, device=dev)
+        kf = torch.empty((R, kpf, H, d), dtype=tdt, device=dev)
         vf = torch.empty_like(kf)
-        kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+        kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d, rtr.RTR_F32 if f32 else rtr.RTR_BF16)
         if args.ref_rope:
             rtr.rtr_kv_set_ref_rope(kv, torch.empty_like(kf), 22, 10000.0, R)
         rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, to_dev(x["ref_k"]), to_dev(x["ref_v"]), R, -1)
@@ -374,7 +389,7 @@ def main():
         o = torch.empty_like(q)
         frames = C
         flops = 4 * d * H * stream_pairs_per_head(kpf, C, R + W, args.block_frames)
-        append_bytes = 2 * 2 * C * kpf * H * d * 2     # K and V, read + write
+        append_bytes = 2 * 2 * C * kpf * H * d * (4 if f32 else 2)     # K and V, read + write
         config = {"workload": args.workload, "heads": H, "head_dim": d, "tokens_per_frame": kpf,
                   "chunk_frames": C, "window_frames": W, "ref_frames": R,
                   "query_tokens": C * kpf, "key_tokens": (R + W + C) * kpf}
@@ -448,7 +463,14 @@ def main():
     # the committed counter records cover each workload's own configuration only
     default_cfg = (not args.split and not args.ref_rope and args.block_frames == 1
                    and args.chunk_frames in (0, w.get("C", 0)) and args.ref_frames in (0, w.get("R", 0)))
+    default_cfg = default_cfg and not f32 and args.head_dim in (0, w["d"])
     traffic = read_traffic(args.workload) if default_cfg else None
+    peak = PEAK_F32_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    if f32:
+        kname = "attn_fwd_f32"
+    else:
+        kname = ("attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16") \
+            + ("" if ws is None else " (+ attn_combine_d128 when the library splits)")
 
     out = {
         "metric": METRIC,
@@ -461,20 +483,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": args.dtype,
         "data": "synthetic",
         "config": config,
         "latent_frames_per_s_per_layer": round(frames / (ms_per_step * 1e-3), 1),
-        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "frac_of_mfma_peak": round(value / peak, 4),
         "roofline": {
-            "bound": "mfma",
+            "bound": "alu" if f32 else "mfma",
             "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "kernel": ("attn_fwd_bf16_d128" if d == 128 else "attn_fwd_bf16")
-                      + ("" if ws is None else " (+ attn_combine_d128 when the library splits)"),
+            "kernel": kname,
             "schedule": "plain" if ws is None else "workspace given: split-K where the planner predicts a gain",
             **timing_stats(attn_ms),
             "algorithmic_flop_per_launch": flops,
