@@ -534,15 +534,18 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
                 nr = min(32, a.Tq - r0);
             }
         } else {
-            const int np = a.nframes >> 1;
+            // numbered from the last block, so that the dispatcher's
+            // highest-index-first order starts the heaviest blocks (frame pair
+            // 0) first and the light middle-frame blocks last
+            const int np = a.nframes >> 1, b = a.nqb - 1 - qb;
             int f, j;
-            if (qb < np * a.w1) {
-                const int fp = qb / a.w1, q = qb - fp * a.w1;
+            if (b < np * a.w1) {
+                const int fp = b / a.w1, q = b - fp * a.w1;
                 f = w < 4 ? fp : a.nframes - 1 - fp;
                 j = 4 * q + (w & 3);
             } else {
                 f = np;
-                j = 8 * (qb - np * a.w1) + w;
+                j = 8 * (b - np * a.w1) + w;
             }
             if (j < a.wpf) {
                 r0 = f * a.kpf + 32 * j;
@@ -582,7 +585,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             r0 = 32 * (hr >= nlight ? hr : min(4 * qb + 3, nlight - 1));
             nr = min(32, a.Tq - r0);
         } else {
-            wave_rows(qb < (a.nframes >> 1) * a.w1 ? 4 : 0, r0, nr);
+            wave_rows(a.nqb - 1 - qb < (a.nframes >> 1) * a.w1 ? 4 : 0, r0, nr);
         }
         lim_wg = key_limit(nr > 0 ? r0 + nr - 1 : a.Tq - 1, a);
     }
