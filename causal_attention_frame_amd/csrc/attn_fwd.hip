@@ -572,9 +572,8 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     // The block's largest limit sets the steps every wave takes: that of the
     // last row of its highest group (limits grow with the row): wave 7's
     // group with GMAP 0, wave 4's with GMAP 1 and 2 (that of a middle-frame
-    // block of GMAP 2 has wave 0's limit), or the highest light group (GMAP
-    // 1).  A highest group past the rows gives the limit of row Tq - 1,
-    // which can only add steps that every wave skips.
+    // block of GMAP 2 has wave 0's limit, as has a frame-pair block whose
+    // late groups are empty), or the highest light group (GMAP 1).
     int lim_wg;
     if constexpr (GMAP == 0) {
         lim_wg = key_limit(min(BM * qb + BM - 1, a.Tq - 1), a);
@@ -586,6 +585,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             nr = min(32, a.Tq - r0);
         } else {
             wave_rows(a.nqb - 1 - qb < (a.nframes >> 1) * a.w1 ? 4 : 0, r0, nr);
+            // a frame pair whose late-frame groups lie past the rows (a
+            // partial last frame) has the early frame's limit
+            if (nr <= 0) wave_rows(0, r0, nr);
         }
         lim_wg = key_limit(nr > 0 ? r0 + nr - 1 : a.Tq - 1, a);
     }

@@ -154,6 +154,11 @@ FULL_CASES = [
     (1, 1, 1, 128),        # a single token
     (129, 7, 2, 64),
     (2000, 160, 2, 128),
+    # launches of one round that the forward planner serves with paired row
+    # groups: frames of 160 and 96 rows (groups aligned to frames), an even
+    # frame count (960 rows) and an odd one with a partial last frame
+    (960, 160, 2, 128),
+    (1000, 96, 2, 128),
 ]
 
 
