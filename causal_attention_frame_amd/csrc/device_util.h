@@ -36,20 +36,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 // cuts a head in two then gets about its share of that head's work, where
 // ranges of consecutive blocks gave one XCD the heavy half and its neighbour
 // the light half.
+//
+// With lo = A nblk + a and hi - 1 = B nblk + bl, the heads whose position p
+// lies in the range are A + [p < a] .. B - [p > bl], so the walk over the
+// blocks needs two divisions in all (integer divisions by a variable are long
+// instruction sequences; one per block and head bound cost the last
+// workgroups of a 20-block launch ~3 us before their first key tile).
 __device__ inline void xcd_order(int b, int nwg, int nblk, int &head, int &blk) {
     const int x = b & 7, i = b >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
     const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
     const int half = nblk >> 1;
+    const int A = lo / nblk, a = lo - A * nblk;
+    const int B = (hi - 1) / nblk, bl = (hi - 1) - B * nblk;
     int rem = i;
-    head = lo / nblk;
-    blk = lo - head * nblk;  // not reached for a valid b
+    head = A;
+    blk = a;  // not reached for a valid b
     for (int q = nblk - 1; q >= 0; --q) {
         const int p = q >= half ? 2 * (nblk - 1 - q) : 2 * q + 1;  // position of block q
-        if (hi - 1 - p < 0) continue;
-        const int hmin = lo - p > 0 ? (lo - p + nblk - 1) / nblk : 0;
-        const int hmax = (hi - 1 - p) / nblk;
-        const int cnt = hmax >= hmin ? hmax - hmin + 1 : 0;
+        const int hmin = A + (p < a ? 1 : 0), hmax = B - (p > bl ? 1 : 0);
+        const int cnt = hmax - hmin + 1;
+        if (cnt <= 0) continue;
         if (rem < cnt) {
             head = hmin + rem;
             blk = q;
