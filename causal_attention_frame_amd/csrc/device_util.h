@@ -42,7 +42,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // blocks needs two divisions in all (integer divisions by a variable are long
 // instruction sequences; one per block and head bound cost the last
 // workgroups of a 20-block launch ~3 us before their first key tile).
-__device__ inline void xcd_order(int b, int nwg, int nblk, int &head, int &blk) {
+__host__ __device__ inline void xcd_order(int b, int nwg, int nblk, int &head, int &blk) {
     const int x = b & 7, i = b >> 3;
     const int q8 = nwg >> 3, r8 = nwg & 7;
     const int lo = x * q8 + (x < r8 ? x : r8), hi = lo + q8 + (x < r8 ? 1 : 0);
