@@ -539,8 +539,9 @@ __device__ __attribute__((always_inline)) inline void dkdv_block(const BArgs &a,
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_d128(const BArgs a) {
     __shared__ __attribute__((aligned(256))) uint16_t smem[kDkdvLds];
+    __shared__ int sMap[2];
     int head, blk;
-    xcd_order(blockIdx.x, a.nwg, a.nkb + a.nkbp * a.nsplit, head, blk);
+    xcd_order_shared(blockIdx.x, a.nwg, a.nkb + a.nkbp * a.nsplit, head, blk, sMap);
     // Blocks of cached prefix keys (streaming step; every row sees them, so
     // they carry the most work) take the highest indices, then the blocks of
     // the query rows' own keys, earliest keys highest.
@@ -571,8 +572,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
 
+    __shared__ int sMap[2];
     int head, qb;
-    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order_shared(blockIdx.x, a.nwg, a.nqb, head, qb, sMap);
     const int q0 = qb * 256;
     const long hoff = (long)head * kD;
     const int qi = q0 + 32 * wave + n;

@@ -158,8 +158,9 @@ void attn_fwd_bf16(const KArgs a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 31, g = lane >> 5;
 
+    __shared__ int sMap[2];
     int head, qb;
-    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order_shared(blockIdx.x, a.nwg, a.nqb, head, qb, sMap);
     const int q0 = qb * BM;
     const long hoff = (long)head * D;
 
@@ -492,8 +493,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
 
+    __shared__ int sMap[2];
     int head, qb;
-    xcd_order(blockIdx.x, a.nwg, a.nqb, head, qb);
+    xcd_order_shared(blockIdx.x, a.nwg, a.nqb, head, qb, sMap);
     const long hoff = (long)head * D;
     // byte strides of the DMA addressing (a segment is below 2^31 bytes)
     const int32_t ld2 = (int32_t)(a.ld * 2), hoff2 = (int32_t)(hoff * 2);

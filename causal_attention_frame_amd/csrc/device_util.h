@@ -66,6 +66,25 @@ __host__ __device__ inline void xcd_order(int b, int nwg, int nblk, int &head, i
     }
 }
 
+// xcd_order for the whole workgroup, walked by its first wave and shared
+// through smap (two ints of LDS): the waves of a compute unit share one scalar
+// unit, so every wave walking the blocks itself took eight times as long (up
+// to ~3 us before the first key tile of a 20-block launch).  Ends with a
+// workgroup barrier.
+__device__ inline void xcd_order_shared(int b, int nwg, int nblk, int &head, int &blk, int *smap) {
+    if (threadIdx.x < 64) {
+        int h, q;
+        xcd_order(b, nwg, nblk, h, q);
+        if (threadIdx.x == 0) {
+            smap[0] = h;
+            smap[1] = q;
+        }
+    }
+    __syncthreads();
+    head = __builtin_amdgcn_readfirstlane(smap[0]);
+    blk = __builtin_amdgcn_readfirstlane(smap[1]);
+}
+
 __device__ inline uint32_t lds_addr(const lds_u16 *p) { return (uint32_t)(uintptr_t)p; }
 
 __device__ inline v4i16 lds_tr16(const lds_u16 *p) {
