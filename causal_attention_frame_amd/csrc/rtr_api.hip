@@ -27,7 +27,7 @@
 
 struct rtr_kv_cache {
     void *k_ring, *v_ring, *k_ref, *v_ref;
-    int32_t W, R_cap;
+    int32_t W, N, R_cap;  // window frames, physical ring slots (N >= W), reference capacity
     int64_t kpf;
     int32_t H, d;
     rtr_dtype dt;
@@ -35,6 +35,7 @@ struct rtr_kv_cache {
     int32_t count, head, ref_frames;
     int64_t ref_gen, next_id;
     int64_t slot_frame_id[RTR_MAX_WINDOW];  // indexed by physical slot
+    // The window's count frames occupy slots head, head + 1, ... (mod N).
     // Position-aware reference (rtr_kv_set_ref_rope): the reference K rotated
     // into k_ref_view for the last shift applied, valid while (shift, ref_gen,
     // ref_frames) are unchanged.
@@ -98,18 +99,21 @@ int check_scale(float scale) {
 
 int64_t frame_bytes(const rtr_kv_cache *kv) { return kv->kpf * kv->H * kv->d * esize(kv->dt); }
 
-// One append of a frame to the ring metadata; returns the slot written or -1
-// when W == 0 (nothing is kept).
-int ring_push(int32_t W, int32_t &count, int32_t &head, int64_t &next_id, int64_t *slot_ids) {
+// One append of a frame to the ring metadata (W window frames over N >= W
+// slots); returns the slot written or -1 when W == 0 (nothing is kept).  A
+// full window takes the new frame in the slot after its newest and frees its
+// oldest: with N == W that is the oldest frame's slot, with N > W a slot the
+// window does not use.
+int ring_push(int32_t W, int32_t N, int32_t &count, int32_t &head, int64_t &next_id, int64_t *slot_ids) {
     const int64_t id = next_id++;
     if (W == 0) return -1;
     int slot;
     if (count < W) {
-        slot = (head + count) % W;
+        slot = (head + count) % N;
         ++count;
     } else {
-        slot = head;
-        head = (head + 1) % W;
+        slot = (head + W) % N;
+        head = (head + 1) % N;
     }
     slot_ids[slot] = id;
     return slot;
@@ -124,7 +128,7 @@ void plan_append(const rtr_kv_cache *kv, int32_t n, int32_t *slots, int32_t &cou
     std::memcpy(slot_ids, kv->slot_frame_id, sizeof(kv->slot_frame_id));
     const int32_t keep_from = n - (n < kv->W ? n : kv->W);  // survivors: f >= n - min(n, W)
     for (int32_t f = 0; f < n; ++f) {
-        const int s = ring_push(kv->W, count, head, next_id, slot_ids);
+        const int s = ring_push(kv->W, kv->N, count, head, next_id, slot_ids);
         if (slots) slots[f] = (f >= keep_from) ? s : -1;
     }
 }
@@ -349,9 +353,19 @@ int rtr_attn_block_causal_bwd(const void *q, const void *k, const void *v, const
 int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
                   int32_t window_frames, int32_t ref_capacity_frames, int64_t tokens_per_frame,
                   int32_t H, int32_t d, rtr_dtype dtype) {
+    return rtr_kv_create_slots(out, k_ring, v_ring, k_ref, v_ref, window_frames, window_frames,
+                               ref_capacity_frames, tokens_per_frame, H, d, dtype);
+}
+
+int rtr_kv_create_slots(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
+                        int32_t window_frames, int32_t ring_slots, int32_t ref_capacity_frames,
+                        int64_t tokens_per_frame, int32_t H, int32_t d, rtr_dtype dtype) {
     if (!out) return fail(RTR_EINVAL, "out is NULL");
     if (window_frames < 0 || window_frames > RTR_MAX_WINDOW)
         return fail(RTR_EUNSUPPORTED, "window_frames=%d outside [0, %d]", window_frames, RTR_MAX_WINDOW);
+    if (ring_slots < window_frames || ring_slots > RTR_MAX_WINDOW)
+        return fail(RTR_EUNSUPPORTED, "ring_slots=%d outside [window_frames=%d, %d]", ring_slots, window_frames,
+                    RTR_MAX_WINDOW);
     if (ref_capacity_frames < 0 || ref_capacity_frames > RTR_MAX_REF)
         return fail(RTR_EUNSUPPORTED, "ref_capacity_frames=%d outside [0, %d]", ref_capacity_frames,
                     RTR_MAX_REF);
@@ -369,7 +383,7 @@ int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, v
     if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(k_ref) || !aligned16(v_ref))
         return fail(RTR_EINVAL, "cache buffers must be 16-byte aligned");
     const int64_t fb = tokens_per_frame * H * d * esize(dtype);
-    const int64_t ring_b = fb * window_frames, ref_b = fb * ref_capacity_frames;
+    const int64_t ring_b = fb * ring_slots, ref_b = fb * ref_capacity_frames;
     const void *bufs[4] = {k_ring, v_ring, k_ref, v_ref};
     const int64_t sizes[4] = {ring_b, ring_b, ref_b, ref_b};
     for (int i = 0; i < 4; ++i)
@@ -384,6 +398,7 @@ int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, v
     kv->k_ref = k_ref;
     kv->v_ref = v_ref;
     kv->W = window_frames;
+    kv->N = ring_slots;
     kv->R_cap = ref_capacity_frames;
     kv->kpf = tokens_per_frame;
     kv->H = H;
@@ -436,7 +451,7 @@ int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new, 
     if (!aligned16(k_new) || !aligned16(v_new)) return fail(RTR_EINVAL, "k_new/v_new must be 16-byte aligned");
     const int64_t fb = frame_bytes(kv);
     const int64_t nb = fb * n_frames;
-    const int64_t ring_b = fb * kv->W;
+    const int64_t ring_b = fb * kv->N;
     for (const void *src : {k_new, v_new})
         for (const void *dst : {kv->k_ring, kv->v_ring})
             if (overlaps(src, nb, dst, ring_b)) return fail(RTR_EINVAL, "new frames overlap the ring buffers");
@@ -450,7 +465,7 @@ int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new, 
     int64_t next_id = kv->next_id, ids[RTR_MAX_WINDOW];
     std::memcpy(ids, kv->slot_frame_id, sizeof ids);
     for (int32_t f = 0; f < n_frames; ++f) {
-        const int s = ring_push(kv->W, count, head, next_id, ids);
+        const int s = ring_push(kv->W, kv->N, count, head, next_id, ids);
         if (f >= first) slots[f - first] = s;
     }
     rtr::CopyJobs jobs;
@@ -498,7 +513,7 @@ int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, con
                         if (overlaps(src, nb, dst, fb * kv->R_cap))
                             return fail(RTR_EINVAL, "new reference overlaps the reference slot");
                     for (const void *dst : {kv->k_ring, kv->v_ring})
-                        if (overlaps(src, nb, dst, fb * kv->W))
+                        if (overlaps(src, nb, dst, fb * kv->N))
                             return fail(RTR_EINVAL, "new reference overlaps the ring buffers");
                 }
                 copy = true;
@@ -523,7 +538,7 @@ int rtr_kv_reset_ref(rtr_kv_cache *kv, rtr_ref_mode mode, const void *k_ref, con
         kv->ref_frames = 0;
     }
     if (keep_recent >= 0 && keep_recent < kv->count) {
-        kv->head = (kv->head + kv->count - keep_recent) % kv->W;
+        kv->head = (kv->head + kv->count - keep_recent) % kv->N;
         kv->count = keep_recent;
     }
     return ok();
@@ -578,7 +593,7 @@ int key_segments(const rtr_kv_cache *kv, const void *kref, const void *k, const 
         vseg[nseg++] = (const char *)kv->v_ref + r * fb;
     }
     for (int i = 0; i < kv->count; ++i) {
-        const int slot = (kv->head + i) % kv->W;
+        const int slot = (kv->head + i) % kv->N;
         kseg[nseg] = (const char *)kv->k_ring + slot * fb;
         vseg[nseg++] = (const char *)kv->v_ring + slot * fb;
     }
@@ -596,7 +611,7 @@ int key_segments(const rtr_kv_cache *kv, const void *kref, const void *k, const 
 bool aliases_cache(const rtr_kv_cache *kv, const void *p, int64_t nb) {
     const int64_t fb = frame_bytes(kv);
     for (int i = 0; i < kv->count; ++i) {
-        const int64_t off = (int64_t)((kv->head + i) % kv->W) * fb;
+        const int64_t off = (int64_t)((kv->head + i) % kv->N) * fb;
         if (overlaps(p, nb, (const char *)kv->k_ring + off, fb) || overlaps(p, nb, (const char *)kv->v_ring + off, fb))
             return true;
     }
@@ -659,7 +674,7 @@ int stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void
     const int64_t out_b = Tq * kv->H * kv->d * esize(out_dtype);
     const int64_t lse_b = Tq * kv->H * 4;
     const void *ins[8] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, kv->k_ref_view};
-    const int64_t in_sz[8] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap,
+    const int64_t in_sz[8] = {in_b, in_b, in_b, fb * kv->N, fb * kv->N, fb * kv->R_cap, fb * kv->R_cap,
                               kv->k_ref_view ? fb * kv->R_cap : 0};
     for (int i = 0; i < 8; ++i) {
         if (overlaps(o, out_b, ins[i], in_sz[i])) return fail(RTR_EINVAL, "o overlaps an input or the cache");
@@ -669,7 +684,7 @@ int stream_step(const rtr_kv_cache *kv, const void *q, const void *k, const void
     void *ws = nullptr;
     {
         const void *bufs[9] = {q, k, v, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref, o, lse};
-        const int64_t sizes[9] = {in_b, in_b, in_b, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap,
+        const int64_t sizes[9] = {in_b, in_b, in_b, fb * kv->N, fb * kv->N, fb * kv->R_cap, fb * kv->R_cap,
                                   out_b, lse ? lse_b : 0};
         if (int rc = check_workspace(workspace, workspace_bytes, kv->d, kv->dt, bufs, sizes, 9, &ws, ws_slots))
             return rc;
@@ -740,7 +755,7 @@ int rtr_attn_stream_step_bwd(const rtr_kv_cache *kv, const void *q, const void *
             return fail(RTR_EINVAL, "q, k, v, o or d_o overlaps a window slot or the reference that the step reads");
     const int64_t out_sz[5] = {tb, tb, tb, dk_cache ? pb : 0, dv_cache ? pb : 0};
     const void *src[10] = {q, k, v, o, lse, d_o, kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
-    const int64_t src_sz[10] = {tb, tb, tb, tb, lb, tb, fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
+    const int64_t src_sz[10] = {tb, tb, tb, tb, lb, tb, fb * kv->N, fb * kv->N, fb * kv->R_cap, fb * kv->R_cap};
     for (int i = 0; i < 5; ++i) {
         for (int j = 0; j < 10; ++j)
             if (overlaps(out[i], out_sz[i], src[j], src_sz[j])) return fail(RTR_EINVAL, "an output overlaps an input or the cache");
@@ -1026,7 +1041,7 @@ int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, 
     if (!aligned16(k_ref_view)) return fail(RTR_EINVAL, "k_ref_view must be 16-byte aligned");
     const int64_t fb = frame_bytes(kv);
     const void *bufs[4] = {kv->k_ring, kv->v_ring, kv->k_ref, kv->v_ref};
-    const int64_t sizes[4] = {fb * kv->W, fb * kv->W, fb * kv->R_cap, fb * kv->R_cap};
+    const int64_t sizes[4] = {fb * kv->N, fb * kv->N, fb * kv->R_cap, fb * kv->R_cap};
     for (int i = 0; i < 4; ++i)
         if (overlaps(k_ref_view, fb * kv->R_cap, bufs[i], sizes[i]))
             return fail(RTR_EINVAL, "k_ref_view overlaps a cache buffer");
@@ -1051,6 +1066,7 @@ int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out) {
     if (!out) return fail(RTR_EINVAL, "out is NULL");
     std::memset(out, 0, sizeof *out);
     out->window_frames = kv->W;
+    out->ring_slots = kv->N;
     out->count = kv->count;
     out->head = kv->head;
     out->ref_frames = kv->ref_frames;
@@ -1061,7 +1077,7 @@ int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out) {
         out->frame_id[p] = -1;
     }
     for (int p = 0; p < kv->count; ++p) {
-        const int s = (kv->head + p) % kv->W;
+        const int s = (kv->head + p) % kv->N;
         out->slot[p] = s;
         out->frame_id[p] = kv->slot_frame_id[s];
     }
@@ -1072,13 +1088,15 @@ int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in) {
     if (int rc = check_cache(kv)) return rc;
     if (!in) return fail(RTR_EINVAL, "in is NULL");
     if (in->window_frames != kv->W) return fail(RTR_ESTATE, "snapshot window %d != cache window %d", in->window_frames, kv->W);
+    if (in->ring_slots != kv->N)
+        return fail(RTR_ESTATE, "snapshot ring slots %d != cache ring slots %d", in->ring_slots, kv->N);
     if (in->count < 0 || in->count > kv->W) return fail(RTR_ESTATE, "count out of range");
-    if (kv->W > 0 ? (in->head < 0 || in->head >= kv->W) : in->head != 0) return fail(RTR_ESTATE, "head out of range");
+    if (kv->N > 0 ? (in->head < 0 || in->head >= kv->N) : in->head != 0) return fail(RTR_ESTATE, "head out of range");
     if (in->ref_frames < 0 || in->ref_frames > kv->R_cap) return fail(RTR_ESTATE, "ref_frames out of range");
     if (in->ref_generation < 0 || in->next_frame_id < 0) return fail(RTR_ESTATE, "negative counters");
     int64_t prev = -1;
     for (int p = 0; p < in->count; ++p) {
-        if (in->slot[p] != (in->head + p) % kv->W) return fail(RTR_ESTATE, "slot list is not a ring from head");
+        if (in->slot[p] != (in->head + p) % kv->N) return fail(RTR_ESTATE, "slot list is not a ring from head");
         if (in->frame_id[p] <= prev || in->frame_id[p] >= in->next_frame_id)
             return fail(RTR_ESTATE, "frame ids must increase and stay below next_frame_id");
         prev = in->frame_id[p];

@@ -31,11 +31,12 @@ class rtr_kv_state(ctypes.Structure):
         ("next_frame_id", _c_i64),
         ("slot", _c_i32 * RTR_MAX_WINDOW),
         ("frame_id", _c_i64 * RTR_MAX_WINDOW),
+        ("ring_slots", _c_i32),
     ]
 
     def as_dict(self):
         n = self.count
-        return dict(window_frames=self.window_frames, count=n, head=self.head,
+        return dict(window_frames=self.window_frames, ring_slots=self.ring_slots, count=n, head=self.head,
                     ref_frames=self.ref_frames, ref_generation=self.ref_generation,
                     next_frame_id=self.next_frame_id, slot=list(self.slot[:n]),
                     frame_id=list(self.frame_id[:n]))
@@ -53,6 +54,8 @@ _SIGNATURES = {
     "rtr_attn_bwd_workspace_size": (ctypes.c_int, [_c_i64, _c_i32, _c_i32, ctypes.POINTER(ctypes.c_size_t)]),
     "rtr_kv_create": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _c_i32, _c_i32,
                                      _c_i64, _c_i32, _c_i32, ctypes.c_int]),
+    "rtr_kv_create_slots": (ctypes.c_int, [ctypes.POINTER(_vp), _vp, _vp, _vp, _vp, _c_i32, _c_i32,
+                                           _c_i32, _c_i64, _c_i32, _c_i32, ctypes.c_int]),
     "rtr_kv_destroy": (ctypes.c_int, [_vp]),
     "rtr_kv_append_evict": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _vp]),
     "rtr_kv_next_slots": (ctypes.c_int, [_vp, _c_i32, ctypes.POINTER(_c_i32)]),
@@ -252,20 +255,27 @@ def rtr_attn_stream_step_bwd(kv, q, k, v, o, lse, d_o, chunk_frames, block_frame
 class KVCache:
     """One layer's reference-anchored rolling KV cache (handle + buffers).
 
-    k_ring, v_ring: [W, k, H, d]; k_ref, v_ref: [R_cap, k, H, d] (or None).
-    Tensors are kept referenced for the handle's lifetime.  Integer device
-    addresses are accepted too (metadata-only use)."""
+    k_ring, v_ring: [N, k, H, d] with N = ring_slots (W when None);
+    k_ref, v_ref: [R_cap, k, H, d] (or None).  Tensors are kept referenced for
+    the handle's lifetime.  Integer device addresses are accepted too
+    (metadata-only use)."""
 
     def __init__(self, k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
-                 tokens_per_frame, H, d, dtype):
+                 tokens_per_frame, H, d, dtype, ring_slots=None):
         self._bufs = (k_ring, v_ring, k_ref, v_ref)
         self.W, self.R_cap, self.kpf, self.H, self.d = (window_frames, ref_capacity_frames,
                                                         tokens_per_frame, H, d)
+        self.N = window_frames if ring_slots is None else ring_slots
         self.dtype = dtype
         h = _vp()
-        _check(lib().rtr_kv_create(ctypes.byref(h), _ptr(k_ring), _ptr(v_ring), _ptr(k_ref),
-                                   _ptr(v_ref), window_frames, ref_capacity_frames,
-                                   tokens_per_frame, H, d, dtype), "rtr_kv_create")
+        if ring_slots is None:
+            _check(lib().rtr_kv_create(ctypes.byref(h), _ptr(k_ring), _ptr(v_ring), _ptr(k_ref),
+                                       _ptr(v_ref), window_frames, ref_capacity_frames,
+                                       tokens_per_frame, H, d, dtype), "rtr_kv_create")
+        else:
+            _check(lib().rtr_kv_create_slots(ctypes.byref(h), _ptr(k_ring), _ptr(v_ring), _ptr(k_ref),
+                                             _ptr(v_ref), window_frames, ring_slots, ref_capacity_frames,
+                                             tokens_per_frame, H, d, dtype), "rtr_kv_create_slots")
         self._h = h
 
     @property
@@ -288,6 +298,12 @@ def rtr_kv_create(k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_fram
                   tokens_per_frame, H, d, dtype=RTR_BF16):
     return KVCache(k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
                    tokens_per_frame, H, d, dtype)
+
+
+def rtr_kv_create_slots(k_ring, v_ring, k_ref, v_ref, window_frames, ring_slots, ref_capacity_frames,
+                        tokens_per_frame, H, d, dtype=RTR_BF16):
+    return KVCache(k_ring, v_ring, k_ref, v_ref, window_frames, ref_capacity_frames,
+                   tokens_per_frame, H, d, dtype, ring_slots=ring_slots)
 
 
 def rtr_kv_destroy(kv):

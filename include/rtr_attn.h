@@ -68,8 +68,8 @@ typedef void *rtr_stream; /* hipStream_t */
 typedef struct rtr_kv_cache rtr_kv_cache; /* opaque, host-side ring metadata */
 
 /* Snapshot of a cache's metadata.  Window entries are in logical order, oldest
- * first: entry p lives in physical ring slot slot[p] and holds the frame with
- * generation-order id frame_id[p]. */
+ * first: entry p lives in physical ring slot slot[p] = (head + p) mod
+ * ring_slots and holds the frame with generation-order id frame_id[p]. */
 typedef struct {
     int32_t window_frames;  /* W */
     int32_t count;          /* valid window frames, 0..W */
@@ -79,6 +79,7 @@ typedef struct {
     int64_t next_frame_id;  /* id the next appended frame receives */
     int32_t slot[RTR_MAX_WINDOW];
     int64_t frame_id[RTR_MAX_WINDOW];
+    int32_t ring_slots;     /* physical ring slots N, W <= N <= RTR_MAX_WINDOW */
 } rtr_kv_state;
 
 /* ------------------------------------------------------------------------
@@ -171,26 +172,46 @@ int rtr_attn_bwd_workspace_size(int64_t T, int32_t H, int32_t d, size_t *bytes);
 int rtr_kv_create(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
                   int32_t window_frames, int32_t ref_capacity_frames,
                   int64_t tokens_per_frame, int32_t H, int32_t d, rtr_dtype dtype);
+
+/* The same cache over a ring of ring_slots >= W physical frame slots
+ * (k_ring, v_ring: [ring_slots, k, H, d]; W <= ring_slots <= RTR_MAX_WINDOW);
+ * rtr_kv_create is this with ring_slots = W.  The window is still the W
+ * newest frames.  With ring_slots >= W + n, an append of n frames writes only
+ * slots that the current window does not use (once the window is full, each
+ * new frame goes to the slot after the newest and the oldest frame's slot is
+ * freed), so it may run concurrently with a step that reads the current
+ * window -- on another stream, after the previous step completes (which read
+ * the slots this append overwrites) and before the next step starts -- and a
+ * producer may write a chunk into the slots rtr_kv_next_slots reports before
+ * the step that reads the chunk. */
+int rtr_kv_create_slots(rtr_kv_cache **out, void *k_ring, void *v_ring, void *k_ref, void *v_ref,
+                        int32_t window_frames, int32_t ring_slots, int32_t ref_capacity_frames,
+                        int64_t tokens_per_frame, int32_t H, int32_t d, rtr_dtype dtype);
 int rtr_kv_destroy(rtr_kv_cache *kv);
 
 /* Commit n_frames newly generated frames, given as [n_frames, k, H, d] device
  * buffers k_new, v_new (Key Designs 4: appended in order; once the window is
  * full each append evicts the oldest frame; the reference slot is never
  * touched).  Only the newest min(n_frames, W) frames are copied; the copy is
- * enqueued on `stream`.  n_frames == 0 is a no-op. */
+ * enqueued on `stream`.  n_frames == 0 is a no-op.  With ring_slots = W the
+ * copy overwrites the evicted frames' slots, which a step of the current
+ * window reads: enqueue it after that step (same stream, or after it
+ * completes). */
 int rtr_kv_append_evict(rtr_kv_cache *kv, const void *k_new, const void *v_new,
                         int32_t n_frames, rtr_stream stream);
 
 /* Physical ring slots the next n_frames appends would be written to, in
  * order; frames that the same append would evict again get -1.  Changes
  * nothing.  Lets a producer write K/V straight into the ring (zero-copy
- * append).  Order: once the window is full these are the slots of the oldest
- * frames, which every step until the commit still reads, so the producer
- * writes them only after the last step that reads the current window is
- * enqueued, on the same stream (or after it completes).  While the window has
- * free slots, the slots it reports are not read by any step, and a chunk may
- * be written there first and passed to the step as its k, v.  A step whose q,
- * k or v overlaps a slot in use or the reference returns RTR_EINVAL. */
+ * append).  Order: once the window is full and ring_slots < W + n_frames,
+ * some of these are slots of the oldest frames, which every step until the
+ * commit still reads, so the producer writes them only after the last step
+ * that reads the current window is enqueued, on the same stream (or after it
+ * completes).  Slots outside the window (while it has free slots, or the
+ * spare slots of a ring_slots > W cache) are not read by any step, and a
+ * chunk may be written there first and passed to the step as its k, v.  A
+ * step whose q, k or v overlaps a slot in use or the reference returns
+ * RTR_EINVAL. */
 int rtr_kv_next_slots(const rtr_kv_cache *kv, int32_t n_frames, int32_t *slots);
 
 /* Metadata-only commit of n_frames frames that the caller has already written
@@ -365,7 +386,8 @@ int rtr_kv_set_ref_rope(rtr_kv_cache *kv, void *k_ref_view, int32_t rope_pairs, 
                         int64_t position_offset);
 
 /* Metadata snapshot / restore (checkpoint-resume).  set_state validates the
- * snapshot against the cache's W and R_cap and changes nothing on error. */
+ * snapshot against the cache's W, ring slots and R_cap and changes nothing on
+ * error. */
 int rtr_kv_get_state(const rtr_kv_cache *kv, rtr_kv_state *out);
 int rtr_kv_set_state(rtr_kv_cache *kv, const rtr_kv_state *in);
 

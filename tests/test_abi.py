@@ -105,11 +105,11 @@ def test_block_causal_empty_is_noop():
     assert _attn(T=0, q=None, k=None, v=None, o=None) == rtr.RTR_OK
 
 
-def _cache(W=4, R=1, kpf=8, H=2, d=64, dtype=rtr.RTR_BF16):
+def _cache(W=4, R=1, kpf=8, H=2, d=64, dtype=rtr.RTR_BF16, N=None):
     fb = kpf * H * d * (2 if dtype == rtr.RTR_BF16 else 4)
     base = FAKE
     return rtr.KVCache(base, base + 64 * fb + 4096, base + 128 * fb + 8192,
-                       base + 130 * fb + 12288, W, R, kpf, H, d, dtype)
+                       base + 130 * fb + 12288, W, R, kpf, H, d, dtype, ring_slots=N)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -118,6 +118,8 @@ def _cache(W=4, R=1, kpf=8, H=2, d=64, dtype=rtr.RTR_BF16):
     (dict(R=rtr.RTR_MAX_REF + 1), rtr.RTR_EUNSUPPORTED),
     (dict(kpf=0), rtr.RTR_EINVAL),
     (dict(d=80), rtr.RTR_EUNSUPPORTED),
+    (dict(W=4, N=3), rtr.RTR_EUNSUPPORTED),             # fewer ring slots than window frames
+    (dict(W=4, N=rtr.RTR_MAX_WINDOW + 1), rtr.RTR_EUNSUPPORTED),
 ])
 def test_create_rejects(args, code):
     with pytest.raises(rtr.RtrError) as e:
@@ -198,23 +200,29 @@ def _check_against(kv, ref):
     assert s["next_frame_id"] == ref.next_frame_id
     assert s["ref_frames"] == ref.ref_frames()
     assert s["ref_generation"] == ref.ref_generation
-    W = s["window_frames"]
-    # physical slots: distinct, in range, a ring walk from head
+    N = s["ring_slots"]
+    # physical slots: distinct, in range, a ring walk from head over the N slots
     assert len(set(s["slot"])) == len(s["slot"])
-    assert all(0 <= x < max(W, 1) for x in s["slot"])
-    assert s["slot"] == [(s["head"] + p) % W for p in range(s["count"])] if W else s["slot"] == []
+    assert all(0 <= x < max(N, 1) for x in s["slot"])
+    assert s["slot"] == [(s["head"] + p) % N for p in range(s["count"])] if N else s["slot"] == []
 
 
-@settings(max_examples=200, deadline=None)
-@given(W=st.integers(0, 7), ops=st.lists(_op, max_size=40))
-def test_ring_metadata_matches_listkv(W, ops):
-    kv = _cache(W=W)
+@settings(max_examples=300, deadline=None)
+@given(W=st.integers(0, 7), spare=st.integers(0, 3), ops=st.lists(_op, max_size=40))
+def test_ring_metadata_matches_listkv(W, spare, ops):
+    """The window (ids, order, eviction) follows the list oracle for any number
+    of ring slots N = W + spare; an append of at most `spare` frames writes no
+    slot of the window before it, so it can run beside a step of that window."""
+    kv = _cache(W=W, N=W + spare)
     ref = ListKV(W)
     z = np.zeros((1, 1, 1, 1))
     for op in ops:
         if op[0] == "append":
             n = op[1]
+            before = set(_state(kv)["slot"])
             predicted = rtr.rtr_kv_next_slots(kv, n)
+            if n <= spare:
+                assert not before & {p for p in predicted if p >= 0}
             rtr.rtr_kv_commit_inplace(kv, n)
             ref.append(np.zeros((n, 1, 1, 1)), np.zeros((n, 1, 1, 1)))
             s = _state(kv)
@@ -245,19 +253,25 @@ def test_ring_matches_hand_schedule_file():
         assert (s["ref_generation"] if s["ref_frames"] else 0) == ref_gen
 
 
-def test_state_roundtrip_resume():
-    a = _cache(W=5)
+@pytest.mark.parametrize("N", [5, 8])
+def test_state_roundtrip_resume(N):
+    a = _cache(W=5, N=N)
     rtr.rtr_kv_commit_inplace(a, 7)
     rtr.rtr_kv_reset_ref(a, rtr.RTR_REF_REPLACE, None, None, 1, 2)
     rtr.rtr_kv_commit_inplace(a, 4)
     snap = rtr.rtr_kv_get_state(a)
-    b = _cache(W=5)
+    b = _cache(W=5, N=N)
     rtr.rtr_kv_set_state(b, snap)
     for kv in (a, b):
         rtr.rtr_kv_commit_inplace(kv, 3)
         rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_CLEAR, None, None, 1, 1)
         rtr.rtr_kv_commit_inplace(kv, 2)
     assert _state(a) == _state(b)
+    # a snapshot of a cache with other ring slots is refused
+    c = _cache(W=5, N=13 - N)
+    with pytest.raises(rtr.RtrError) as e:
+        rtr.rtr_kv_set_state(c, snap)
+    assert e.value.code == rtr.RTR_ESTATE
 
 
 def _bwd(**kw):
@@ -477,3 +491,30 @@ def test_step_rejects_a_chunk_in_a_slot_the_window_uses():
     assert step(k=k_ring + 2 * fb) == rtr.RTR_EINVAL
     assert step(k=k_ring) == rtr.RTR_EINVAL
     assert _sbwd(kv, v=v_ring + 2 * fb) == rtr.RTR_EINVAL
+
+
+def test_spare_ring_slots_take_a_chunk_before_its_step():
+    """With ring slots beyond the window, the slots the next append takes are
+    outside the full window, so a producer may write a chunk there and pass it
+    to the step that reads it; the window's own slots are still refused
+    (before anything is launched: these calls carry no device memory)."""
+    W, N, kpf, H, d = 3, 5, 8, 2, 128
+    fb = kpf * H * d * 2
+    kv = _cache(W=W, R=1, kpf=kpf, H=H, d=d, N=N)
+    L = rtr.lib()
+    h = kv.handle
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, None, None, 1, -1)
+    rtr.rtr_kv_commit_inplace(kv, 4)                      # full window: frames in slots 1, 2, 3
+    assert _state(kv)["slot"] == [1, 2, 3]
+    assert list(rtr.rtr_kv_next_slots(kv, 2)) == [4, 0]   # the spare slots, not the window's
+    k_ring, v_ring = FAKE, FAKE + 64 * fb + 4096
+    far = FAKE + 900 * MB
+
+    def step(k, v, C):
+        return L.rtr_attn_stream_step(h, far, k, v, far + 3 * MB, None, C, 0, 0.0, None, 0, None)
+
+    # (a chunk in the spare slots passes these checks; tests/test_gpu_zero_copy.py runs such steps)
+    assert step(k_ring + 1 * fb, v_ring + 4 * fb, 1) == rtr.RTR_EINVAL      # slot 1 is in use
+    assert step(k_ring + 4 * fb, v_ring + 3 * fb, 1) == rtr.RTR_EINVAL      # slot 3 is in use
+    rtr.rtr_kv_commit_inplace(kv, 2)
+    assert _state(kv)["slot"] == [3, 4, 0]

@@ -24,13 +24,14 @@ from tests.gpu_util import assert_bf16_close, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def _run(kpf, H, W, C, n_chunks, wid):
+def _run(kpf, H, W, C, n_chunks, wid, N=None):
     d = 128
-    kr = torch.zeros((W, kpf, H, d), dtype=torch.bfloat16, device="cuda")
+    N = W if N is None else N
+    kr = torch.zeros((N, kpf, H, d), dtype=torch.bfloat16, device="cuda")
     vr = torch.zeros_like(kr)
     kf = torch.zeros((1, kpf, H, d), dtype=torch.bfloat16, device="cuda")
     vf = torch.zeros_like(kf)
-    kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, 1, kpf, H, d, rtr.RTR_BF16)
+    kv = rtr.rtr_kv_create_slots(kr, vr, kf, vf, W, N, 1, kpf, H, d, rtr.RTR_BF16)
     ref = ListKV(W)
     rk = gen.normal((1, kpf, H, d), "bf16", 0, wid, 0, gen.TAG_REFK)
     rv = gen.normal((1, kpf, H, d), "bf16", 0, wid, 0, gen.TAG_REFV)
@@ -97,3 +98,11 @@ def test_zero_copy_append_two_frame_chunks():
 def test_zero_copy_append_wan_shape():
     staged, after = _run(kpf=1560, H=12, W=6, C=3, n_chunks=4, wid=302)
     assert staged >= 1 and after >= 1
+
+
+def test_zero_copy_append_spare_slots_write_before_every_step():
+    """A ring with C spare slots (rtr_kv_create_slots): once the window is full,
+    the slots the next append takes are still outside it, so every chunk is
+    written into the ring before its step and read from there."""
+    staged, after = _run(kpf=96, H=2, W=4, C=2, n_chunks=8, wid=303, N=6)
+    assert staged == 8 and after == 0
