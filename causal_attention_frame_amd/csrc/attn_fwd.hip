@@ -928,9 +928,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
                 if (base + 4 > ntiles) break;
                 idle(base + 4, I4{});
             }
-            __builtin_amdgcn_s_waitcnt(wait_vm(0));
-            compiler_fence();
-            return;
+            return;  // look-ahead tiles still in flight: see drain()
         }
         if (first_sweep) {
 #pragma unroll
@@ -1000,7 +998,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
             if (base + 4 > ntiles) break;
             step(base + 4, I4{}, std::true_type{}, maxonly, PC{});
         }
-        // drain the look-ahead tiles before the stages are reused
+        // The look-ahead tiles past the last one may still be in flight here;
+        // drain() waits for them before the stages are reused or the wave
+        // ends, so that their latency overlaps the epilogue.
+    };
+    auto drain = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
         compiler_fence();
     };
@@ -1020,7 +1022,9 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(sRedo)) {
         asm volatile("");
+        drain();
         sweep(false, std::true_type{});  // exact row maxima
+        drain();
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
@@ -1068,6 +1072,7 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128(const KArgs a) {
         }
     }
     if (g == 0 && a.lse && qv[0]) a.lse[(long)head * a.Tq + qi[0]] = mref[0] / kLog2e + logf(lt);
+    drain();
 }
 
 // Work decomposition of the head_dim-128 kernel.  A unit is one (head, query
