@@ -90,6 +90,9 @@ struct BArgs {
     // part[p][key][head][2][128], summed in piece order by attn_bwd_reduce.
     int32_t nsplit, tpp;
     float *part;
+    // Row groups of the dQ launch (its GMAP instance; RowGroups): groups per
+    // frame, frames, and workgroups per frame pair.
+    int32_t wpf, nframes, w1;
 };
 
 constexpr int kD = 128;
@@ -554,9 +557,15 @@ void attn_bwd_dkdv_d128(const BArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per 256 query rows.  SEG: keys through the segment table
-// (streaming step), otherwise one contiguous [T, H, 128] block.
+// (streaming step), otherwise one contiguous [T, H, 128] block.  GMAP 0: wave
+// w of block qb takes rows 256 qb + 32 w .. + 31; GMAP 2 (one-round launches
+// with several frames): 32-row groups aligned to frames, frame f paired with
+// frame F-1-f, so that each SIMD (waves w and w + 4) holds an early and a late
+// group (RowGroups).  A wave whose rows all lie before a key tile skips its
+// products from there on (it still loads its share of the tiles and meets the
+// barriers).
 // ---------------------------------------------------------------------------
-template <bool SEG>
+template <bool SEG, int GMAP>
 __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     constexpr int NS = 8, NT = 4, NSTG = 4;
     __shared__ __attribute__((aligned(16))) uint16_t sK[NSTG * kTile];
@@ -575,13 +584,50 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     __shared__ int sMap[2];
     int head, qb;
     xcd_order_shared(blockIdx.x, a.nwg, a.nqb, head, qb, sMap);
-    const int q0 = qb * 256;
     const long hoff = (long)head * kD;
-    const int qi = q0 + 32 * wave + n;
-    const bool qv = qi < a.T;
     auto key_limit = [&](int i) __attribute__((always_inline)) {
         return (int)min((long)a.prefix + (long)(i / a.kpf + 1) * a.kpf, (long)a.Tk);
     };
+    // first row and row count (0: none) of wave w's group
+    auto wave_rows = [&](int w, int &r0, int &nr) __attribute__((always_inline)) {
+        r0 = 0;
+        nr = 0;
+        if constexpr (GMAP == 0) {
+            r0 = 256 * qb + 32 * w;
+            nr = min(32, a.T - r0);
+        } else {
+            // blocks counted from the last one, as in the forward kernel
+            const int np = a.nframes >> 1, b = a.nqb - 1 - qb;
+            int f, j;
+            if (b < np * a.w1) {
+                const int fp = b / a.w1, q = b - fp * a.w1;
+                f = w < 4 ? fp : a.nframes - 1 - fp;
+                j = 4 * q + (w & 3);
+            } else {
+                f = np;
+                j = 8 * (b - np * a.w1) + w;
+            }
+            if (j < a.wpf) {
+                r0 = f * a.kpf + 32 * j;
+                nr = min(min(32, a.kpf - 32 * j), a.T - r0);
+            }
+        }
+        nr = max(nr, 0);
+    };
+    int r0w, nrw;
+    wave_rows(wave, r0w, nrw);
+    const int qi = r0w + n;
+    const bool qv = n < nrw;
+    // Key limits grow with the row: a wave's largest is its last row's, the
+    // block's the largest over its waves.
+    const int lim_wave = nrw > 0 ? key_limit(r0w + nrw - 1) : 0;
+    int lim_blk = 0;
+#pragma unroll 1
+    for (int w = 0; w < 8; ++w) {
+        int r0, nr;
+        wave_rows(w, r0, nr);
+        if (nr > 0) lim_blk = max(lim_blk, key_limit(r0 + nr - 1));
+    }
     if (SEG) {
         for (int f = tid; f < a.nseg; f += 512) {
             sSegK[f] = (const uint16_t *)a.kseg[f];
@@ -590,10 +636,9 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
         __syncthreads();
     }
     const int lim = key_limit(qv ? qi : a.T - 1);
-    const int lim_lo = key_limit(q0);
-    const int lim_hi = key_limit(min(q0 + 255, a.T - 1));
-    const int ntiles = (lim_hi + 31) / 32;
-    const int nfull = min(ntiles, lim_lo / 32);  // tiles every row of the block sees whole
+    const int ntiles = (lim_blk + 31) / 32;
+    // tiles every row of this wave sees whole (none for a wave without rows)
+    const int nfull = nrw > 0 ? min(ntiles, key_limit(r0w) / 32) : 0;
 
     // Q and dO as B operands: lane (n, g) holds row qi, columns 16 s + 8 g .. + 7.
     bf16x8 qf[NS], df[NS];
@@ -678,6 +723,15 @@ __global__ __launch_bounds__(512) void attn_bwd_dq_d128(const BArgs a) {
     auto iter = [&](int j, auto S, auto masked) __attribute__((always_inline)) {
         constexpr int st = decltype(S)::value, st1 = (st + 1) % NSTG;
         constexpr bool MASK = decltype(masked)::value;
+        if (MASK && j * 32 >= lim_wave) {
+            // tile j and later lie past every row of this wave (P = 0): only
+            // the loads and the barrier (masked loop only, so that the
+            // unmasked iterations stay one basic block)
+            __builtin_amdgcn_s_waitcnt(wait_vm(2));
+            lds_barrier();
+            issue(j + 3, std::integral_constant<int, (st + 3) % NSTG>{});
+            return;
+        }
 
         // Phase 1: dP^T = V dO^T under P = exp2(s c - LSE2).
         f32x16 dp = {};
@@ -910,11 +964,25 @@ hipError_t launch_attention_bwd(const BwdProblem &p, hipStream_t stream) {
         hipLaunchKernelGGL(attn_bwd_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, a);
         if (hipError_t e = hipGetLastError()) return e;
     }
+    // dQ: the row mapping of the forward launch over the same rows and keys
+    RowGroups rg{};
+    if (const hipError_t e = plan_row_groups(a.T, a.Tk, a.kpf, a.prefix, p.H, &rg)) return e;
+    a.nqb = rg.nqb;
+    a.wpf = rg.wpf;
+    a.nframes = rg.nframes;
+    a.w1 = rg.w1;
     a.nwg = p.H * a.nqb;
-    if (seg)
-        hipLaunchKernelGGL(attn_bwd_dq_d128<true>, dim3(a.nwg), dim3(512), 0, stream, a);
-    else
-        hipLaunchKernelGGL(attn_bwd_dq_d128<false>, dim3(a.nwg), dim3(512), 0, stream, a);
+    if (rg.gm == 2) {
+        if (seg)
+            hipLaunchKernelGGL((attn_bwd_dq_d128<true, 2>), dim3(a.nwg), dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_bwd_dq_d128<false, 2>), dim3(a.nwg), dim3(512), 0, stream, a);
+    } else {
+        if (seg)
+            hipLaunchKernelGGL((attn_bwd_dq_d128<true, 0>), dim3(a.nwg), dim3(512), 0, stream, a);
+        else
+            hipLaunchKernelGGL((attn_bwd_dq_d128<false, 0>), dim3(a.nwg), dim3(512), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -2190,6 +2190,28 @@ hipError_t attention_workspace_bytes(int32_t d, rtr_dtype in_dtype, size_t *byte
     return hipSuccess;
 }
 
+hipError_t plan_row_groups(int64_t Tq, int64_t Tk, int64_t kpf, int64_t prefix, int32_t H, RowGroups *out) {
+    int cu = 0;
+    if (const hipError_t e = cu_count(&cu)) return e;
+    KArgs k{};
+    k.Tq = (int32_t)Tq;
+    k.Tk = (int32_t)Tk;
+    k.kpf = (int32_t)kpf;
+    k.prefix = (int32_t)prefix;
+    double steps = 0.0;
+    int gm = plan_rows(k, H, cu, &steps);
+    if (gm != 2) {  // blocks of consecutive rows (GMAP 1 has no counterpart here)
+        gm = 0;
+        k.nqb = (int32_t)((Tq + 255) / 256);
+    }
+    out->gm = gm;
+    out->nqb = k.nqb;
+    out->wpf = k.wpf;
+    out->nframes = k.nframes;
+    out->w1 = k.w1;
+    return hipSuccess;
+}
+
 hipError_t launch_attention(const AttnProblem &p, hipStream_t stream) {
     KArgs k{};
     k.q = p.q;

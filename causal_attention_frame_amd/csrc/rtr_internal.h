@@ -83,6 +83,20 @@ struct BwdProblem {
     bool cross = false;
 };
 
+// Row groups of a launch of 256-row workgroups (8 waves x 32 rows) over Tq
+// query rows of H heads whose key limits follow the frame mask (as in
+// AttnProblem): gm 0 = blocks of 256 consecutive rows; gm 2 = 32-row groups
+// aligned to frames, frame f paired with frame F-1-f in each workgroup (waves
+// 0-3 the early frame's groups, 4-7 the late frame's), the middle frame of an
+// odd F in blocks of 8 groups.  gm 2 is chosen only for launches of one round
+// on the compute units where it shortens the estimated longest block.  nqb is
+// the workgroups per head, wpf the groups per frame, w1 the workgroups per
+// frame pair.
+struct RowGroups {
+    int32_t gm = 0, nqb = 0, wpf = 0, nframes = 0, w1 = 0;
+};
+hipError_t plan_row_groups(int64_t Tq, int64_t Tk, int64_t kpf, int64_t prefix, int32_t H, RowGroups *out);
+
 hipError_t attention_bwd_workspace_bytes(int64_t T, int32_t H, size_t *bytes);
 // Workspace of the cross-attention backward over Tq rows and n text keys:
 // the above plus, when the text key blocks are split over the rows, their

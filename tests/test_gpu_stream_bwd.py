@@ -178,3 +178,21 @@ def test_stream_bwd_through_a_rollout():
         rtr.rtr_kv_append_evict(kv, dev(x["k"]).view(C, kpf, H, D), dev(x["v"]).view(C, kpf, H, D), C)
         ref.append(x["k"].values.reshape(C, kpf, H, D), x["v"].values.reshape(C, kpf, H, D))
     kv.close()
+
+
+def test_stream_bwd_wan13b_every_element():
+    """The timed backward workload (Wan-1.3B layer: 12 heads, 1,560-token
+    frames, a 3-frame chunk over the reference and a full 6-frame window):
+    every element of dQ, dK, dV and of the cache gradients against the dense
+    oracle.  One launch of the dQ kernel covers the whole chunk here, so its
+    workgroups take frame-paired row groups (frame 0 with frame 2, frame 1 on
+    its own) and waves whose rows end before a key tile skip its products."""
+    kpf, H, W, R, C = 1560, 12, 6, 1, 3
+    print(f"kpf={kpf} H={H} W={W} R={R} C={C}", flush=True)
+    kv, ref = _cache(kpf, H, W, R)
+    _fill(kv, ref, kpf, H, R, W, seed=21)
+    x, do, got = _step(kv, kpf, H, C, 1, seed=22, cache_grads=True)
+    pk, pv = ref.prefix(kpf, H, D)
+    r = attn_stream_step_bwd(pk, pv, x["q"].values, x["k"].values, x["v"].values, do.values, kpf)
+    _compare(got, r, True, "Wan-1.3B step")
+    kv.close()
