@@ -334,6 +334,9 @@ def main():
                          "on a second stream beside the step that reads the window (default: the "
                          "commit after the step on the same stream, over a ring of W slots; faster "
                          "here, since the chip runs the step at its power limit)")
+    ap.add_argument("--tokens-per-frame", type=int, default=0,
+                    help="streaming forward workloads: tokens per latent frame instead of the workload's "
+                         "(e.g. 2080 = 40x52 patches of an 832x640 frame, a sensitivity run)")
     ap.add_argument("--split", action="store_true",
                     help="split-K schedule with a workspace (default: one workgroup per "
                          "(head, query block), the faster schedule on these shapes)")
@@ -361,9 +364,11 @@ def main():
     if args.workload in ("wan13b_cross_step", "wan13b_cross_step_bwd"):
         return cross(args, w, dev)
 
+    if args.tokens_per_frame:
+        w = dict(w, k=args.tokens_per_frame)
     f32 = args.dtype == "f32"
-    if (f32 or args.head_dim) and not args.workload.endswith("stream_step"):
-        sys.exit("--dtype f32 and --head-dim apply to the streaming forward workloads")
+    if (f32 or args.head_dim or args.tokens_per_frame) and not args.workload.endswith("stream_step"):
+        sys.exit("--dtype f32, --head-dim and --tokens-per-frame apply to the streaming forward workloads")
 
     def to_dev(t):
         if f32:

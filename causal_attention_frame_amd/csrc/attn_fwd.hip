@@ -69,6 +69,11 @@ struct KArgs {
     int32_t nspare;
     int32_t tail_total;
     int32_t piece;
+    // Overflow split (nxqb > 0, units beyond the workgroups): query blocks qb
+    // < nxqb of every head have no main, all their tiles are tail pieces, and
+    // every workgroup takes its share of the pieces after its main, which
+    // covers a whole unit.
+    int32_t nxqb;
     // Row groups of the plain head_dim-128 kernel (its GMAP instance, picked
     // by plan_rows): 32-row groups per head (GMAP 1), or groups per frame,
     // frames and blocks per frame pair (GMAP 2).
@@ -1105,15 +1110,27 @@ __device__ inline int block_tiles(int qb, const KArgs &a) {
 
 // Tail pieces of unit u.
 __device__ inline int unit_pieces(int u, const KArgs &a) {
-    const int r = block_tiles(u % a.nqb, a) - a.cut;
+    const int qb = u % a.nqb;
+    if (a.nxqb > 0) return qb < a.nxqb ? (block_tiles(qb, a) + a.piece - 1) / a.piece : 0;
+    const int r = block_tiles(qb, a) - a.cut;
     return r > 0 ? (r + a.piece - 1) / a.piece : 0;
 }
 
-// sPre[u] = tail pieces of units 0 .. u-1 (u = 0 .. U), built by the first 256
-// threads of the workgroup, one unit each; every thread takes the barriers.
+// Units that can have tail pieces, in unit order: every unit, or with an
+// overflow split the nxqb first query blocks of each head.
+__device__ inline int piece_units(const KArgs &a) {
+    return a.nxqb > 0 ? (a.units / a.nqb) * a.nxqb : a.units;
+}
+__device__ inline int piece_unit(int pu, const KArgs &a) {
+    return a.nxqb > 0 ? (pu / a.nxqb) * a.nqb + pu % a.nxqb : pu;
+}
+
+// sPre[i] = tail pieces of piece units 0 .. i-1 (i = 0 .. piece_units), built
+// by the first 256 threads of the workgroup, one unit each; every thread takes
+// the barriers.
 __device__ __forceinline__ void build_piece_prefix(const KArgs &a, int *sPre, int *sTmp) {
     const int tid = threadIdx.x;
-    if (tid < 256) sTmp[tid] = tid < a.units ? unit_pieces(tid, a) : 0;
+    if (tid < 256) sTmp[tid] = tid < piece_units(a) ? unit_pieces(piece_unit(tid, a), a) : 0;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {  // inclusive scan
         const int v = (tid < 256 && tid >= off) ? sTmp[tid - off] : 0;
@@ -1142,9 +1159,15 @@ __device__ inline int find_tail_unit(const int *sPre, int U, int x) {
 // share that XCD's L2), and its remaining workgroups are spares.
 __device__ inline void split_role(int b, const KArgs &a, int &unit, int &spare) {
     const int x = b & 7, i = b >> 3;
-    const int ulo = x * a.units / 8, un = (x + 1) * a.units / 8 - ulo;
     unit = -1;
     spare = -1;
+    if (a.nxqb > 0) {  // overflow split: the mains are the units of query blocks >= nxqb
+        const int per = a.nqb - a.nxqb, um = (a.units / a.nqb) * per;
+        const int mlo = x * um / 8, mn = (x + 1) * um / 8 - mlo;
+        if (i < mn) unit = (mlo + i) / per * a.nqb + a.nxqb + (mlo + i) % per;
+        return;
+    }
+    const int ulo = x * a.units / 8, un = (x + 1) * a.units / 8 - ulo;
     if (i < un) {
         unit = ulo + i;
         return;
@@ -1677,22 +1700,35 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     // spare its share of the tail pieces.
     int unit, spare;
     split_role(blockIdx.x, a, unit, spare);
+    const bool ovf = a.nxqb > 0;
     auto run_tail = [&](int k) __attribute__((always_inline)) {
-        const int u = __builtin_amdgcn_readfirstlane(find_tail_unit(sPre, a.units, k));
-        const int i = k - __builtin_amdgcn_readfirstlane(sPre[u]);
+        const int pu = __builtin_amdgcn_readfirstlane(find_tail_unit(sPre, piece_units(a), k));
+        const int i = k - __builtin_amdgcn_readfirstlane(sPre[pu]);
+        const int u = piece_unit(pu, a);
         const int head = u / a.nqb, qb = u - head * a.nqb;
-        const int tb = a.cut + i * a.piece;
+        const int tb = (ovf ? 0 : a.cut) + i * a.piece;
         const int te = min(block_tiles(qb, a), tb + a.piece);
-        do_piece(head, qb, tb, te, a.units + k);
+        do_piece(head, qb, tb, te, (ovf ? 0 : a.units) + k);
     };
     if (unit >= 0) {
         const int head = unit / a.nqb, qb = unit - head * a.nqb;
         const int nt = block_tiles(qb, a);
         do_piece(head, qb, 0, min(nt, a.cut), nt > a.cut ? unit : -1);
-        return;
+        if (!ovf) return;
     }
-    const int k0 = (int)((long)spare * a.tail_total / a.nspare);
-    const int k1 = (int)((long)(spare + 1) * a.tail_total / a.nspare);
+    int k0, k1;
+    if (ovf) {
+        // every workgroup, after its main: XCD x takes pieces [x K / 8, (x +
+        // 1) K / 8) (head-major, so mostly the heads of its own mains), split
+        // evenly over its workgroups
+        const int x = blockIdx.x & 7, i = blockIdx.x >> 3, nx = (a.nprog - x + 7) / 8;
+        const int xlo = (int)((long)x * a.tail_total / 8), xn = (int)((long)(x + 1) * a.tail_total / 8) - xlo;
+        k0 = xlo + i * xn / nx;
+        k1 = xlo + (i + 1) * xn / nx;
+    } else {
+        k0 = (int)((long)spare * a.tail_total / a.nspare);
+        k1 = (int)((long)(spare + 1) * a.tail_total / a.nspare);
+    }
 #pragma unroll 1
     for (int k = k0; k < k1; ++k) run_tail(k);
 }
@@ -1717,8 +1753,10 @@ __global__ __launch_bounds__(256) void attn_combine_d128(const KArgs a) {
         const int qb_pieces = unit_pieces(b, a);
         k0 += qb_pieces * head + (b < qb ? qb_pieces : 0);
     }
-    const int npieces = 1 + q;
-    auto slot_of = [&](int k) { return k == 0 ? u : a.units + k0 + k - 1; };
+    // with an overflow split the unit has no main: its pieces are slots k0 ..
+    const bool ovf = a.nxqb > 0;
+    const int npieces = ovf ? q : 1 + q;
+    auto slot_of = [&](int k) { return ovf ? k0 + k : (k == 0 ? u : a.units + k0 + k - 1); };
     const int row = part * RP + tid / 8, c0 = 16 * (tid % 8);
     const int qrow = qb * BM + row;
 
@@ -1942,6 +1980,51 @@ bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, double plai
     return ok;
 }
 
+// Overflow split, for U units just beyond one round of G workgroups (U <=
+// 1.5 G): the nx = ceil((U - G) / H) first query blocks of every head (the
+// lightest under the frame mask) have no main; the others run whole on one
+// workgroup each, and every workgroup then takes its share of the extra
+// blocks' key tiles, cut into pieces of P tiles.  The plain launch would run
+// the extra blocks as a second round after the first compute units free up.
+// Costs as for plan_split; taken when predicted at least 10 % shorter.
+bool plan_overflow(const KArgs &k, int64_t H, int64_t G, int64_t max_slots, SplitPlan *out, int32_t *nxqb) {
+    const int64_t nqb = k.nqb, U = nqb * H;
+    if (U <= G || 2 * U > 3 * G) return false;
+    const int64_t nx = (U - G + H - 1) / H;
+    if (nx >= nqb || nx * H > kMaxSplitUnits) return false;
+    const int64_t um = U - nx * H;
+    for (int64_t x = 0; x < 8; ++x)  // every XCD has a workgroup for each of its mains
+        if ((x + 1) * um / 8 - x * um / 8 > (G - x + 7) / 8) return false;
+    int64_t nmax = 0, nmin_main = INT64_MAX, next_max = 0;
+    for (int64_t qb = 0; qb < nqb; ++qb) {
+        const int64_t t = host_block_tiles(qb, k);
+        if (qb >= nx) {
+            nmax = std::max(nmax, t);
+            nmin_main = std::min(nmin_main, t);
+        } else {
+            next_max = std::max(next_max, t);
+        }
+    }
+    const double plain = (double)std::max(nmax, nmin_main + next_max);
+    double best = plain * kSplitMargin;
+    bool ok = false;
+    for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512}) {
+        int64_t K = 0;
+        for (int64_t qb = 0; qb < nx; ++qb) K += H * ((host_block_tiles(qb, k) + P - 1) / P);
+        if (K > max_slots) continue;
+        const int64_t per = (K + G - 1) / G;  // pieces of the busiest workgroup
+        const double mk = (double)nmax + kPieceOverheadTiles + (double)per * (kSpareTileCost * P + kPieceOverheadTiles) +
+                          kMergeTilesPerSlot * (double)K;
+        if (mk < best) {
+            best = mk;
+            ok = true;
+            *out = SplitPlan{1 << 30, P, (int32_t)K};
+            *nxqb = (int32_t)nx;
+        }
+    }
+    return ok;
+}
+
 // Compute units of the current device, cached per device.
 hipError_t cu_count(int *out) {
     static std::atomic<int> cache[64];
@@ -2133,9 +2216,9 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
         double plain_steps = 0.0;
         const int gm = plan_rows(kp, p.H, cu, &plain_steps);
         const int64_t U = (int64_t)k.nqb * p.H;
-        if (p.ws && U < kMaxSplitUnits) {
-            const int64_t G = std::min<int64_t>(cu, kMaxSplitUnits);
-            bool fit = G > U;  // every XCD has a workgroup for each of its mains
+        const int64_t G = std::min<int64_t>(cu, kMaxSplitUnits);
+        if (p.ws && U < G) {
+            bool fit = true;  // every XCD has a workgroup for each of its mains
             for (int64_t x = 0; fit && x < 8; ++x) fit = (x + 1) * U / 8 - x * U / 8 <= (G - x + 7) / 8;
             SplitPlan plan{};
             const int64_t max_slots = p.ws_slots > 0 ? std::min<int64_t>(p.ws_slots, 2 * G) : 2 * G;
@@ -2147,6 +2230,20 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
                 k.nspare = (int32_t)(G - U);
                 k.tail_total = plan.pieces;
                 k.piece = plan.piece;
+            }
+        } else if (p.ws && U > G) {
+            const int64_t max_slots = p.ws_slots > 0 ? std::min<int64_t>(p.ws_slots, 2 * G) : 2 * G;
+            SplitPlan plan{};
+            int32_t nx = 0;
+            if (plan_overflow(k, p.H, G, max_slots, &plan, &nx)) {
+                k.ws = (float *)p.ws;
+                k.nprog = (int32_t)G;
+                k.units = (int32_t)U;
+                k.cut = plan.cut;
+                k.nspare = 0;
+                k.tail_total = plan.pieces;
+                k.piece = plan.piece;
+                k.nxqb = nx;
             }
         }
         const bool fast = k.seg_len >= 32 && k.seg_len % 4 == 0;

@@ -266,7 +266,9 @@ def _sample_rows(Tq, kpf, n_rand, seed):
 
 
 def _stream_workload(name, seed=0):
-    w = gen.WORKLOADS[name]
+    """A streaming workload by name; a `_k<N>` suffix sets N tokens per frame."""
+    base, _, k = name.partition("_k")
+    w = dict(gen.WORKLOADS[base], **({"k": int(k)} if k else {}))
     kpf, H, d, C, W, R = w["k"], w["H"], w["d"], w["C"], w["W"], w["R"]
     x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=seed, wid=w["wid"],
                           outlier_frac=w.get("outlier_frac", 0.0),
@@ -291,12 +293,14 @@ def _dense_stream_reference(name, x, w):
     return _DENSE[name]
 
 
-@pytest.mark.parametrize("name", ["wan13b_stream_step", "wan14b_stream_step"])
+@pytest.mark.parametrize("name", ["wan13b_stream_step", "wan14b_stream_step", "wan13b_stream_step_k2080"])
 @pytest.mark.parametrize("split", [False, True], ids=["plain", "split"])
 def test_full_size_stream_step_every_element(name, split):
     """The Wan-1.3B step and the Wan-14B step (1 % of key rows x8) at full
     size, every head and every row of O and LSE against the dense float64
-    oracle over [reference | window | chunk]."""
+    oracle over [reference | window | chunk]; also the Wan-1.3B step with
+    2,080-token frames (40 x 52 patches of an 832 x 640 frame), whose 288
+    workgroups take more than one round."""
     w, x, kv, bufs = _stream_workload(name)
     kpf, H, d, C = w["k"], w["H"], w["d"], w["C"]
     Tq = C * kpf
@@ -424,6 +428,42 @@ def test_split_runs_and_matches_plain_one_frame_chunk():
                                      rows, heads)
     assert_bf16_close(host(o2)[rows][:, heads], ro, "o")
     assert_bf16_close(host(l2)[heads][:, rows], rl, "lse")
+
+
+@pytest.mark.parametrize("kpf,C,H", [(700, 3, 30), (1000, 2, 35)])
+def test_overflow_split_runs_and_matches_oracle(kpf, C, H):
+    # Units (heads x 256-row blocks: 270 and 280) just beyond one round of the
+    # 256 compute units, behind a reference and a full 6-frame window: with a
+    # workspace the launch runs the heavier query blocks whole and cuts the
+    # first block of every head into pieces shared by all workgroups, so the
+    # workspace must be written; every element of O and LSE against the dense
+    # oracle, and against the plain launch within the split bars above.
+    d, W, R = 128, 6, 1
+    x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=7, wid=3)
+    kv, kr, vr, kf, vf = _make_cache(W, R, kpf, H, d, "bf16")
+    rtr.rtr_kv_reset_ref(kv, REF_REPLACE, dev(x["ref_k"]), dev(x["ref_v"]), R, -1)
+    rtr.rtr_kv_append_evict(kv, dev(x["ring_k"]), dev(x["ring_v"]), W)
+    q, k, v = dev(x["q"]), dev(x["k"]), dev(x["v"])
+    print(f"kpf={kpf} C={C} H={H}: units {(C * kpf + 255) // 256 * H}", flush=True)
+    o1, l1 = rtr.rtr_attn_stream_step(kv, q, k, v, C, want_lse=True, out_dtype=torch.float32)
+    ws, chk_w = _workspace(d)
+    ws.fill_(0xFF)
+    o2, chk_o = guarded_empty((C * kpf, H, d), torch.bfloat16)
+    l2, chk_l = guarded_empty((H, C * kpf), torch.float32)
+    rtr.rtr_attn_stream_step(kv, q, k, v, C, o=o2, lse=l2, workspace=ws)
+    torch.cuda.synchronize()
+    chk_w()
+    chk_o()
+    chk_l()
+    assert int((ws != 0xFF).sum()) > 0, "the split path did not run"
+    d_o = (o1 - o2.float()).abs()
+    assert float(d_o.max()) < 2e-2 and float(d_o.mean()) < 1e-3
+    assert float((l1 - l2).abs().max()) < 1e-3
+    pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
+    pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
+    ro, rl = oracle.attn_stream_step(pk, pv, x["q"].values, x["k"].values, x["v"].values, kpf)
+    assert_bf16_close(host(o2), ro, "o")
+    assert_bf16_close(host(l2), rl, "lse")
 
 
 def test_split_workspace_too_small_is_rejected():
