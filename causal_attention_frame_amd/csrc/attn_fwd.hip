@@ -72,8 +72,10 @@ struct KArgs {
     // Overflow split (nxqb > 0, units beyond the workgroups): query blocks qb
     // < nxqb of every head have no main, all their tiles are tail pieces, and
     // every workgroup takes its share of the pieces after its main, which
-    // covers a whole unit.
+    // covers a whole unit: workgroup b the pieces [pk[b], pk[b + 8]) (the end
+    // of its XCD's range when b + 8 is past the grid).
     int32_t nxqb;
+    int16_t pk[256];
     // Row groups of the plain head_dim-128 kernel (its GMAP instance, picked
     // by plan_rows): 32-row groups per head (GMAP 1), or groups per frame,
     // frames and blocks per frame pair (GMAP 2).
@@ -1719,12 +1721,11 @@ __global__ __launch_bounds__(512) void attn_fwd_bf16_d128_split(const KArgs a) {
     int k0, k1;
     if (ovf) {
         // every workgroup, after its main: XCD x takes pieces [x K / 8, (x +
-        // 1) K / 8) (head-major, so mostly the heads of its own mains), split
-        // evenly over its workgroups
-        const int x = blockIdx.x & 7, i = blockIdx.x >> 3, nx = (a.nprog - x + 7) / 8;
-        const int xlo = (int)((long)x * a.tail_total / 8), xn = (int)((long)(x + 1) * a.tail_total / 8) - xlo;
-        k0 = xlo + i * xn / nx;
-        k1 = xlo + (i + 1) * xn / nx;
+        // 1) K / 8) (head-major, so mostly the heads of its own mains), shared
+        // by its workgroups in order, lighter mains taking more (host plan)
+        const int b = blockIdx.x;
+        k0 = a.pk[b];
+        k1 = b + 8 < a.nprog ? a.pk[b + 8] : (int)((long)((b & 7) + 1) * a.tail_total / 8);
     } else {
         k0 = (int)((long)spare * a.tail_total / a.nspare);
         k1 = (int)((long)(spare + 1) * a.tail_total / a.nspare);
@@ -1983,45 +1984,128 @@ bool plan_split(const KArgs &k, int64_t H, int G, int64_t max_slots, double plai
 // Overflow split, for U units just beyond one round of G workgroups (U <=
 // 1.5 G): the nx = ceil((U - G) / H) first query blocks of every head (the
 // lightest under the frame mask) have no main; the others run whole on one
-// workgroup each, and every workgroup then takes its share of the extra
-// blocks' key tiles, cut into pieces of P tiles.  The plain launch would run
-// the extra blocks as a second round after the first compute units free up.
-// Costs as for plan_split; taken when predicted at least 10 % shorter.
-bool plan_overflow(const KArgs &k, int64_t H, int64_t G, int64_t max_slots, SplitPlan *out, int32_t *nxqb) {
-    const int64_t nqb = k.nqb, U = nqb * H;
-    if (U <= G || 2 * U > 3 * G) return false;
-    const int64_t nx = (U - G + H - 1) / H;
-    if (nx >= nqb || nx * H > kMaxSplitUnits) return false;
-    const int64_t um = U - nx * H;
-    for (int64_t x = 0; x < 8; ++x)  // every XCD has a workgroup for each of its mains
-        if ((x + 1) * um / 8 - x * um / 8 > (G - x + 7) / 8) return false;
-    int64_t nmax = 0, nmin_main = INT64_MAX, next_max = 0;
-    for (int64_t qb = 0; qb < nqb; ++qb) {
-        const int64_t t = host_block_tiles(qb, k);
-        if (qb >= nx) {
-            nmax = std::max(nmax, t);
-            nmin_main = std::min(nmin_main, t);
-        } else {
-            next_max = std::max(next_max, t);
-        }
+// workgroup each, and every workgroup then takes a contiguous run of the
+// extra blocks' key tiles, cut into pieces of P tiles: each XCD's pieces go to
+// its workgroups in order, as many as fit under a common finish time (found
+// by bisection), so that workgroups with lighter mains take more.  The plain
+// launch would run the extra blocks as a second round after the first compute
+// units free up.  Costs as for plan_split; taken when predicted at least 10 %
+// shorter.  Plans are kept per shape (fixed-size storage).
+bool plan_overflow(const KArgs &k, int64_t H, int64_t G, int64_t max_slots, SplitPlan *out, int32_t *nxqb,
+                   int16_t *pk) {
+    struct Entry {
+        int64_t key[7];
+        bool ok;
+        SplitPlan plan;
+        int32_t nx;
+        int16_t pk[kMaxSplitUnits];
+    };
+    constexpr int kCache = 16;
+    static std::mutex mu;
+    static Entry cache[kCache];
+    static int ncache = 0, next = 0;
+    const int64_t key[7] = {k.Tq, k.Tk, k.kpf, k.prefix, H, G, max_slots};
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < ncache; ++i)
+            if (std::equal(key, key + 7, cache[i].key)) {
+                *out = cache[i].plan;
+                *nxqb = cache[i].nx;
+                std::copy(cache[i].pk, cache[i].pk + kMaxSplitUnits, pk);
+                return cache[i].ok;
+            }
     }
-    const double plain = (double)std::max(nmax, nmin_main + next_max);
-    double best = plain * kSplitMargin;
     bool ok = false;
-    for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512}) {
-        int64_t K = 0;
-        for (int64_t qb = 0; qb < nx; ++qb) K += H * ((host_block_tiles(qb, k) + P - 1) / P);
-        if (K > max_slots) continue;
-        const int64_t per = (K + G - 1) / G;  // pieces of the busiest workgroup
-        const double mk = (double)nmax + kPieceOverheadTiles + (double)per * (kSpareTileCost * P + kPieceOverheadTiles) +
-                          kMergeTilesPerSlot * (double)K;
-        if (mk < best) {
-            best = mk;
-            ok = true;
-            *out = SplitPlan{1 << 30, P, (int32_t)K};
-            *nxqb = (int32_t)nx;
+    SplitPlan bp{};
+    int32_t bnx = 0;
+    int16_t bpk[kMaxSplitUnits] = {};
+    const int64_t nqb = k.nqb, U = nqb * H;
+    const int64_t nx = (U - G + H - 1) / H;
+    bool fit = U > G && 2 * U <= 3 * G && nx < nqb && nx * H <= kMaxSplitUnits && G <= kMaxSplitUnits;
+    const int64_t um = U - nx * H, per = nqb - nx;
+    for (int64_t x = 0; fit && x < 8; ++x)  // every XCD has a workgroup for each of its mains
+        fit = (x + 1) * um / 8 - x * um / 8 <= (G - x + 7) / 8;
+    if (fit) {
+        int64_t nt[kMaxSplitUnits];
+        int64_t nmax = 0, nmin_main = INT64_MAX, next_max = 0;
+        for (int64_t qb = 0; qb < nqb && qb < kMaxSplitUnits; ++qb) {
+            nt[qb] = host_block_tiles(qb, k);
+            if (qb >= nx) {
+                nmax = std::max(nmax, nt[qb]);
+                nmin_main = std::min(nmin_main, nt[qb]);
+            } else {
+                next_max = std::max(next_max, nt[qb]);
+            }
+        }
+        double mainlen[kMaxSplitUnits];  // per workgroup, as split_role assigns the mains
+        for (int64_t b = 0; b < G; ++b) {
+            const int64_t x = b & 7, i = b >> 3, mlo = x * um / 8, mn = (x + 1) * um / 8 - mlo;
+            mainlen[b] = i < mn ? (double)nt[nx + (mlo + i) % per] + kPieceOverheadTiles : 0.0;
+        }
+        const double plain = (double)std::max(nmax, nmin_main + next_max);
+        double best = plain * kSplitMargin;
+        double cost[2 * kMaxSplitUnits];
+        for (int32_t P : {8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 256, 384, 512}) {
+            int64_t K = 0;
+            for (int64_t qb = 0; qb < nx; ++qb) K += H * ((nt[qb] + P - 1) / P);
+            if (K > max_slots || K > 2 * kMaxSplitUnits) continue;
+            {  // piece costs in piece order (head-major, then query block, then tiles)
+                int64_t kk = 0;
+                for (int64_t h = 0; h < H; ++h)
+                    for (int64_t qb = 0; qb < nx; ++qb)
+                        for (int64_t t = 0; t < nt[qb]; t += P)
+                            cost[kk++] = kSpareTileCost * (double)std::min<int64_t>(P, nt[qb] - t) + kPieceOverheadTiles;
+            }
+            double mk = 0.0;
+            int16_t st[kMaxSplitUnits] = {};
+            for (int64_t x = 0; x < 8; ++x) {
+                const int64_t xlo = x * K / 8, xhi = (x + 1) * K / 8, nw = (G - x + 7) / 8;
+                // fill the workgroups of XCD x in order up to finish time M;
+                // returns the pieces left over
+                auto fill = [&](double M, bool store) {
+                    int64_t ptr = xlo;
+                    for (int64_t i = 0; i < nw; ++i) {
+                        const int64_t b = x + 8 * i;
+                        if (store) st[b] = (int16_t)ptr;
+                        double t = mainlen[b];
+                        while (ptr < xhi && t + cost[ptr] <= M) t += cost[ptr++];
+                    }
+                    return xhi - ptr;
+                };
+                double lo = 0.0, hi = 0.0;
+                for (int64_t i = 0; i < nw; ++i) lo = std::max(lo, mainlen[x + 8 * i]);
+                hi = lo;
+                for (int64_t kk = xlo; kk < xhi; ++kk) hi += cost[kk];
+                for (int it = 0; it < 40; ++it) {
+                    const double mid = 0.5 * (lo + hi);
+                    if (fill(mid, false) == 0) hi = mid;
+                    else lo = mid;
+                }
+                fill(hi, true);
+                mk = std::max(mk, hi);
+            }
+            mk += kMergeTilesPerSlot * (double)K;
+            if (mk < best) {
+                best = mk;
+                ok = true;
+                bp = SplitPlan{1 << 30, P, (int32_t)K};
+                bnx = (int32_t)nx;
+                std::copy(st, st + kMaxSplitUnits, bpk);
+            }
         }
     }
+    std::lock_guard<std::mutex> lock(mu);
+    Entry &e = cache[next];
+    next = (next + 1) % kCache;
+    ncache = std::min(ncache + 1, kCache);
+    std::copy(key, key + 7, e.key);
+    e.ok = ok;
+    e.plan = bp;
+    e.nx = bnx;
+    std::copy(bpk, bpk + kMaxSplitUnits, e.pk);
+    *out = bp;
+    *nxqb = bnx;
+    std::copy(bpk, bpk + kMaxSplitUnits, pk);
     return ok;
 }
 
@@ -2235,7 +2319,7 @@ hipError_t launch_d(const KArgs &ka, const AttnProblem &p, hipStream_t stream) {
             const int64_t max_slots = p.ws_slots > 0 ? std::min<int64_t>(p.ws_slots, 2 * G) : 2 * G;
             SplitPlan plan{};
             int32_t nx = 0;
-            if (plan_overflow(k, p.H, G, max_slots, &plan, &nx)) {
+            if (plan_overflow(k, p.H, G, max_slots, &plan, &nx, k.pk)) {
                 k.ws = (float *)p.ws;
                 k.nprog = (int32_t)G;
                 k.units = (int32_t)U;
