@@ -64,6 +64,29 @@ def test_noalloc_two_calls_wan_shape_then_smaller():
     kv.close()
 
 
+def test_noalloc_overflow_shape_matches_oracle():
+    # 700-token frames, 30 heads, a 3-frame chunk: 270 units of 256 rows for
+    # 256 compute units, which a launch with a workspace serves with the
+    # overflow split (the scratch's 256 slots bound its pieces); every element
+    # against the dense oracle and within the bar of the workspace call.
+    kpf, H, d, W, R, C = 700, 30, 128, 6, 1, 3
+    x = gen.stream_inputs(kpf, H, d, C, W, R, "bf16", base_seed=0, wid=404)
+    kr = torch.zeros((W, kpf, H, d), dtype=torch.bfloat16, device="cuda")
+    vr = torch.zeros_like(kr)
+    kf = torch.zeros((R, kpf, H, d), dtype=torch.bfloat16, device="cuda")
+    vf = torch.zeros_like(kf)
+    kv = rtr.rtr_kv_create(kr, vr, kf, vf, W, R, kpf, H, d)
+    rtr.rtr_kv_reset_ref(kv, rtr.RTR_REF_REPLACE, dev(x["ref_k"]), dev(x["ref_v"]), R, -1)
+    rtr.rtr_kv_append_evict(kv, dev(x["ring_k"]), dev(x["ring_v"]), W)
+    o, lse, _ = _both(kv, dev(x["q"]), dev(x["k"]), dev(x["v"]), C, H, d)
+    pk = np.concatenate([x["ref_k"].values.reshape(-1, H, d), x["ring_k"].values.reshape(-1, H, d)])
+    pv = np.concatenate([x["ref_v"].values.reshape(-1, H, d), x["ring_v"].values.reshape(-1, H, d)])
+    ro, rl = oracle.attn_stream_step(pk, pv, x["q"].values, x["k"].values, x["v"].values, kpf)
+    assert_bf16_close(host(o), ro, "noalloc vs oracle o (overflow shape)")
+    assert_bf16_close(host(lse), rl, "noalloc vs oracle lse (overflow shape)")
+    kv.close()
+
+
 def test_noalloc_small_cache_matches_oracle():
     kpf, H, d, W, R = 96, 2, 128, 3, 1
     kv, x, bufs = _cache(kpf, H, d, W, R, wid=402)
