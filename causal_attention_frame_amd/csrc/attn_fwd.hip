@@ -1761,17 +1761,28 @@ __global__ __launch_bounds__(256) void attn_combine_d128(const KArgs a) {
     const int row = part * RP + tid / 8, c0 = 16 * (tid % 8);
     const int qrow = qb * BM + row;
 
+    // Both loops are unrolled and load every piece's statistics without a
+    // branch (selecting afterwards), so that the loads of several pieces are
+    // in flight together; the values and the order of the additions are those
+    // of the plain loops.
     float M = -INFINITY;
+#pragma unroll 4
     for (int k = 0; k < npieces; ++k) {
         const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
-        if (ps[BM * D + BM + row] > 0.f) M = fmaxf(M, ps[BM * D + row]);
+        const float ls = ps[BM * D + BM + row], ms = ps[BM * D + row];
+        // ms is used either way (a piece without keys adds -inf, or NaN for
+        // an infinite reference, which fmaxf drops), so its load is not
+        // deferred behind the test of ls
+        M = fmaxf(M, ms + (ls > 0.f ? 0.f : -INFINITY));
     }
     float L = 0.f;
     f32x4 o[4] = {};
+#pragma unroll 4
     for (int k = 0; k < npieces; ++k) {
         const float *ps = a.ws + (long)slot_of(k) * kSlotFloats;
-        const float ls = ps[BM * D + BM + row];
-        const float w = ls > 0.f ? exp2f(ps[BM * D + row] - M) : 0.f;
+        const float ls = ps[BM * D + BM + row], ms = ps[BM * D + row];
+        const float e = exp2f(ms - M);
+        const float w = ls > 0.f ? e : 0.f;
         L += w * ls;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] += w * *(const f32x4 *)(ps + row * D + c0 + 4 * i);
