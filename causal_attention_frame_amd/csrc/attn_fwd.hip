@@ -83,7 +83,7 @@ struct KArgs {
     int32_t wpf, nframes, w1;
 };
 
-__device__ inline int key_limit(int i, const KArgs &a) {
+__host__ __device__ inline int key_limit(int i, const KArgs &a) {
     const int f = i / a.kpf;
     const long lim = (long)a.prefix + (long)(f + 1) * a.kpf;
     return lim < a.Tk ? (int)lim : a.Tk;
@@ -1105,13 +1105,13 @@ constexpr int kMaxSplitUnits = 256;                       // units of a split la
 constexpr int kSlotFloats = kD128BM * 128 + 2 * kD128BM;  // partial O, reference, sum
 static_assert(kSlotFloats * sizeof(float) == kSplitSlotBytes, "slot size");
 
-__device__ inline int block_tiles(int qb, const KArgs &a) {
+__host__ __device__ inline int block_tiles(int qb, const KArgs &a) {
     const int last = min(qb * kD128BM + kD128BM - 1, a.Tq - 1);
     return (key_limit(last, a) + kD128BN - 1) / kD128BN;
 }
 
 // Tail pieces of unit u.
-__device__ inline int unit_pieces(int u, const KArgs &a) {
+__host__ __device__ inline int unit_pieces(int u, const KArgs &a) {
     const int qb = u % a.nqb;
     if (a.nxqb > 0) return qb < a.nxqb ? (block_tiles(qb, a) + a.piece - 1) / a.piece : 0;
     const int r = block_tiles(qb, a) - a.cut;
@@ -1120,10 +1120,10 @@ __device__ inline int unit_pieces(int u, const KArgs &a) {
 
 // Units that can have tail pieces, in unit order: every unit, or with an
 // overflow split the nxqb first query blocks of each head.
-__device__ inline int piece_units(const KArgs &a) {
+__host__ __device__ inline int piece_units(const KArgs &a) {
     return a.nxqb > 0 ? (a.units / a.nqb) * a.nxqb : a.units;
 }
-__device__ inline int piece_unit(int pu, const KArgs &a) {
+__host__ __device__ inline int piece_unit(int pu, const KArgs &a) {
     return a.nxqb > 0 ? (pu / a.nxqb) * a.nqb + pu % a.nxqb : pu;
 }
 
@@ -1146,7 +1146,7 @@ __device__ __forceinline__ void build_piece_prefix(const KArgs &a, int *sPre, in
 }
 
 // Largest u with sPre[u] <= x (sPre non-decreasing).
-__device__ inline int find_tail_unit(const int *sPre, int U, int x) {
+__host__ __device__ inline int find_tail_unit(const int *sPre, int U, int x) {
     int lo = 0, hi = U;  // sPre[lo] <= x < sPre[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -1159,7 +1159,7 @@ __device__ inline int find_tail_unit(const int *sPre, int U, int x) {
 // Role of workgroup b in a split launch.  Workgroup b runs on XCD b mod 8;
 // each XCD gets a contiguous head-major run of units (so the mains of one head
 // share that XCD's L2), and its remaining workgroups are spares.
-__device__ inline void split_role(int b, const KArgs &a, int &unit, int &spare) {
+__host__ __device__ inline void split_role(int b, const KArgs &a, int &unit, int &spare) {
     const int x = b & 7, i = b >> 3;
     unit = -1;
     spare = -1;
